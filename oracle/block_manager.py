@@ -1,0 +1,149 @@
+"""Block manager with reference counts and copy-on-write (oracle; test infrastructure only).
+
+Model of the host-side KV block allocator, written from the pages:
+  * "PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
+    steps 1-4: a request's first block is allocated when it starts; tokens fill the block;
+    when the block is full the next one is allocated wherever there is space; a page table
+    records logical block -> physical block.
+  * same page, "Memory Efficiency": blocks are allocated on demand, so the only waste is the
+    unused tail of each sequence's last block (100 tokens -> 7 blocks of 16 -> 112 slots,
+    12 unused).
+  * same page, "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)": sequences that share
+    a prefix share its blocks; only divergent tokens get new blocks; like fork(), pages stay
+    shared until someone writes to them.
+  * "Efficient Memory Management for Large Language Model Serving with PagedAttention",
+    observer card, "Key ideas": prefix blocks are shared across sequences of one prompt
+    (parallel sampling, beam search) via copy-on-write.
+
+Readings where the pages are silent:
+  * "wherever there's space" is a free list whose initial order is an input (tests pass a
+    seeded random permutation); a freed block goes back on top of the list and is handed out
+    next (last in, first out); a freed sequence returns its blocks so that its logical block
+    0 is on top;
+  * a write to a block whose reference count is above one takes a fresh block, records the
+    pair (src, dst) for the device copy and drops one reference from src; the last holder
+    (count one) writes in place, as fork() does;
+  * a write that starts a new block never copies anything, even if earlier blocks are shared;
+  * wasted slots = for every physical block in use, block_size minus the largest number of
+    valid tokens any sequence keeps in it.
+"""
+from __future__ import annotations
+
+
+class OutOfBlocks(Exception):
+    """No free block is left in the pool."""
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of the block ids")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self._free = order[::-1]            # top of the stack = next block handed out
+        self.ref = [0] * num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.lens: dict[int, int] = {}
+
+    # -- free list ---------------------------------------------------------------------
+    def _take(self) -> int:
+        if not self._free:
+            raise OutOfBlocks()
+        b = self._free.pop()
+        assert self.ref[b] == 0
+        self.ref[b] = 1
+        return b
+
+    def _drop(self, b: int) -> None:
+        assert self.ref[b] > 0
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self._free.append(b)
+
+    # -- sequences ---------------------------------------------------------------------
+    def add_seq(self, seq: int, length: int) -> None:
+        """A new sequence holding ``length`` tokens gets ceil(length / BS) blocks."""
+        if seq in self.tables or length < 0:
+            raise ValueError("bad sequence")
+        n = -(-length // self.block_size)
+        if n > len(self._free):
+            raise OutOfBlocks()
+        self.tables[seq] = [self._take() for _ in range(n)]
+        self.lens[seq] = length
+
+    def fork(self, parent: int, child: int) -> None:
+        """The child shares every block of the parent; each gains one reference."""
+        if parent not in self.tables or child in self.tables:
+            raise ValueError("bad sequence")
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+
+    def append_slot(self, seq: int):
+        """Make room for one more token of ``seq``.
+
+        Returns (slot, cow) where slot = physical_block * BS + offset for the new token and
+        cow is None or the (src, dst) pair of blocks to copy before the write.
+        """
+        if seq not in self.tables:
+            raise ValueError("bad sequence")
+        table = self.tables[seq]
+        L = self.lens[seq]
+        j, offset = divmod(L, self.block_size)
+        cow = None
+        if j == len(table):
+            table.append(self._take())
+        else:
+            src = table[j]
+            if self.ref[src] > 1:
+                dst = self._take()
+                self.ref[src] -= 1
+                table[j] = dst
+                cow = (src, dst)
+        self.lens[seq] = L + 1
+        return table[j] * self.block_size + offset, cow
+
+    def append_slots(self, seqs):
+        """``append_slot`` for each sequence in order; stops at the first failure.
+
+        Returns (slots, cow_pairs, n_done).
+        """
+        slots, pairs = [], []
+        for i, s in enumerate(seqs):
+            try:
+                slot, cow = self.append_slot(s)
+            except (OutOfBlocks, ValueError):
+                return slots, pairs, i
+            slots.append(slot)
+            if cow is not None:
+                pairs.append(cow)
+        return slots, pairs, len(slots)
+
+    def free_seq(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise ValueError("bad sequence")
+        for b in reversed(self.tables.pop(seq)):
+            self._drop(b)
+        del self.lens[seq]
+
+    # -- queries -----------------------------------------------------------------------
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def block_table(self, seq: int) -> list[int]:
+        return list(self.tables[seq])
+
+    def seq_len(self, seq: int) -> int:
+        return self.lens[seq]
+
+    def wasted_slots(self) -> int:
+        fill: dict[int, int] = {}
+        for s, table in self.tables.items():
+            L = self.lens[s]
+            for j, b in enumerate(table):
+                fill[b] = max(fill.get(b, 0), min(self.block_size, L - j * self.block_size))
+        return sum(self.block_size - f for f in fill.values())

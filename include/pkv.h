@@ -1,0 +1,211 @@
+/*
+ * pkv.h -- C ABI of libpkv, the paged KV-cache decode path for AMD Instinct MI355X (gfx950).
+ *
+ * The method ("PagedAttention: Efficient LLM Serving with vLLM", "How PagedAttention Works";
+ * "Efficient Memory Management for Large Language Model Serving with PagedAttention",
+ * Abstract and observer card "Key ideas"): each sequence's key/value cache is cut into
+ * fixed-size blocks of block_size tokens (16 by default) that sit anywhere in a physical
+ * block pool; a per-sequence block table maps logical block j to its physical block; decode
+ * attention gathers K/V through that table; new tokens are written into the slot the block
+ * manager hands out; sequences that share a prefix share its blocks until one of them writes
+ * (copy-on-write).
+ *
+ * Conventions for every call below
+ *   - Device pointers are plain addresses in the current HIP device's memory; host pointers
+ *     are marked "host".  The caller owns every buffer (the library never allocates or frees
+ *     device memory).  Nothing here keeps a pointer after the call returns.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and never synchronize.  Argument errors are detected on the host before
+ *     anything is launched and returned as a status; nothing is launched then.
+ *   - Pool layout (K and V alike): [num_blocks][num_heads][block_size][head_dim], element type
+ *     `dtype`, row-major, contiguous.  Token t of a sequence lives in physical block
+ *     block_table[t / block_size] at slot t % block_size.  A "slot" number is
+ *     physical_block * block_size + offset.
+ *   - Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32}; dtype f32, f16, bf16;
+ *     otherwise PKV_EUNSUPPORTED.
+ *   - Device index arrays (block tables, context lengths, slot mappings, copy pairs) are read
+ *     by the kernels and cannot be checked on the host.  Out-of-range entries never cause an
+ *     out-of-bounds access: see each call for what they produce instead.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* a null pointer, a negative or inconsistent size, an unknown id */
+  PKV_EUNSUPPORTED = 2,  /* a shape or dtype this build has no kernel for */
+  PKV_ENOMEM = 3,        /* block pool exhausted (allocator) or workspace too small */
+  PKV_EHIP = 4           /* the HIP runtime reported an error at launch */
+} pkv_status_t;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype_t;
+
+/* Shape of one layer's K (or V) block pool. */
+typedef struct {
+  int32_t num_blocks;  /* physical blocks in the pool */
+  int32_t num_heads;   /* KV heads (one query head per KV head) */
+  int32_t block_size;  /* tokens per block: 8, 16 or 32 */
+  int32_t head_dim;    /* 64 or 128 */
+  int32_t dtype;       /* pkv_dtype_t of the pool, of q / out and of new k / v */
+} pkv_cache_desc_t;
+
+typedef void* pkv_stream_t; /* a hipStream_t */
+
+int32_t pkv_abi_version(void);
+const char* pkv_status_string(pkv_status_t status);
+
+/* ---------------------------------------------------------------------------------------
+ * Paged decode attention.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
+ * steps 4-5: the page table maps logical to physical blocks and attention gathers the
+ * scattered K/V pairs through it.)
+ *
+ * For every sequence s < num_seqs and head h < num_heads, with L = context_lens[s]:
+ *     z_t = scale * <q[s][h][:], K(s, t, h)>      for t = 0 .. L-1
+ *     out[s][h][:] = sum_t softmax(z)_t * V(s, t, h)
+ * where K(s, t, h) = k_pool[block_tables[s * max_blocks_per_seq + t / block_size]][h]
+ *                          [t % block_size][:], and V alike.  Arithmetic is binary32 with
+ * binary32 accumulation; out is rounded to dtype (round to nearest even).  L = 0 gives a zero
+ * vector.  The new token is attended like any other: append it first (pkv_reshape_and_cache),
+ * then pass its length including it.
+ *
+ *   out           device, [num_seqs][num_heads][head_dim], dtype; written
+ *   q             device, [num_seqs][num_heads][head_dim], dtype
+ *   k_pool,v_pool device, pool layout above
+ *   block_tables  device, int32 [num_seqs][max_blocks_per_seq]; entries past a sequence's
+ *                 last block are never read
+ *   context_lens  device, int32 [num_seqs]; a value above max_context_len or above
+ *                 max_blocks_per_seq * block_size is clamped to the smaller of the two, a
+ *                 negative value reads as 0
+ *   max_context_len  host; an upper bound of context_lens, sizes the launch and workspace
+ *   scale         host; the softmax temperature (usually 1/sqrt(head_dim))
+ *   workspace     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned; may be
+ *                 NULL when that size is 0.  Scratch for the split-context partials; its
+ *                 contents need no initialization and are garbage afterwards.
+ *
+ * Long contexts are split into partitions of pkv_decode_partition_tokens(...) tokens, each
+ * attended by its own workgroup; a second kernel merges the partial (max, sum, output)
+ * triples.  The split depends only on (desc, num_seqs, max_context_len) and the reduction
+ * order only on logical token order, so results are bit-identical run to run and for any
+ * physical placement of the blocks.
+ *
+ * A block id outside [0, num_blocks) in a block table is never dereferenced: that
+ * (sequence, head) output is set to NaN instead.
+ * Returns PKV_EINVAL (null pointers, negative sizes, workspace too small: PKV_ENOMEM),
+ * PKV_EUNSUPPORTED, PKV_EHIP or PKV_OK.
+ */
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                  int32_t max_context_len);
+int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                    int32_t max_context_len); /* 0: single pass, no split */
+pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t max_context_len, float scale, void* workspace,
+                                        size_t workspace_bytes, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Append new tokens' keys and values to the cache.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
+ * step 2: generated tokens fill the current block.)
+ *
+ * For every i < num_tokens with slot = slot_mapping[i] in [0, num_blocks * block_size):
+ *     k_pool[slot / block_size][h][slot % block_size][:] = k[i][h][:]   for every head h
+ * and the same for v.  A byte copy: bit-exact, NaN payloads included.  A negative slot, or
+ * one at or past num_blocks * block_size, writes nothing.  Slots in one call must be
+ * distinct (two tokens writing one slot leave either value).
+ *
+ *   k, v          device, [num_tokens][num_heads][head_dim], dtype, contiguous
+ *   k_pool,v_pool device, pool layout above; written
+ *   slot_mapping  device, int32 [num_tokens]
+ */
+pkv_status_t pkv_reshape_and_cache(const pkv_cache_desc_t* desc, const void* k, const void* v,
+                                   void* k_pool, void* v_pool, const int32_t* slot_mapping,
+                                   int32_t num_tokens, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Copy whole blocks, in every layer, for copy-on-write of shared prefix blocks.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" ->
+ * "KV-Cache Sharing (Copy-on-Write)": blocks stay shared until a write, like fork().)
+ *
+ * For every layer l < num_layers and pair p < num_pairs with (src, dst) = (pairs[2p],
+ * pairs[2p+1]):  k_pools[l][dst] = k_pools[l][src] and v_pools[l][dst] = v_pools[l][src]
+ * (one block = num_heads * block_size * head_dim elements).  Bit-exact.  A pair with src or
+ * dst outside [0, num_blocks) is skipped.  Destinations must be distinct and no destination
+ * may be a source in the same call (the block manager only produces such pairs).
+ *
+ *   k_pools,v_pools host arrays of num_layers device pointers, each a pool of shape `desc`
+ *   pairs           device, int32 [num_pairs][2]
+ */
+pkv_status_t pkv_copy_blocks(const pkv_cache_desc_t* desc, void* const* k_pools,
+                             void* const* v_pools, int32_t num_layers, const int32_t* pairs,
+                             int32_t num_pairs, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Host block manager: on-demand allocation, reference counts, copy-on-write decisions.
+ * Plain C++, no device calls; one instance is used by one thread.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
+ * steps 1-4 and "Memory Efficiency"; "Advanced Features" -> "KV-Cache Sharing
+ * (Copy-on-Write)".)
+ *
+ * Policy: free blocks are handed out from a free list whose initial order is `free_order`
+ * (host, a permutation of 0..num_blocks-1; NULL = ascending ids); a freed block goes on top
+ * of the list and is handed out next.  free_seq returns a sequence's blocks so that its
+ * logical block 0 is on top.
+ *   add_seq(seq, len)     new sequence with ceil(len / block_size) blocks
+ *   fork(parent, child)   child shares every block of parent (each gains a reference)
+ *   append_slot(seq)      room for one more token: a new block when the last one is full;
+ *                         if the target block is shared (reference count > 1) a fresh block
+ *                         replaces it in this sequence's table and (src, dst) is reported
+ *                         for pkv_copy_blocks; the last holder writes in place.
+ *   free_seq(seq)         drop one reference from each block; blocks at zero are freed
+ * Errors: PKV_EINVAL for an unknown or duplicate sequence id or a null argument;
+ * PKV_ENOMEM when the pool has no free block -- the state is then left unchanged.
+ * ---------------------------------------------------------------------------------------*/
+typedef struct pkv_alloc pkv_alloc_t;
+
+pkv_alloc_t* pkv_alloc_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* free_order /* host, may be NULL */);
+void pkv_alloc_destroy(pkv_alloc_t* a);
+pkv_status_t pkv_alloc_add_seq(pkv_alloc_t* a, int64_t seq, int32_t len);
+pkv_status_t pkv_alloc_fork(pkv_alloc_t* a, int64_t parent, int64_t child);
+/* slot: host out; cow_src / cow_dst: host out, -1 when no copy is needed. */
+pkv_status_t pkv_alloc_append_slot(pkv_alloc_t* a, int64_t seq, int32_t* slot, int32_t* cow_src,
+                                   int32_t* cow_dst);
+/* append_slot for seqs[0..n-1] in order; slots[i] (host out, n entries) receives each slot;
+ * cow_pairs (host out, room for 2*n int32) receives the (src, dst) pairs in order and
+ * *num_cow their count; *num_done the number of sequences served -- processing stops at
+ * the first error, which is returned. */
+pkv_status_t pkv_alloc_append_slots(pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                                    int32_t* slots, int32_t* cow_pairs, int32_t* num_cow,
+                                    int32_t* num_done);
+pkv_status_t pkv_alloc_free_seq(pkv_alloc_t* a, int64_t seq);
+/* Copies up to `cap` physical block ids of seq's table into out (host); *n = table length. */
+pkv_status_t pkv_alloc_block_table(const pkv_alloc_t* a, int64_t seq, int32_t* out, int32_t cap,
+                                   int32_t* n);
+/* Fills a dense host int32 [n][max_blocks] table (unused entries -1) and int32 [n] lengths
+ * for seqs[0..n-1]; PKV_EINVAL if a table is longer than max_blocks. */
+pkv_status_t pkv_alloc_export(const pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t* tables, int32_t* lens);
+int32_t pkv_alloc_seq_len(const pkv_alloc_t* a, int64_t seq); /* -1 if unknown */
+int32_t pkv_alloc_num_free(const pkv_alloc_t* a);
+int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block); /* -1 if out of range */
+/* Unused slots of blocks in use: per block, block_size minus the most tokens any sequence
+ * keeps in it ("Memory Efficiency": 100 tokens in 16-token blocks waste 12 slots). */
+int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

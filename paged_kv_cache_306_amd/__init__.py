@@ -1,0 +1,317 @@
+"""paged_kv_cache_306_amd -- paged KV-cache decode path for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libpkv.so (C ABI in include/pkv.h).  Every step of the path --
+block allocation, cache writes, block copies and decode attention -- runs in the native
+library; this module only marshals torch tensors (device memory, streams) into pointers.
+If libpkv.so has not been built, importing the functions raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
+    "paged_attention_decode", "reshape_and_cache", "copy_blocks", "BlockAllocator",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOMEM, PKV_EHIP = range(5)
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib().pkv_status_string(status).decode() if _LIB is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_LIB = None
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+_pdesc = ctypes.POINTER(CacheDesc)
+
+_SIGNATURES = {
+    "pkv_abi_version": (_i32, []),
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_decode_workspace_bytes": (_sz, [_pdesc, _i32, _i32]),
+    "pkv_decode_partition_tokens": (_i32, [_pdesc, _i32, _i32]),
+    "pkv_paged_attention_decode": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
+                                          _p, _sz, _p]),
+    "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
+    "pkv_copy_blocks": (_i32, [_pdesc, _p, _p, _i32, _p, _i32, _p]),
+    "pkv_alloc_create": (_p, [_i32, _i32, _p]),
+    "pkv_alloc_destroy": (None, [_p]),
+    "pkv_alloc_add_seq": (_i32, [_p, _i64, _i32]),
+    "pkv_alloc_fork": (_i32, [_p, _i64, _i64]),
+    "pkv_alloc_append_slot": (_i32, [_p, _i64, _pi32, _pi32, _pi32]),
+    "pkv_alloc_append_slots": (_i32, [_p, _p, _i32, _p, _p, _pi32, _pi32]),
+    "pkv_alloc_free_seq": (_i32, [_p, _i64]),
+    "pkv_alloc_block_table": (_i32, [_p, _i64, _p, _i32, _pi32]),
+    "pkv_alloc_export": (_i32, [_p, _p, _i32, _i32, _p, _p]),
+    "pkv_alloc_seq_len": (_i32, [_p, _i64]),
+    "pkv_alloc_num_free": (_i32, [_p]),
+    "pkv_alloc_refcount": (_i32, [_p, _i32]),
+    "pkv_alloc_wasted_slots": (_i64, [_p]),
+}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_306_amd.build` "
+                "(there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded libpkv.so (ctypes.CDLL), loading it on first use."""
+    return _lib()
+
+
+def _check(status: int, what: str):
+    if status != PKV_OK:
+        raise PkvError(status, what)
+
+
+# ----------------------------------------------------------------------------- torch glue
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def desc_for_pool(k_pool) -> CacheDesc:
+    """CacheDesc of a [num_blocks][num_heads][block_size][head_dim] pool tensor."""
+    nb, h, bs, d = k_pool.shape
+    return CacheDesc(nb, h, bs, d, _dtype_code(k_pool))
+
+
+def decode_workspace_bytes(desc: CacheDesc, num_seqs: int, max_context_len: int) -> int:
+    return int(_lib().pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, max_context_len))
+
+
+def decode_partition_tokens(desc: CacheDesc, num_seqs: int, max_context_len: int) -> int:
+    return int(_lib().pkv_decode_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len))
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                           max_context_len: int, workspace=None, stream=None):
+    """out[s, h] = softmax(scale * q[s, h] . K(s, :, h)) V(s, :, h) over the context_lens[s]
+    tokens of sequence s, gathered through block_tables (see include/pkv.h)."""
+    import torch
+    desc = desc_for_pool(k_pool)
+    S = q.shape[0]
+    if q.shape != out.shape or q.shape[1:] != (desc.num_heads, desc.head_dim):
+        raise ValueError("q/out shape mismatch")
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool/v_pool mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables/context_lens shape mismatch")
+    need = decode_workspace_bytes(desc, S, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib().pkv_paged_attention_decode(
+        ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables",
+                                                              torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S,
+        int(max_context_len), float(scale), ws_ptr, ws_bytes, _stream_ptr(stream))
+    _check(st, "pkv_paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(k, v, k_pool, v_pool, slot_mapping, stream=None):
+    """Write token i's K/V rows into slot slot_mapping[i] of the pools (include/pkv.h)."""
+    import torch
+    desc = desc_for_pool(k_pool)
+    N = k.shape[0]
+    if k.shape != (N, desc.num_heads, desc.head_dim) or v.shape != k.shape:
+        raise ValueError("k/v shape mismatch")
+    if slot_mapping.shape != (N,):
+        raise ValueError("slot_mapping shape mismatch")
+    st = _lib().pkv_reshape_and_cache(
+        ctypes.byref(desc), _dev(k, "k", k_pool.dtype), _dev(v, "v", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+        _dev(slot_mapping, "slot_mapping", torch.int32), N, _stream_ptr(stream))
+    _check(st, "pkv_reshape_and_cache")
+
+
+def copy_blocks(k_pools, v_pools, pairs, stream=None):
+    """pool[dst] = pool[src] for every (src, dst) row of `pairs` (int32 [n][2], device), in
+    every layer's K and V pool."""
+    import torch
+    if len(k_pools) != len(v_pools) or not k_pools:
+        raise ValueError("need one K and one V pool per layer")
+    desc = desc_for_pool(k_pools[0])
+    for p in list(k_pools) + list(v_pools):
+        if p.shape != k_pools[0].shape or p.dtype != k_pools[0].dtype:
+            raise ValueError("all pools must share one shape and dtype")
+    n = pairs.shape[0] if pairs.numel() else 0
+    if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
+        raise ValueError("pairs must be [n][2]")
+    L = len(k_pools)
+    kp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in k_pools])
+    vp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in v_pools])
+    for p in list(k_pools) + list(v_pools):
+        _dev(p, "pool")
+    pptr = _dev(pairs, "pairs", torch.int32) if n else ctypes.c_void_p(0)
+    st = _lib().pkv_copy_blocks(ctypes.byref(desc), kp, vp, L, pptr, n, _stream_ptr(stream))
+    _check(st, "pkv_copy_blocks")
+
+
+# ----------------------------------------------------------------------------- allocator
+class BlockAllocator:
+    """Host block manager (plain C++ inside libpkv): on-demand blocks, reference counts and
+    copy-on-write decisions.  See include/pkv.h for the policy."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        import numpy as np
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        arr = None
+        if free_order is not None:
+            arr = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if arr.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+        ptr = arr.ctypes.data_as(ctypes.c_void_p) if arr is not None else None
+        self._h = _lib().pkv_alloc_create(num_blocks, block_size, ptr)
+        if not self._h:
+            raise PkvError(PKV_EINVAL, "pkv_alloc_create")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _LIB is not None:
+            _LIB.pkv_alloc_destroy(h)
+
+    def add_seq(self, seq: int, length: int):
+        _check(_lib().pkv_alloc_add_seq(self._h, seq, length), "pkv_alloc_add_seq")
+
+    def fork(self, parent: int, child: int):
+        _check(_lib().pkv_alloc_fork(self._h, parent, child), "pkv_alloc_fork")
+
+    def append_slot(self, seq: int):
+        slot, src, dst = _i32(), _i32(), _i32()
+        _check(_lib().pkv_alloc_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
+                                            ctypes.byref(dst)), "pkv_alloc_append_slot")
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_slots(self, seqs):
+        """Returns (slots int32 [n], cow_pairs int32 [k][2]) as numpy arrays."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = int(seqs.shape[0])
+        slots = np.empty(n, np.int32)
+        pairs = np.empty((max(n, 1), 2), np.int32)
+        ncow, ndone = _i32(), _i32()
+        st = _lib().pkv_alloc_append_slots(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
+                                           slots.ctypes.data_as(ctypes.c_void_p),
+                                           pairs.ctypes.data_as(ctypes.c_void_p),
+                                           ctypes.byref(ncow), ctypes.byref(ndone))
+        if st != PKV_OK:
+            err = PkvError(st, "pkv_alloc_append_slots")
+            err.num_done = ndone.value
+            raise err
+        return slots, pairs[:ncow.value].copy()
+
+    def append_slots_into(self, seqs, slots, pairs) -> int:
+        """Like ``append_slots`` but writes into caller arrays (int64 seqs [n], int32 slots
+        [n], int32 pairs [n][2], all C-contiguous numpy); returns the number of pairs."""
+        n = int(seqs.shape[0])
+        ncow, ndone = _i32(), _i32()
+        st = _lib().pkv_alloc_append_slots(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
+                                           slots.ctypes.data_as(ctypes.c_void_p),
+                                           pairs.ctypes.data_as(ctypes.c_void_p),
+                                           ctypes.byref(ncow), ctypes.byref(ndone))
+        if st != PKV_OK:
+            err = PkvError(st, "pkv_alloc_append_slots")
+            err.num_done = ndone.value
+            raise err
+        return ncow.value
+
+    def export_into(self, seqs, tables, lens):
+        """Like ``export`` but writes into caller arrays (int32 tables [n][max_blocks],
+        int32 lens [n], C-contiguous numpy)."""
+        n = int(seqs.shape[0])
+        _check(_lib().pkv_alloc_export(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
+                                       tables.shape[1], tables.ctypes.data_as(ctypes.c_void_p),
+                                       lens.ctypes.data_as(ctypes.c_void_p)), "pkv_alloc_export")
+
+    def free_seq(self, seq: int):
+        _check(_lib().pkv_alloc_free_seq(self._h, seq), "pkv_alloc_free_seq")
+
+    def block_table(self, seq: int):
+        n = _i32()
+        _check(_lib().pkv_alloc_block_table(self._h, seq, None, 0, ctypes.byref(n)),
+               "pkv_alloc_block_table")
+        buf = (ctypes.c_int32 * max(1, n.value))()
+        _check(_lib().pkv_alloc_block_table(self._h, seq, buf, n.value, ctypes.byref(n)),
+               "pkv_alloc_block_table")
+        return list(buf[:n.value])
+
+    def export(self, seqs, max_blocks: int):
+        """Dense (tables int32 [n][max_blocks], lens int32 [n]) for the given sequences."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = int(seqs.shape[0])
+        tables = np.empty((n, max_blocks), np.int32)
+        lens = np.empty(n, np.int32)
+        _check(_lib().pkv_alloc_export(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
+                                       max_blocks, tables.ctypes.data_as(ctypes.c_void_p),
+                                       lens.ctypes.data_as(ctypes.c_void_p)), "pkv_alloc_export")
+        return tables, lens
+
+    def seq_len(self, seq: int) -> int:
+        return int(_lib().pkv_alloc_seq_len(self._h, seq))
+
+    def num_free(self) -> int:
+        return int(_lib().pkv_alloc_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib().pkv_alloc_refcount(self._h, block))
+
+    def wasted_slots(self) -> int:
+        return int(_lib().pkv_alloc_wasted_slots(self._h))

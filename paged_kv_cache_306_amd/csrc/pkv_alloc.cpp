@@ -1,0 +1,211 @@
+// Host block manager for the paged KV cache: plain C++, no device calls.
+//
+// On-demand allocation from a free list, per-block reference counts and the copy-on-write
+// decision ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention
+// Algorithm" steps 1-4, "Memory Efficiency", and "Advanced Features" -> "KV-Cache Sharing
+// (Copy-on-Write)").  The policy is stated in include/pkv.h.
+//
+// Per decode step the scheduler calls pkv_alloc_append_slots once for the whole batch; the
+// slots go to pkv_reshape_and_cache and the (src, dst) pairs to pkv_copy_blocks, which must
+// run first on the same stream.
+#include "pkv.h"
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+struct pkv_alloc {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> ref;
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t take() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    ref[b] = 1;
+    return b;
+  }
+  void drop(int32_t b) {
+    if (--ref[b] == 0) free_stack.push_back(b);
+  }
+};
+
+extern "C" {
+
+pkv_alloc_t* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order) {
+  if (num_blocks <= 0 || block_size <= 0) return nullptr;
+  pkv_alloc_t* a = new (std::nothrow) pkv_alloc_t();
+  if (!a) return nullptr;
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ref.assign(num_blocks, 0);
+  a->free_stack.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return nullptr;
+      }
+      seen[b] = 1;
+      a->free_stack[num_blocks - 1 - i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->free_stack[num_blocks - 1 - i] = i;
+  }
+  return a;
+}
+
+void pkv_alloc_destroy(pkv_alloc_t* a) { delete a; }
+
+pkv_status_t pkv_alloc_add_seq(pkv_alloc_t* a, int64_t seq, int32_t len) {
+  if (!a || len < 0 || a->seqs.count(seq)) return PKV_EINVAL;
+  int64_t n = (static_cast<int64_t>(len) + a->block_size - 1) / a->block_size;
+  if (n > static_cast<int64_t>(a->free_stack.size())) return PKV_ENOMEM;
+  pkv_alloc::Seq s;
+  s.len = len;
+  s.table.reserve(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) s.table.push_back(a->take());
+  a->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_fork(pkv_alloc_t* a, int64_t parent, int64_t child) {
+  if (!a) return PKV_EINVAL;
+  auto it = a->seqs.find(parent);
+  if (it == a->seqs.end() || a->seqs.count(child)) return PKV_EINVAL;
+  pkv_alloc::Seq c = it->second;
+  for (int32_t b : c.table) ++a->ref[b];
+  a->seqs.emplace(child, std::move(c));
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_append_slot(pkv_alloc_t* a, int64_t seq, int32_t* slot, int32_t* cow_src,
+                                   int32_t* cow_dst) {
+  if (!a || !slot || !cow_src || !cow_dst) return PKV_EINVAL;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_EINVAL;
+  pkv_alloc::Seq& s = it->second;
+  if (s.len == INT32_MAX) return PKV_EINVAL;
+  const int32_t j = s.len / a->block_size;
+  const int32_t off = s.len % a->block_size;
+  int32_t src = -1, dst = -1;
+  if (j == static_cast<int32_t>(s.table.size())) {
+    if (a->free_stack.empty()) return PKV_ENOMEM;
+    s.table.push_back(a->take());
+  } else if (a->ref[s.table[j]] > 1) {
+    if (a->free_stack.empty()) return PKV_ENOMEM;
+    src = s.table[j];
+    dst = a->take();
+    --a->ref[src];
+    s.table[j] = dst;
+  }
+  const int64_t sl = static_cast<int64_t>(s.table[j]) * a->block_size + off;
+  *slot = static_cast<int32_t>(sl);
+  *cow_src = src;
+  *cow_dst = dst;
+  ++s.len;
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_append_slots(pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                                    int32_t* slots, int32_t* cow_pairs, int32_t* num_cow,
+                                    int32_t* num_done) {
+  if (!a || n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_cow || !num_done)
+    return PKV_EINVAL;
+  *num_cow = 0;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src, dst;
+    pkv_status_t st = pkv_alloc_append_slot(a, seqs[i], &slots[i], &src, &dst);
+    if (st != PKV_OK) return st;
+    if (src >= 0) {
+      cow_pairs[2 * *num_cow] = src;
+      cow_pairs[2 * *num_cow + 1] = dst;
+      ++*num_cow;
+    }
+    ++*num_done;
+  }
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_free_seq(pkv_alloc_t* a, int64_t seq) {
+  if (!a) return PKV_EINVAL;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_EINVAL;
+  const std::vector<int32_t>& t = it->second.table;
+  for (auto b = t.rbegin(); b != t.rend(); ++b) a->drop(*b);
+  a->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_block_table(const pkv_alloc_t* a, int64_t seq, int32_t* out, int32_t cap,
+                                   int32_t* n) {
+  if (!a || !n || cap < 0 || (cap > 0 && !out)) return PKV_EINVAL;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PKV_EINVAL;
+  const std::vector<int32_t>& t = it->second.table;
+  *n = static_cast<int32_t>(t.size());
+  const size_t m = std::min(t.size(), static_cast<size_t>(cap));
+  if (m) std::memcpy(out, t.data(), m * sizeof(int32_t));
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_export(const pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                              int32_t max_blocks, int32_t* tables, int32_t* lens) {
+  if (!a || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables || !lens))) return PKV_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seqs[i]);
+    if (it == a->seqs.end()) return PKV_EINVAL;
+    const std::vector<int32_t>& t = it->second.table;
+    if (static_cast<int64_t>(t.size()) > max_blocks) return PKV_EINVAL;
+    int32_t* row = tables + static_cast<int64_t>(i) * max_blocks;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + max_blocks, -1);
+    lens[i] = it->second.len;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_seq_len(const pkv_alloc_t* a, int64_t seq) {
+  if (!a) return -1;
+  auto it = a->seqs.find(seq);
+  return it == a->seqs.end() ? -1 : it->second.len;
+}
+
+int32_t pkv_alloc_num_free(const pkv_alloc_t* a) {
+  return a ? static_cast<int32_t>(a->free_stack.size()) : -1;
+}
+
+int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->ref[block];
+}
+
+int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a) {
+  if (!a) return -1;
+  std::vector<int32_t> fill(a->num_blocks, 0);
+  for (const auto& kv : a->seqs) {
+    const auto& s = kv.second;
+    for (size_t j = 0; j < s.table.size(); ++j) {
+      int64_t in_block = static_cast<int64_t>(s.len) - static_cast<int64_t>(j) * a->block_size;
+      int32_t f = static_cast<int32_t>(std::min<int64_t>(a->block_size, in_block));
+      fill[s.table[j]] = std::max(fill[s.table[j]], f);
+    }
+  }
+  int64_t w = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b)
+    if (a->ref[b] > 0) w += a->block_size - fill[b];
+  return w;
+}
+
+}  // extern "C"

@@ -1,0 +1,376 @@
+// Paged decode attention for gfx950: one query per (sequence, head) attends over that
+// sequence's K/V, which sit in fixed-size blocks scattered through a physical pool and are
+// reached through the sequence's block table ("PagedAttention: Efficient LLM Serving with
+// vLLM", "The PagedAttention Algorithm", steps 4-5).
+//
+// Work split.  A workgroup of 4 waves takes one (sequence, head, partition); a partition is
+// a run of `part_tokens` consecutive tokens (the whole sequence in single-pass mode).  The
+// partition is cut into chunks of CHUNK tokens (8 KiB of K and 8 KiB of V per chunk at
+// fp16/bf16, head_dim 128) dealt round-robin to the 4 waves.
+//
+// Lane mapping.  A token's K row (head_dim elements) is read by LPT consecutive lanes, 16
+// bytes each, so one wave-wide 16-byte load covers TPL = 64 / LPT whole token rows and a
+// (block, head) tile of block_size rows -- contiguous in the pool -- is read by fully
+// coalesced loads.  At fp16/bf16 head_dim 128: LPT = 16 lanes (one DPP row), TPL = 4.
+// The q.K dot product is a per-lane 16-byte partial (v_dot2 for f16/bf16) summed over the
+// LPT lanes with DPP.  Each 16-lane row then owns every TPL-th token of the chunk and keeps
+// its own online-softmax state (running max m, running sum l, fp32 output slice), so the
+// hot loop has no cross-row traffic; the 4 x TPL states are merged once per workgroup
+// through LDS.  Scores are kept in log2 units (scale * log2 e folded into one multiply) so
+// the exponentials are single v_exp_f32 instructions.
+//
+// Split-context mode.  Each partition writes (m, l, o = acc / l) to the workspace and a
+// second kernel merges them: M = max m_p, out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p.
+// Sequences that fit in one partition are written out directly by the first kernel.
+//
+// Masking.  Only the last chunk of a partition can hold tokens at or past the end; their
+// scores become -inf and their V rows are replaced by zero before the multiply (the slots
+// may hold stale data or NaN, and NaN * 0 is NaN).  Blocks past the last valid one are never
+// dereferenced: the block index is clamped to the last valid block.
+#include "pkv.h"
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace pkv {
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
+template <class Ty, int D, int BS>
+struct DecodeCfg {
+  static constexpr int kEPL = 16 / Ty::kBytes;         // elements per lane per 16-byte load
+  static constexpr int kLPT = D / kEPL;                // lanes per token row
+  static constexpr int kTPL = 64 / kLPT;               // token rows per wave-wide load
+  static constexpr int kChunkBytes = 8192;             // K bytes per wave per iteration
+  static constexpr int kChunkByBytes = kChunkBytes / (D * Ty::kBytes);
+  static constexpr int kChunk = kChunkByBytes > BS ? kChunkByBytes : BS;  // tokens
+  static constexpr int kBlocksPerChunk = kChunk / BS;
+  static constexpr int kLoads = kChunk / kTPL;         // 16-byte K loads per lane per chunk
+  static constexpr int kStates = kDecodeWaves * kTPL;  // softmax states per workgroup
+  static_assert(kLPT == 8 || kLPT == 16 || kLPT == 32, "row width");
+  static_assert(BS % kTPL == 0, "a wave load must not straddle two blocks");
+  static_assert(kChunk % BS == 0, "chunks hold whole blocks");
+};
+
+// Clamp a device-provided length to what the launch was sized for.
+__device__ __forceinline__ int effective_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+template <class Ty, int D, int BS>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
+    typename Ty::store_t* __restrict__ out, const typename Ty::store_t* __restrict__ q,
+    const typename Ty::store_t* __restrict__ k_pool, const typename Ty::store_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
+    int num_heads, int num_blocks, int max_len, float scale_log2, int part_tokens, int max_parts,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+  using C = DecodeCfg<Ty, D, BS>;
+  using T = typename Ty::store_t;
+
+  // flattened grid: partition fastest, then head, then sequence
+  const int wg = blockIdx.x;
+  const int p = wg % max_parts;
+  const int sh = wg / max_parts;
+  const int h = sh % num_heads;
+  const int s = sh / num_heads;
+
+  const int L = effective_len(context_lens[s], max_len);
+  const int plen = part_tokens > 0 ? part_tokens : (L > 0 ? L : 1);
+  const int t0 = p * plen;
+  if (p > 0 && t0 >= L) return;  // uniform across the workgroup
+  const int t1 = min(L, t0 + plen);
+  const int nparts = part_tokens > 0 ? (L + part_tokens - 1) / part_tokens : 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane / C::kLPT;
+  const int col = lane % C::kLPT;
+
+  const size_t head_off = (static_cast<size_t>(s) * num_heads + h) * D;
+  const u32x4 qv = load16(q + head_off + col * C::kEPL);
+
+  const size_t blk_stride = static_cast<size_t>(num_heads) * BS * D;  // elements per block
+  const T* k_head = k_pool + static_cast<size_t>(h) * BS * D + col * C::kEPL;
+  const T* v_head = v_pool + static_cast<size_t>(h) * BS * D + col * C::kEPL;
+  const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
+
+  float m = -INFINITY, l = 0.0f;
+  float acc[C::kEPL];
+#pragma unroll
+  for (int e = 0; e < C::kEPL; ++e) acc[e] = 0.0f;
+  int bad = 0;
+
+  if (t1 > t0) {
+    const int last_lb = (t1 - 1) / BS;
+    for (int c0 = t0 + wave * C::kChunk; c0 < t1; c0 += kDecodeWaves * C::kChunk) {
+      size_t boff[C::kBlocksPerChunk];
+#pragma unroll
+      for (int b = 0; b < C::kBlocksPerChunk; ++b) {
+        const int lb = min(c0 / BS + b, last_lb);
+        int pb = table[lb];
+        if (static_cast<unsigned>(pb) >= static_cast<unsigned>(num_blocks)) {
+          bad = 1;
+          pb = 0;
+        }
+        boff[b] = static_cast<size_t>(pb) * blk_stride;
+      }
+      u32x4 kr[C::kLoads], vr[C::kLoads];
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const int b = (i * C::kTPL) / BS;
+        const int o = (i * C::kTPL) % BS + row;
+        const size_t off = boff[b] + static_cast<size_t>(o) * D;
+        kr[i] = load16(k_head + off);
+        vr[i] = load16(v_head + off);
+      }
+      float sc[C::kLoads];
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i)
+        sc[i] = group_sum<C::kLPT>(Ty::dot(qv, kr[i])) * scale_log2;
+      if (c0 + C::kChunk > t1) {
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) {
+          const bool valid = c0 + i * C::kTPL + row < t1;
+          sc[i] = valid ? sc[i] : -INFINITY;
+          vr[i] = valid ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      float mx = m;
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) mx = fmaxf(mx, sc[i]);
+      const float ms = (mx == -INFINITY) ? 0.0f : mx;
+      const float alpha = __builtin_amdgcn_exp2f(m - ms);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < C::kEPL; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(sc[i] - ms);
+        l += pr;
+        Ty::axpy(acc, pr, vr[i]);
+      }
+      m = mx;
+    }
+  }
+
+  // ---- merge the kStates (wave, row) states of this workgroup
+  __shared__ float sm_m[C::kStates];
+  __shared__ float sm_l[C::kStates];
+  __shared__ __attribute__((aligned(16))) float sm_acc[C::kStates][D];
+  const int st = wave * C::kTPL + row;
+  if (col == 0) {
+    sm_m[st] = m;
+    sm_l[st] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < C::kEPL; ++e) sm_acc[st][col * C::kEPL + e] = acc[e];
+  const int any_bad = __syncthreads_or(bad);
+
+  const int d = threadIdx.x;
+  if (d < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < C::kStates; ++j) M = fmaxf(M, sm_m[j]);
+    const float Ms = (M == -INFINITY) ? 0.0f : M;
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C::kStates; ++j) {
+      const float w = __builtin_amdgcn_exp2f(sm_m[j] - Ms);
+      den = fmaf(w, sm_l[j], den);
+      num = fmaf(w, sm_acc[j][d], num);
+    }
+    float o = den > 0.0f ? num / den : 0.0f;
+    if (any_bad) o = __builtin_nanf("");
+    if (nparts <= 1) {
+      out[head_off + d] = Ty::store(o);
+    } else {
+      const size_t slot = (static_cast<size_t>(s) * num_heads + h) * max_parts + p;
+      ws_o[slot * D + d] = o;
+      if (d == 0) {
+        ws_ml[2 * slot] = M;
+        ws_ml[2 * slot + 1] = den;
+      }
+    }
+  }
+}
+
+// Merge the partitions of every (sequence, head) that was split.  One workgroup of D
+// threads per (sequence, head); thread d owns output element d.
+template <class Ty, int D>
+__global__ __launch_bounds__(D) void decode_reduce_kernel(
+    typename Ty::store_t* __restrict__ out, const int32_t* __restrict__ context_lens, int num_heads,
+    int max_len, int part_tokens, int max_parts, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_o) {
+  const int h = blockIdx.x % num_heads;
+  const int s = blockIdx.x / num_heads;
+  const int L = effective_len(context_lens[s], max_len);
+  const int nparts = (L + part_tokens - 1) / part_tokens;
+  if (nparts <= 1) return;  // written by the partition kernel
+  const size_t base = (static_cast<size_t>(s) * num_heads + h) * max_parts;
+  const int d = threadIdx.x;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+  float num = 0.0f, den = 0.0f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = __builtin_amdgcn_exp2f(ws_ml[2 * (base + p)] - M) * ws_ml[2 * (base + p) + 1];
+    den += w;
+    num = fmaf(w, ws_o[(base + p) * D + d], num);
+  }
+  out[(static_cast<size_t>(s) * num_heads + h) * D + d] = Ty::store(num / den);
+}
+
+// ------------------------------------------------------------------ host side
+constexpr int kPartTokens = 512;
+
+static int effective_max_len(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
+  const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;
+  return static_cast<int>(std::min<int64_t>(max_context_len, cap));
+}
+
+static int partition_tokens(const pkv_cache_desc_t* d, int32_t num_seqs, int32_t max_len) {
+  (void)d;
+  (void)num_seqs;
+  return max_len > kPartTokens ? kPartTokens : 0;
+}
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_heads;
+  int num_blocks;
+  int max_len;
+  float scale_log2;
+  int part_tokens;
+  int max_parts;
+  float* ws_ml;
+  float* ws_o;
+  hipStream_t stream;
+};
+
+template <class Ty, int D, int BS>
+static void launch_decode(const DecodeArgs& a) {
+  using T = typename Ty::store_t;
+  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * a.num_heads * a.max_parts;
+  hipLaunchKernelGGL((decode_partition_kernel<Ty, D, BS>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(kDecodeThreads), 0, a.stream, static_cast<T*>(a.out),
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+                     static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
+                     a.num_heads, a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts,
+                     a.ws_ml, a.ws_o);
+  if (a.part_tokens > 0) {
+    const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+    hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)), dim3(D),
+                       0, a.stream, static_cast<T*>(a.out), a.context_lens, a.num_heads, a.max_len,
+                       a.part_tokens, a.max_parts, a.ws_ml, a.ws_o);
+  }
+}
+
+template <class Ty, int D>
+static pkv_status_t dispatch_bs(int bs, const DecodeArgs& a) {
+  switch (bs) {
+    case 8: launch_decode<Ty, D, 8>(a); return PKV_OK;
+    case 16: launch_decode<Ty, D, 16>(a); return PKV_OK;
+    case 32: launch_decode<Ty, D, 32>(a); return PKV_OK;
+  }
+  return PKV_EUNSUPPORTED;
+}
+
+template <class Ty>
+static pkv_status_t dispatch_d(int dim, int bs, const DecodeArgs& a) {
+  switch (dim) {
+    case 64: return dispatch_bs<Ty, 64>(bs, a);
+    case 128: return dispatch_bs<Ty, 128>(bs, a);
+  }
+  return PKV_EUNSUPPORTED;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                    int32_t max_context_len) {
+  if (!desc || num_seqs < 0 || max_context_len < 0) return 0;
+  return partition_tokens(desc, num_seqs, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                  int32_t max_context_len) {
+  if (!desc || num_seqs <= 0 || max_context_len <= 0 || desc->head_dim <= 0 ||
+      desc->num_heads <= 0)
+    return 0;
+  const int part = partition_tokens(desc, num_seqs, max_context_len);
+  if (part == 0) return 0;
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + part - 1) / part;
+  const int64_t slots = static_cast<int64_t>(num_seqs) * desc->num_heads * parts;
+  const int64_t ml = align_up(slots * 2 * 4, 256);
+  return static_cast<size_t>(ml + slots * desc->head_dim * 4);
+}
+
+pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t max_context_len, float scale, void* workspace,
+                                        size_t workspace_bytes, pkv_stream_t stream) {
+  pkv_status_t st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale))
+    return PKV_EINVAL;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+
+  const int max_len = effective_max_len(max_context_len, max_blocks_per_seq, desc->block_size);
+  const int part = partition_tokens(desc, num_seqs, max_len);
+  const int max_parts = part > 0 ? (max_len + part - 1) / part : 1;
+  const int64_t wgs = static_cast<int64_t>(num_seqs) * desc->num_heads * max_parts;
+  if (wgs > INT32_MAX) return PKV_EUNSUPPORTED;
+
+  DecodeArgs a{};
+  if (part > 0) {
+    const size_t need = pkv_decode_workspace_bytes(desc, num_seqs, max_len);
+    if (!workspace || workspace_bytes < need) return PKV_ENOMEM;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return PKV_EINVAL;
+    const int64_t slots = static_cast<int64_t>(num_seqs) * desc->num_heads * max_parts;
+    a.ws_ml = static_cast<float*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * 8, 256));
+  }
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_heads = desc->num_heads;
+  a.num_blocks = desc->num_blocks;
+  a.max_len = max_len;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.part_tokens = part;
+  a.max_parts = max_parts;
+  a.stream = static_cast<hipStream_t>(stream);
+
+  (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
+  switch (desc->dtype) {
+    case PKV_F32: st = dispatch_d<F32>(desc->head_dim, desc->block_size, a); break;
+    case PKV_F16: st = dispatch_d<F16>(desc->head_dim, desc->block_size, a); break;
+    case PKV_BF16: st = dispatch_d<BF16>(desc->head_dim, desc->block_size, a); break;
+    default: return PKV_EUNSUPPORTED;
+  }
+  if (st != PKV_OK) return st;
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"

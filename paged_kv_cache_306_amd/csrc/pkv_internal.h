@@ -1,0 +1,35 @@
+// Host-side helpers shared by the libpkv entry points.
+#pragma once
+
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+inline int dtype_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+  }
+  return 0;
+}
+
+// Shape checks common to every device call: positive sizes, and a shape this build has
+// kernels for (head_dim 64 or 128, block_size 8, 16 or 32, dtype f32 / f16 / bf16).
+// Slot numbers (block * block_size + offset) must fit in int32.
+inline pkv_status_t check_desc(const pkv_cache_desc_t* d) {
+  if (!d) return PKV_EINVAL;
+  if (d->num_blocks <= 0 || d->num_heads <= 0 || d->block_size <= 0 || d->head_dim <= 0)
+    return PKV_EINVAL;
+  if (static_cast<int64_t>(d->num_blocks) * d->block_size > INT32_MAX) return PKV_EINVAL;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_EUNSUPPORTED;
+  if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32) return PKV_EUNSUPPORTED;
+  if (dtype_bytes(d->dtype) == 0) return PKV_EUNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace pkv

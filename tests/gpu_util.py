@@ -1,0 +1,69 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, call the HIP path
+through the binding, and evaluate the oracle on the stored values."""
+import numpy as np
+
+import oracle
+import workloads as W
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def device():
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch.device("cuda:0")
+
+
+def to_dev(arr, dtype, dev):
+    return W.to_torch(arr, dtype).to(dev)
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers at |x| (x float64)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def check_close(got64, ref64, dtype, what=""):
+    """|got - ref| <= the stated bound: 1e-5 (f32) or 2e-3 (f16 / bf16).  Where a bfloat16
+    output's own spacing exceeds 2e-3 (|ref| >= 0.5) the bound is one bfloat16 ulp, since
+    rounding to the output type alone can exceed 2e-3 there."""
+    assert got64.shape == ref64.shape
+    assert np.isfinite(ref64).all()
+    assert np.isfinite(got64).all(), f"{what}: non-finite output"
+    err = np.abs(got64 - ref64)
+    bound = np.full_like(ref64, TOL[dtype])
+    if dtype == "bf16":
+        bound = np.maximum(bound, bf16_ulp(ref64))
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), (
+        f"{what}: max err {err.max():.3g} at {worst} (got {got64[worst]}, ref {ref64[worst]})")
+    return float(err.max())
+
+
+def sampled_oracle(q_np, k_pool_t, v_pool_t, tables, lens, units, dtype, scale):
+    """Oracle outputs for (s, h) in ``units``, reading each sampled sequence's blocks back
+    from the device pools (the stored values)."""
+    import torch
+    out = {}
+    by_seq = {}
+    for s, h in units:
+        by_seq.setdefault(int(s), []).append(int(h))
+    BS = k_pool_t.shape[2]
+    for s, heads in by_seq.items():
+        L = int(lens[s])
+        n = W.nblocks_for(L, BS)
+        if n:
+            idx = torch.from_numpy(np.asarray(tables[s, :n], np.int64)).to(k_pool_t.device)
+            kc = W.from_torch(k_pool_t.index_select(0, idx), dtype)
+            vc = W.from_torch(v_pool_t.index_select(0, idx), dtype)
+        else:
+            kc = W.from_torch(k_pool_t[:1], dtype)
+            vc = W.from_torch(v_pool_t[:1], dtype)
+        tab = np.arange(max(n, 1), dtype=np.int32)[None, :]
+        for h in heads:
+            out[(s, h)] = oracle.decode_unit(q_np[s:s + 1], kc, vc, tab, np.array([L]), scale,
+                                             dtype, 0, h)
+    return out

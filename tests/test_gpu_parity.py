@@ -1,0 +1,230 @@
+"""Parity of the HIP path (through the C ABI binding) with the float64 oracle.
+
+Small cases span several partitions, chunks and ragged tails in every supported dtype, head
+size and block size; full-size cases use the LLaMA-13B-shaped workloads with sampled units.
+Unused blocks and slots past each length are NaN-poisoned, so a stray read shows up.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_306_amd as pkv
+import workloads as W
+from gpu_util import TOL, check_close, device, sampled_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(q_np, kp_np, vp_np, tables, lens, scale, dtype, dev, max_len=None):
+    import torch
+    q = to_dev(q_np, dtype, dev)
+    kp = to_dev(kp_np, dtype, dev)
+    vp = to_dev(vp_np, dtype, dev)
+    bt = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+    cl = torch.from_numpy(np.ascontiguousarray(lens, np.int32)).to(dev)
+    out = torch.empty_like(q)
+    ml = int(np.max(lens)) if max_len is None else max_len
+    pkv.paged_attention_decode(out, q, kp, vp, bt, cl, scale, ml)
+    torch.cuda.synchronize()
+    return W.from_torch(out, dtype)
+
+
+def make_case(seed, S, H, D, BS, lens, dtype, pool_factor=1.3):
+    g = W.rng(seed)
+    lens = np.asarray(lens, np.int32)
+    tables, nb = W.permuted_block_tables(g, lens, BS, pool_factor=pool_factor)
+    q = W.normal_values(g, (S, H, D), dtype)
+    kp = W.normal_values(g, (nb, H, BS, D), dtype)
+    vp = W.normal_values(g, (nb, H, BS, D), dtype)
+    W.poison_unused(kp, tables, lens, BS, dtype)
+    W.poison_unused(vp, tables, lens, BS, dtype)
+    return q, kp, vp, tables, lens
+
+
+# ============================================================================ small cases
+def test_tiny_fp32_config():
+    """4 seqs, 4 heads, head_dim 64, block 16, lengths {1,15,16,37}, 32-block permuted pool."""
+    dev = device()
+    w = W.tiny_fp32()
+    g = W.rng(1001)
+    q = W.normal_values(g, (w.S, w.H, w.D), "f32")
+    kp = W.normal_values(g, (w.num_blocks, w.H, w.BS, w.D), "f32")
+    vp = W.normal_values(g, (w.num_blocks, w.H, w.BS, w.D), "f32")
+    W.poison_unused(kp, w.tables, w.lens, w.BS, "f32")
+    W.poison_unused(vp, w.tables, w.lens, w.BS, "f32")
+    got = run_decode(q, kp, vp, w.tables, w.lens, w.scale, "f32", dev)
+    ref = oracle.paged_attention_decode(q, kp, vp, w.tables, w.lens, w.scale, "f32")
+    err = check_close(got.astype(np.float64), ref, "f32", "tiny fp32")
+    print(f"tiny fp32 max abs err {err:.3g}")
+    # one token: exactly the stored V row
+    assert np.array_equal(got[0], vp[w.tables[0, 0], :, 0, :])
+
+
+SHAPES = [(dt, D, BS) for dt in ("f32", "f16", "bf16") for D in (64, 128) for BS in (8, 16, 32)]
+
+
+@pytest.mark.parametrize("dtype,D,BS", SHAPES, ids=lambda v: str(v))
+def test_ragged_multi_partition(dtype, D, BS):
+    dev = device()
+    lens = [0, 1, BS - 1, BS, BS + 1, 511, 512, 513, 1300, 2100]
+    S, H = len(lens), 3
+    q, kp, vp, tables, lens = make_case(7 + D + BS, S, H, D, BS, lens, dtype)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    got = run_decode(q, kp, vp, tables, lens, scale, dtype, dev)
+    ref = oracle.paged_attention_decode(q, kp, vp, tables, lens, scale, dtype)
+    check_close(oracle.decode(got, dtype), ref, dtype, f"{dtype} D{D} BS{BS}")
+    assert not oracle.decode(got[0], dtype).any(), "length 0 must give zeros"
+
+
+def test_placement_invariance_and_determinism():
+    """The same logical KV under two physical placements gives bit-identical outputs, and a
+    second run gives the same bits."""
+    dev = device()
+    S, H, D, BS, dt = 6, 4, 128, 16, "f16"
+    lens = np.array([5, 100, 600, 1025, 2048, 17], np.int32)
+    g = W.rng(77)
+    q = W.normal_values(g, (S, H, D), dt)
+    lk = [W.normal_values(g, (int(L), H, D), dt) for L in lens]
+    lv = [W.normal_values(g, (int(L), H, D), dt) for L in lens]
+    outs = []
+    for seed in (1, 2):
+        tables, nb = W.permuted_block_tables(W.rng(seed), lens, BS, pool_factor=1.5)
+        kp = np.zeros((nb, H, BS, D), np.float16)
+        vp = np.zeros((nb, H, BS, D), np.float16)
+        for s, L in enumerate(lens):
+            t = np.arange(L)
+            kp[tables[s, t // BS], :, t % BS] = lk[s]
+            vp[tables[s, t // BS], :, t % BS] = lv[s]
+        outs.append(run_decode(q, kp, vp, tables, lens, 0.088, dt, dev))
+        outs.append(run_decode(q, kp, vp, tables, lens, 0.088, dt, dev))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint16), outs[0].view(np.uint16))
+
+
+def test_bad_block_id_gives_nan_not_a_fault():
+    dev = device()
+    q, kp, vp, tables, lens = make_case(5, 3, 2, 128, 16, [40, 40, 700], "f16")
+    tables = tables.copy()
+    tables[1, 1] = 10 ** 6          # out of range
+    tables[2, 30] = -5              # out of range, in a split sequence
+    got = run_decode(q, kp, vp, tables, lens, 0.1, "f16", dev)
+    assert np.isnan(got[1].astype(np.float64)).all() and np.isnan(got[2].astype(np.float64)).all()
+    ref = oracle.paged_attention_decode(q, kp, vp, tables[:1], lens[:1], 0.1, "f16")
+    check_close(oracle.decode(got[:1], "f16"), ref, "f16")
+
+
+def test_context_len_clamped_to_max_context_len():
+    """A length above the host bound is read as the bound (no read past the table row)."""
+    dev = device()
+    q, kp, vp, tables, lens = make_case(6, 2, 2, 64, 16, [30, 64], "f32")
+    got = run_decode(q, kp, vp, tables, lens, 0.2, "f32", dev, max_len=48)
+    ref = oracle.paged_attention_decode(q, kp, vp, tables, np.minimum(lens, 48), 0.2, "f32")
+    check_close(got.astype(np.float64), ref, "f32")
+
+
+# ============================================================================ cache ops
+@pytest.mark.parametrize("dtype,D,BS", [("f32", 64, 16), ("f16", 128, 16), ("bf16", 128, 8),
+                                        ("f16", 64, 32)])
+def test_reshape_and_cache_bit_exact(dtype, D, BS):
+    import torch
+    dev = device()
+    g = W.rng(31)
+    NB, H, N = 40, 5, 37
+    kp = W.normal_values(g, (NB, H, BS, D), dtype)
+    vp = W.normal_values(g, (NB, H, BS, D), dtype)
+    k = W.normal_values(g, (N, H, D), dtype)
+    v = W.normal_values(g, (N, H, D), dtype)
+    slots = g.permutation(NB * BS)[:N].astype(np.int32)
+    slots[3] = -1                  # no write
+    slots[7] = NB * BS + 5         # past the pool: no write
+    kp_t, vp_t = to_dev(kp, dtype, dev), to_dev(vp, dtype, dev)
+    pkv.reshape_and_cache(to_dev(k, dtype, dev), to_dev(v, dtype, dev), kp_t, vp_t,
+                          torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    ok_slots = np.where((slots >= 0) & (slots < NB * BS), slots, -1)
+    ek, ev = oracle.reshape_and_cache(k, v, kp, vp, ok_slots)
+    assert np.array_equal(W.from_torch(kp_t, dtype).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(W.from_torch(vp_t, dtype).view(np.uint8), ev.view(np.uint8))
+
+
+def test_copy_blocks_bit_exact_all_layers():
+    import torch
+    dev = device()
+    g = W.rng(41)
+    NB, H, BS, D, layers, dt = 30, 40, 16, 128, 3, "f16"
+    kps = [W.normal_values(g, (NB, H, BS, D), dt) for _ in range(layers)]
+    vps = [W.normal_values(g, (NB, H, BS, D), dt) for _ in range(layers)]
+    pairs = np.array([[1, 20], [2, 21], [29, 0], [5, 99]], np.int32)   # last: out of range
+    kt = [to_dev(p, dt, dev) for p in kps]
+    vt = [to_dev(p, dt, dev) for p in vps]
+    pkv.copy_blocks(kt, vt, torch.from_numpy(pairs).to(dev))
+    torch.cuda.synchronize()
+    ek = oracle.copy_blocks(kps, pairs[:3])
+    ev = oracle.copy_blocks(vps, pairs[:3])
+    for l in range(layers):
+        assert np.array_equal(W.from_torch(kt[l], dt).view(np.uint16), ek[l].view(np.uint16))
+        assert np.array_equal(W.from_torch(vt[l], dt).view(np.uint16), ev[l].view(np.uint16))
+
+
+# ============================================================================ full sizes
+def _device_pools(w, dev, seed):
+    kp = W.device_normal((w.num_blocks, w.H, w.BS, w.D), w.dtype, seed, dev)
+    vp = W.device_normal((w.num_blocks, w.H, w.BS, w.D), w.dtype, seed + 1, dev)
+    W.poison_unused_device(kp, w.tables, w.lens, w.BS)
+    W.poison_unused_device(vp, w.tables, w.lens, w.BS)
+    return kp, vp
+
+
+def _run_full(w, dev, seed, units):
+    import torch
+    q_np = W.normal_values(W.rng(seed + 2), (w.S, w.H, w.D), w.dtype)
+    kp, vp = _device_pools(w, dev, seed)
+    q = to_dev(q_np, w.dtype, dev)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.tables).to(dev)
+    cl = torch.from_numpy(w.lens).to(dev)
+    pkv.paged_attention_decode(out, q, kp, vp, bt, cl, w.scale, w.max_len)
+    torch.cuda.synchronize()
+    got = W.from_torch(out, w.dtype)
+    ref = sampled_oracle(q_np, kp, vp, w.tables, w.lens, units, w.dtype, w.scale)
+    g = np.stack([oracle.decode(got[s, h], w.dtype) for s, h in units])
+    r = np.stack([ref[u] for u in units])
+    err = check_close(g, r, w.dtype, w.name)
+    print(f"{w.name}: {len(units)} sampled units, max abs err {err:.3g}")
+    del kp, vp
+    torch.cuda.empty_cache()
+    return got
+
+
+def _sample_units(w, n, seed):
+    g = W.rng(seed)
+    order = np.argsort(w.lens)
+    seqs = set(order[:2].tolist()) | set(order[-2:].tolist())   # shortest and longest
+    seqs |= set(g.choice(w.S, size=min(w.S, n), replace=False).tolist())
+    return [(int(s), int(g.integers(w.H))) for s in sorted(seqs)] + [(int(order[-1]), w.H - 1)]
+
+
+def test_llama13b_layer_full_size():
+    dev = device()
+    w = W.llama13b_layer()
+    _run_full(w, dev, 500, _sample_units(w, 24, 9))
+
+
+def test_shared_prefix_full_size():
+    dev = device()
+    w = W.shared_prefix()
+    units = _sample_units(w, 16, 10)
+    # add a whole group so equal-prefix members are checked side by side
+    units += [(s, 0) for s in range(8)]
+    got = _run_full(w, dev, 600, sorted(set(units)))
+    assert np.isfinite(got.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("BS", [8, 16, 32])
+def test_long_context_full_size(BS):
+    dev = device()
+    w = W.long_context(block_size=BS)
+    units = [(s, h) for s in range(w.S) for h in (0, 17, 39)]
+    _run_full(w, dev, 700 + BS, units)

@@ -288,3 +288,32 @@ def device_normal(shape, dtype: str, seed: int, device):
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
     return torch.randn(shape, dtype=torch_dtype(dtype), device=device, generator=gen)
+
+
+def poison_unused_device(pool_t, tables, lens, block_size: int) -> None:
+    """Device-tensor version of ``poison_unused``: NaN into unreferenced blocks and into
+    slots of referenced blocks that no sequence's length reaches."""
+    import torch
+    nb = pool_t.shape[0]
+    filled = np.zeros(nb, np.int64)
+    used = np.zeros(nb, bool)
+    for s, L in enumerate(np.asarray(lens).tolist()):
+        n = nblocks_for(L, block_size)
+        if n == 0:
+            continue
+        row = np.asarray(tables[s, :n], np.int64)
+        used[row] = True
+        counts = np.minimum(block_size, int(L) - np.arange(n) * block_size)
+        np.maximum.at(filled, row, counts)
+    dev = pool_t.device
+    unused = torch.from_numpy(np.nonzero(~used)[0]).to(dev)
+    if unused.numel():
+        pool_t.index_fill_(0, unused, float("nan"))
+    partial = np.nonzero(used & (filled < block_size))[0]
+    for r in range(1, block_size):
+        sel = partial[filled[partial] == r]
+        if sel.size:
+            idx = torch.from_numpy(sel).to(dev)
+            sub = pool_t.index_select(0, idx)
+            sub[:, :, r:, :] = float("nan")
+            pool_t.index_copy_(0, idx, sub)

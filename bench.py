@@ -1,9 +1,11 @@
 """Decode-step benchmark of the paged KV-cache hot path on one MI355X.
 
-One step = one decode iteration of a batch, all through libpkv:
+One step = one decode iteration of a batch, all inside one call of libpkv's native step
+driver (pkv_stepper_step):
   1. host block manager: append one slot per sequence (new block on a block boundary,
      copy-on-write pairs for shared blocks), export the block tables and lengths;
-  2. copy tables / lengths / slots to the device (pinned, double-buffered, asynchronous);
+  2. one packed copy of tables / lengths / slots / pairs to the device (pinned,
+     double-buffered, asynchronous);
   3. copy_blocks for any copy-on-write pairs;
   4. reshape_and_cache: write each sequence's new K/V token into its slot;
   5. paged_attention_decode over every sequence's context (new token included).
@@ -48,11 +50,26 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=320,
                     help="(sequence, head) units the oracle baseline computes")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     return ap.parse_args()
 
 
+def calibrate_copy(mib: int):
+    """Five plain device-to-device copies of a known size: FETCH_SIZE / WRITE_SIZE of this
+    run divided by the bytes moved gives the scale factor for the counters."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+
+
 class DecodeBatch:
-    """The synthetic decode batch and its device buffers."""
+    """The synthetic decode batch, its block manager and the native step driver."""
 
     def __init__(self, args, dev):
         import torch
@@ -66,7 +83,8 @@ class DecodeBatch:
         self.init_lens = w.lens.astype(np.int64)
         # pool 1.2x the need at the start lengths, as in the workload recipe
         self.NB = w.num_blocks
-        self.MB = -(-(int(w.lens.max()) + GROWTH + 1) // self.BS)
+        self.max_ctx = int(self.init_lens.max()) + GROWTH + 1
+        self.MB = -(-self.max_ctx // self.BS)
         g = W.rng(args.seed * 7919 + 1)
         order = (np.arange(self.NB) if args.placement == "contiguous"
                  else g.permutation(self.NB))
@@ -75,7 +93,7 @@ class DecodeBatch:
         self.next_id = self.S
         for s in range(self.S):
             self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
-        self.grown = np.zeros(self.S, np.int64)
+        self.cur_len = self.init_lens.copy()
 
         shape = (self.NB, self.H, self.BS, self.D)
         self.k_pool = W.device_normal(shape, self.dtype, args.seed * 10 + 1, dev)
@@ -84,70 +102,33 @@ class DecodeBatch:
         self.k_new = W.device_normal((self.S, self.H, self.D), self.dtype, args.seed * 10 + 4, dev)
         self.v_new = W.device_normal((self.S, self.H, self.D), self.dtype, args.seed * 10 + 5, dev)
         self.out = torch.empty_like(self.q)
-
-        # device index buffers and two pinned host staging sets
-        self.d_tables = torch.empty((self.S, self.MB), dtype=torch.int32, device=dev)
-        self.d_lens = torch.empty(self.S, dtype=torch.int32, device=dev)
-        self.d_slots = torch.empty(self.S, dtype=torch.int32, device=dev)
-        self.d_pairs = torch.empty((self.S, 2), dtype=torch.int32, device=dev)
-        self.stage = []
-        for _ in range(2):
-            t = torch.empty((self.S, self.MB), dtype=torch.int32, pin_memory=True)
-            L = torch.empty(self.S, dtype=torch.int32, pin_memory=True)
-            sl = torch.empty(self.S, dtype=torch.int32, pin_memory=True)
-            pr = torch.empty((self.S, 2), dtype=torch.int32, pin_memory=True)
-            self.stage.append({"t": t, "L": L, "sl": sl, "pr": pr, "ev": torch.cuda.Event()})
-        max_ctx = int(self.init_lens.max()) + GROWTH + 1
-        desc = pkv.desc_for_pool(self.k_pool)
-        self.workspace = torch.empty(max(16, pkv.decode_workspace_bytes(desc, self.S, max_ctx)),
-                                     dtype=torch.uint8, device=dev)
-        self.step_i = 0
+        self.stepper = pkv.DecodeStepper(self.alloc, [self.k_pool], [self.v_pool], [self.q],
+                                         [self.k_new], [self.v_new], [self.out], self.scale,
+                                         self.S, self.MB, self.max_ctx)
         self.kv_bytes = []       # logical K+V bytes read by attention, per step
         self.alg_bytes = []      # algorithmic bytes of the attention launch, per step
+        self.last = None
 
     def recycle(self):
         """Replace sequences that grew GROWTH tokens by fresh ones of their start length."""
-        for s in np.nonzero(self.grown >= GROWTH)[0]:
+        done = np.nonzero(self.cur_len - self.init_lens >= GROWTH)[0]
+        for s in done:
             self.alloc.free_seq(int(self.seq_ids[s]))
             self.seq_ids[s] = self.next_id
             self.next_id += 1
             self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
-            self.grown[s] = 0
+            self.cur_len[s] = self.init_lens[s]
 
-    def step(self, ev_pair=None):
-        import paged_kv_cache_306_amd as pkv
-        st = self.stage[self.step_i % 2]
-        self.step_i += 1
-        st["ev"].synchronize()             # its previous copies have left the buffers
+    def step(self, events=None):
         self.recycle()
-        sl, pr = st["sl"].numpy(), st["pr"].numpy()
-        ncow = self.alloc.append_slots_into(self.seq_ids, sl, pr)
-        self.grown += 1
-        tables, lens = st["t"].numpy(), st["L"].numpy()
-        self.alloc.export_into(self.seq_ids, tables, lens)
-        max_len = int(lens.max())
-        self.d_tables.copy_(st["t"], non_blocking=True)
-        self.d_lens.copy_(st["L"], non_blocking=True)
-        self.d_slots.copy_(st["sl"], non_blocking=True)
-        if ncow:
-            self.d_pairs[:ncow].copy_(st["pr"][:ncow], non_blocking=True)
-        st["ev"].record()
-        if ncow:
-            pkv.copy_blocks([self.k_pool], [self.v_pool], self.d_pairs[:ncow])
-        pkv.reshape_and_cache(self.k_new, self.v_new, self.k_pool, self.v_pool, self.d_slots)
-        if ev_pair is not None:
-            ev_pair[0].record()
-        pkv.paged_attention_decode(self.out, self.q, self.k_pool, self.v_pool, self.d_tables,
-                                   self.d_lens, self.scale, max_len, workspace=self.workspace)
-        if ev_pair is not None:
-            ev_pair[1].record()
-        tot = int(lens.astype(np.int64).sum())
-        e = 2
-        kv = 2 * tot * self.H * self.D * e
-        nblk = int(sum(-(-int(L) // self.BS) for L in lens))
+        max_len, ncow = self.stepper.step(self.seq_ids, events)
+        self.cur_len += 1
+        self.last = (max_len, ncow)
+        tot = int(self.cur_len.sum())
+        kv = 2 * tot * self.H * self.D * 2
+        nblk = int(((self.cur_len + self.BS - 1) // self.BS).sum())
         self.kv_bytes.append(kv)
-        self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * e + 4 * nblk + 4 * self.S)
-        return lens
+        self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * 2 + 4 * nblk + 4 * self.S)
 
 
 def cpu_baseline(batch, units_wanted):
@@ -156,8 +137,7 @@ def cpu_baseline(batch, units_wanted):
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
-    lens = batch.stage[(batch.step_i - 1) % 2]["L"].numpy().copy()
-    tables = batch.stage[(batch.step_i - 1) % 2]["t"].numpy().copy()
+    tables, lens = batch.alloc.export(batch.seq_ids, batch.MB)
     q = W.from_torch(batch.q, batch.dtype)
     units, seqs, kv = [], [], 0
     for s in range(batch.S):
@@ -195,6 +175,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU mode in this build", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
     dev = torch.device("cuda:0")
     b = DecodeBatch(args, dev)
@@ -203,12 +186,17 @@ def main():
     torch.cuda.synchronize()
     b.kv_bytes.clear()
     b.alg_bytes.clear()
+    import ctypes
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for a, z in evs:          # create the events; the step driver re-records them
+        a.record()
+        z.record()
+    handles = [(ctypes.c_void_p * 2)(a.cuda_event, z.cuda_event) for a, z in evs]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        b.step(evs[i])
+        b.step(handles[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     attn_ms = [a.elapsed_time(z) for a, z in evs]

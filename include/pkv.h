@@ -12,8 +12,9 @@
  *
  * Conventions for every call below
  *   - Device pointers are plain addresses in the current HIP device's memory; host pointers
- *     are marked "host".  The caller owns every buffer (the library never allocates or frees
- *     device memory).  Nothing here keeps a pointer after the call returns.
+ *     are marked "host".  The caller owns every device buffer (the library never allocates
+ *     or frees device memory).  Only the block manager and the step driver keep pointers
+ *     beyond a call, as stated there.
  *   - Device calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
  *     null stream) and never synchronize.  Argument errors are detected on the host before
  *     anything is launched and returned as a status; nothing is launched then.
@@ -203,6 +204,54 @@ int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block); /* -1 if out of
 /* Unused slots of blocks in use: per block, block_size minus the most tokens any sequence
  * keeps in it ("Memory Efficiency": 100 tokens in 16-token blocks waste 12 slots). */
 int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
+
+
+/* ---------------------------------------------------------------------------------------
+ * Decode-step driver: one decode iteration of a batch over every layer, in one call.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
+ * steps 1-5: extend each sequence's blocks on demand, fill the new slot, keep the page table,
+ * attend through it; "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)".)
+ *
+ * pkv_stepper_step(seqs[0..n-1]) does, in order:
+ *   1. pkv_alloc_append_slots on the stepper's block manager (one new slot per sequence),
+ *      then exports the dense block tables and lengths, into a pinned host staging area
+ *      (two areas used alternately, so the host can prepare step i+1 while step i's copy is
+ *      in flight);
+ *   2. one asynchronous host-to-device copy of the packed index data into d_index:
+ *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2];
+ *   3. pkv_copy_blocks over every layer when there are copy-on-write pairs;
+ *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]), then
+ *      pkv_paged_attention_decode(q[l] -> out[l]) with the lengths including the new token.
+ * Everything after step 1 is asynchronous on `stream`.  If step 1 fails (PKV_ENOMEM: the pool
+ * ran out; PKV_EINVAL: unknown sequence) nothing is launched, and the sequences before the
+ * failing one have already been extended by one slot (*num_done reports how many).
+ *
+ * The stepper allocates only pinned host memory and two HIP events; the caller owns the device
+ * buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned) and the workspace.
+ * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t recorded on `stream` just
+ * before and just after each layer's attention launch (for timing).
+ * ---------------------------------------------------------------------------------------*/
+typedef struct pkv_stepper pkv_stepper_t;
+
+typedef struct {
+  int32_t num_layers;
+  void* const* k_pools;      /* host arrays [num_layers] of device pools (layout above) */
+  void* const* v_pools;
+  const void* const* q;      /* host arrays [num_layers] of device [n][num_heads][head_dim] */
+  const void* const* k_new;
+  const void* const* v_new;
+  void* const* out;
+  float scale;
+} pkv_layer_io_t;
+
+size_t pkv_stepper_index_bytes(int32_t max_seqs, int32_t max_blocks_per_seq);
+pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
+                                  int32_t max_seqs, int32_t max_blocks_per_seq, void* d_index);
+void pkv_stepper_destroy(pkv_stepper_t* st);
+pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
+                              const pkv_layer_io_t* io, void* workspace, size_t workspace_bytes,
+                              void* const* attn_events, int32_t* max_len, int32_t* num_cow,
+                              int32_t* num_done, pkv_stream_t stream);
 
 #ifdef __cplusplus
 }

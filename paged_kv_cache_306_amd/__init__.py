@@ -13,7 +13,7 @@ import os
 __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
     "paged_attention_decode", "reshape_and_cache", "copy_blocks", "BlockAllocator",
-    "LIB_PATH",
+    "DecodeStepper", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -67,6 +67,10 @@ _SIGNATURES = {
     "pkv_alloc_num_free": (_i32, [_p]),
     "pkv_alloc_refcount": (_i32, [_p, _i32]),
     "pkv_alloc_wasted_slots": (_i64, [_p]),
+    "pkv_stepper_index_bytes": (_sz, [_i32, _i32]),
+    "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
+    "pkv_stepper_destroy": (None, [_p]),
+    "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
 }
 
 
@@ -315,3 +319,84 @@ class BlockAllocator:
 
     def wasted_slots(self) -> int:
         return int(_lib().pkv_alloc_wasted_slots(self._h))
+
+
+# ----------------------------------------------------------------------------- step driver
+class LayerIO(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("k_pools", ctypes.c_void_p),
+                ("v_pools", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k_new", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p), ("out", ctypes.c_void_p), ("scale", ctypes.c_float)]
+
+
+class DecodeStepper:
+    """Native decode-step driver (pkv_stepper_* in include/pkv.h): per call, one slot per
+    sequence from the block manager, one packed H2D copy of tables / lengths / slots / pairs,
+    copy_blocks for copy-on-write pairs, then per layer reshape_and_cache and decode."""
+
+    def __init__(self, alloc: BlockAllocator, k_pools, v_pools, q, k_new, v_new, out,
+                 scale: float, max_seqs: int, max_blocks_per_seq: int, max_context_len: int):
+        import torch
+        self.alloc = alloc                 # keep the block manager alive
+        self.desc = desc_for_pool(k_pools[0])
+        L = len(k_pools)
+        tensors = [k_pools, v_pools, q, k_new, v_new, out]
+        if any(len(t) != L for t in tensors):
+            raise ValueError("one tensor per layer in every list")
+        for p in list(k_pools) + list(v_pools):
+            _dev(p, "pool", k_pools[0].dtype)
+            if p.shape != k_pools[0].shape:
+                raise ValueError("all pools must share one shape")
+        for t in list(q) + list(k_new) + list(v_new) + list(out):
+            _dev(t, "q/k_new/v_new/out", k_pools[0].dtype)
+            if t.shape[1:] != (self.desc.num_heads, self.desc.head_dim) or t.shape[0] < max_seqs:
+                raise ValueError("per-layer tensors must be [>= max_seqs][heads][head_dim]")
+        self._keep = tensors
+        self._arrs = [(ctypes.c_void_p * L)(*[t.data_ptr() for t in lst]) for lst in tensors]
+        self.io = LayerIO(L, *[ctypes.cast(a, ctypes.c_void_p) for a in self._arrs], float(scale))
+        dev = k_pools[0].device
+        nbytes = int(_lib().pkv_stepper_index_bytes(max_seqs, max_blocks_per_seq))
+        self.d_index = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+        self.max_blocks = max_blocks_per_seq
+        self.max_seqs = max_seqs
+        ws = decode_workspace_bytes(self.desc, max_seqs, max_context_len)
+        self.workspace = torch.empty(max(16, ws), dtype=torch.uint8, device=dev)
+        self.max_context_len = max_context_len
+        self._h = _lib().pkv_stepper_create(alloc._h, ctypes.byref(self.desc), max_seqs,
+                                            max_blocks_per_seq, self.d_index.data_ptr())
+        if not self._h:
+            raise PkvError(PKV_EINVAL, "pkv_stepper_create")
+        self._max_len, self._ncow, self._ndone = _i32(), _i32(), _i32()
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _LIB is not None:
+            _LIB.pkv_stepper_destroy(h)
+
+    def step(self, seqs, events=None, stream=None):
+        """One decode step for the sequences in ``seqs`` (C-contiguous int64 numpy).
+        ``events``: optional ctypes array of 2 * num_layers hipEvent_t handles.
+        Returns (max_len, num_cow)."""
+        n = int(seqs.shape[0])
+        st = _lib().pkv_stepper_step(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
+                                     ctypes.byref(self.io), self.workspace.data_ptr(),
+                                     self.workspace.numel(), events,
+                                     ctypes.byref(self._max_len), ctypes.byref(self._ncow),
+                                     ctypes.byref(self._ndone), _stream_ptr(stream))
+        if st != PKV_OK:
+            err = PkvError(st, "pkv_stepper_step")
+            err.num_done = self._ndone.value
+            raise err
+        if self._max_len.value > self.max_context_len:
+            raise PkvError(PKV_ENOMEM, "pkv_stepper_step (context grew past the workspace bound)")
+        return self._max_len.value, self._ncow.value
+
+    def index_views(self, n: int, num_cow: int):
+        """Device views of the packed index data of the last step: (tables, lens, slots, pairs)."""
+        import torch
+        ints = self.d_index.view(torch.int32)
+        MB = self.max_blocks
+        t = ints[:n * MB].view(n, MB)
+        lens = ints[n * MB:n * MB + n]
+        slots = ints[n * MB + n:n * MB + 2 * n]
+        pairs = ints[n * MB + 2 * n:n * MB + 2 * n + 2 * num_cow].view(num_cow, 2)
+        return t, lens, slots, pairs

@@ -36,7 +36,17 @@
 
 namespace pkv {
 
-constexpr int kDecodeWaves = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_PART_TOKENS
+#define PKV_PART_TOKENS 512
+#endif
+#ifndef PKV_CHUNK_BYTES
+#define PKV_CHUNK_BYTES 8192
+#endif
+
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 template <class Ty, int D, int BS>
@@ -44,7 +54,7 @@ struct DecodeCfg {
   static constexpr int kEPL = 16 / Ty::kBytes;         // elements per lane per 16-byte load
   static constexpr int kLPT = D / kEPL;                // lanes per token row
   static constexpr int kTPL = 64 / kLPT;               // token rows per wave-wide load
-  static constexpr int kChunkBytes = 8192;             // K bytes per wave per iteration
+  static constexpr int kChunkBytes = PKV_CHUNK_BYTES;  // K bytes per wave per iteration
   static constexpr int kChunkByBytes = kChunkBytes / (D * Ty::kBytes);
   static constexpr int kChunk = kChunkByBytes > BS ? kChunkByBytes : BS;  // tokens
   static constexpr int kBlocksPerChunk = kChunk / BS;
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int kPartTokens = 512;
+constexpr int kPartTokens = PKV_PART_TOKENS;
 
 static int effective_max_len(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
   const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;

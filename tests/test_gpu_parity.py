@@ -111,7 +111,7 @@ def test_bad_block_id_gives_nan_not_a_fault():
     tables[2, 30] = -5              # out of range, in a split sequence
     got = run_decode(q, kp, vp, tables, lens, 0.1, "f16", dev)
     assert np.isnan(got[1].astype(np.float64)).all() and np.isnan(got[2].astype(np.float64)).all()
-    ref = oracle.paged_attention_decode(q, kp, vp, tables[:1], lens[:1], 0.1, "f16")
+    ref = oracle.paged_attention_decode(q[:1], kp, vp, tables[:1], lens[:1], 0.1, "f16")
     check_close(oracle.decode(got[:1], "f16"), ref, "f16")
 
 

@@ -317,3 +317,23 @@ def poison_unused_device(pool_t, tables, lens, block_size: int) -> None:
             sub = pool_t.index_select(0, idx)
             sub[:, :, r:, :] = float("nan")
             pool_t.index_copy_(0, idx, sub)
+
+
+def fork_groups(seed: int = 3, groups: int = 32, per_group: int = 8, prefix_len: int = 512,
+                rmax: int = 15):
+    """Copy-on-write step of the parallel-sampling workload: each group's prompt is
+    prefix_len + r_g tokens (r_g uniform in [1, rmax]), so its last prompt block is partly
+    filled and shared by the group's sequences after forking.  Returns the prompt lengths."""
+    g = rng(seed * 31 + 7)
+    return (prefix_len + uniform_lens(g, groups, 1, rmax)).astype(np.int32)
+
+
+def full_step(seed: int = 5, S: int = 512, block_size: int = 16, slack: float = 1.05):
+    """40-layer decode step: lognormal lengths (mean 600, sigma 0.8, clipped to [1, 2048]);
+    the pool holds every sequence's blocks after one appended token, plus ``slack``.
+    Returns (lens, num_blocks, free_order)."""
+    lens = full_step_lens(seed, S)
+    need = int(sum(nblocks_for(int(L) + 1, block_size) for L in lens))
+    nb = int(math.ceil(slack * need))
+    order = rng(seed * 1000 + 17).permutation(nb).astype(np.int32)
+    return lens, nb, order

@@ -37,6 +37,41 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode-attn KV GB/s (frac of HBM peak) and seq·layer/s, LLaMA-13B shape"
 HBM_PEAK_GBS = 8000.0
+# rocprofv3 counter summary of the decode kernel on this workload (see its header for the
+# commands); its traffic figure is used only while the kernel sources are unchanged.
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "decode_llama13b_layer_fp16_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_306_amd", "csrc", f)
+                  for f in ("pkv_decode.hip", "pkv_device.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Scaled HBM bytes per decode launch from the committed counter profile, or None when
+    there is none or it was taken on different kernel sources."""
+    try:
+        with open(COUNTER_PROFILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    fields = {}
+    for ln in lines:
+        if ln.startswith("- ") and ": " in ln:
+            k, v = ln[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 GROWTH = 64   # tokens a sequence grows before it is replaced
 
 
@@ -47,6 +82,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--placement", choices=["permuted", "contiguous"], default="permuted")
+    ap.add_argument("--workload", choices=WORKLOADS, default="llama13b_layer")
+    ap.add_argument("--block-size", type=int, default=16, help="long_context only: 8, 16, 32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=320,
                     help="(sequence, head) units the oracle baseline computes")
@@ -68,6 +105,47 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
+WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "full_step_40")
+
+
+def workload_spec(name: str, seed: int, block_size: int, placement: str):
+    """Shapes, start lengths, pool and block-manager set-up of one benchmark workload."""
+    import workloads as W
+    if name == "llama13b_layer":
+        w = W.llama13b_layer(seed)
+        spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
+                    lens=w.lens.astype(np.int64), NB=w.num_blocks, growth=64, groups=0,
+                    desc="64 seqs, 40 heads, head_dim 128, BS 16, lengths U[128,2048], fp16")
+    elif name == "long_context":
+        w = W.long_context(seed=4, block_size=block_size)
+        spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
+                    lens=w.lens.astype(np.int64), NB=w.num_blocks, growth=64, groups=0,
+                    desc=f"8 seqs, 40 heads, head_dim 128, BS {block_size}, lengths "
+                         "U[16384,32768], bf16")
+    elif name == "shared_prefix":
+        w = W.shared_prefix(seed=3)
+        # the block manager holds one root per group (the shared 512-token prefix) that is
+        # not stepped; the 8 members are forks of it plus their own tails
+        NB = w.num_blocks + 32 * 8 * 8
+        spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
+                    lens=w.lens.astype(np.int64), NB=NB, growth=64, groups=32, prefix=512,
+                    desc="32 groups x 8 seqs sharing a 512-token prefix, tails U[0,256], fp16")
+    elif name == "full_step_40":
+        lens, nb, _ = W.full_step(seed=5)
+        spec = dict(S=len(lens), H=40, D=128, BS=16, dtype="f16",
+                    scale=float(np.float32(1 / math.sqrt(128))), layers=40,
+                    lens=lens.astype(np.int64), NB=nb, growth=16, groups=0,
+                    desc="512 seqs, 40 layers, 40 heads, head_dim 128, BS 16, lognormal "
+                         "lengths (mean 600, sigma 0.8) in [1,2048], fp16")
+    else:
+        raise ValueError(name)
+    spec["name"] = name
+    g = W.rng(seed * 7919 + 1)
+    spec["order"] = (np.arange(spec["NB"]) if placement == "contiguous"
+                     else g.permutation(spec["NB"]))
+    return spec
+
+
 class DecodeBatch:
     """The synthetic decode batch, its block manager and the native step driver."""
 
@@ -75,48 +153,70 @@ class DecodeBatch:
         import torch
         import paged_kv_cache_306_amd as pkv
         import workloads as W
-        w = W.llama13b_layer(args.seed)
-        self.w = w
-        self.S, self.H, self.D, self.BS = w.S, w.H, w.D, w.BS
-        self.dtype = w.dtype
-        self.scale = w.scale
-        self.init_lens = w.lens.astype(np.int64)
-        # pool 1.2x the need at the start lengths, as in the workload recipe
-        self.NB = w.num_blocks
-        self.max_ctx = int(self.init_lens.max()) + GROWTH + 1
+        sp = workload_spec(args.workload, args.seed, args.block_size, args.placement)
+        self.sp = sp
+        self.S, self.H, self.D, self.BS = sp["S"], sp["H"], sp["D"], sp["BS"]
+        self.dtype, self.scale, self.layers = sp["dtype"], sp["scale"], sp["layers"]
+        self.e = W.ELEM_BYTES[self.dtype]
+        self.init_lens = sp["lens"]
+        self.growth = sp["growth"]
+        self.NB = sp["NB"]
+        self.max_ctx = int(self.init_lens.max()) + self.growth + 1
         self.MB = -(-self.max_ctx // self.BS)
-        g = W.rng(args.seed * 7919 + 1)
-        order = (np.arange(self.NB) if args.placement == "contiguous"
-                 else g.permutation(self.NB))
-        self.alloc = pkv.BlockAllocator(self.NB, self.BS, free_order=order)
+        self.alloc = pkv.BlockAllocator(self.NB, self.BS, free_order=sp["order"])
         self.seq_ids = np.arange(self.S, dtype=np.int64)
         self.next_id = self.S
-        for s in range(self.S):
-            self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
+        self.roots = []
+        if sp["groups"]:
+            per = self.S // sp["groups"]
+            for gi in range(sp["groups"]):
+                root = 1_000_000 + gi
+                self.alloc.add_seq(root, sp["prefix"])
+                self.roots.append(root)
+            for s in range(self.S):
+                self._fork_member(s, int(self.seq_ids[s]))
+        else:
+            for s in range(self.S):
+                self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
         self.cur_len = self.init_lens.copy()
 
         shape = (self.NB, self.H, self.BS, self.D)
-        self.k_pool = W.device_normal(shape, self.dtype, args.seed * 10 + 1, dev)
-        self.v_pool = W.device_normal(shape, self.dtype, args.seed * 10 + 2, dev)
-        self.q = W.device_normal((self.S, self.H, self.D), self.dtype, args.seed * 10 + 3, dev)
-        self.k_new = W.device_normal((self.S, self.H, self.D), self.dtype, args.seed * 10 + 4, dev)
-        self.v_new = W.device_normal((self.S, self.H, self.D), self.dtype, args.seed * 10 + 5, dev)
-        self.out = torch.empty_like(self.q)
-        self.stepper = pkv.DecodeStepper(self.alloc, [self.k_pool], [self.v_pool], [self.q],
-                                         [self.k_new], [self.v_new], [self.out], self.scale,
-                                         self.S, self.MB, self.max_ctx)
-        self.kv_bytes = []       # logical K+V bytes read by attention, per step
-        self.alg_bytes = []      # algorithmic bytes of the attention launch, per step
+        tensors = {k: [] for k in ("kp", "vp", "q", "kn", "vn", "out")}
+        for l in range(self.layers):
+            base = args.seed * 1000 + l * 10
+            tensors["kp"].append(W.device_normal(shape, self.dtype, base + 1, dev))
+            tensors["vp"].append(W.device_normal(shape, self.dtype, base + 2, dev))
+            for j, k in enumerate(("q", "kn", "vn")):
+                tensors[k].append(W.device_normal((self.S, self.H, self.D), self.dtype,
+                                                  base + 3 + j, dev))
+            tensors["out"].append(torch.empty_like(tensors["q"][-1]))
+        self.t = tensors
+        self.k_pool, self.v_pool, self.q = tensors["kp"][0], tensors["vp"][0], tensors["q"][0]
+        self.stepper = pkv.DecodeStepper(self.alloc, tensors["kp"], tensors["vp"], tensors["q"],
+                                         tensors["kn"], tensors["vn"], tensors["out"],
+                                         self.scale, self.S, self.MB, self.max_ctx)
+        self.kv_bytes = []       # logical K+V bytes read by attention, per step (all layers)
+        self.alg_bytes = []      # algorithmic bytes of one attention launch, per step
         self.last = None
 
+    def _fork_member(self, s, sid):
+        """Member s of its group: a fork of the group's prefix root plus its own tail."""
+        per = self.S // self.sp["groups"]
+        self.alloc.fork(self.roots[s // per], sid)
+        for _ in range(int(self.init_lens[s]) - self.sp["prefix"]):
+            self.alloc.append_slot(sid)
+
     def recycle(self):
-        """Replace sequences that grew GROWTH tokens by fresh ones of their start length."""
-        done = np.nonzero(self.cur_len - self.init_lens >= GROWTH)[0]
+        """Replace sequences that grew `growth` tokens by fresh ones of their start length."""
+        done = np.nonzero(self.cur_len - self.init_lens >= self.growth)[0]
         for s in done:
             self.alloc.free_seq(int(self.seq_ids[s]))
             self.seq_ids[s] = self.next_id
             self.next_id += 1
-            self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
+            if self.sp["groups"]:
+                self._fork_member(s, int(self.seq_ids[s]))
+            else:
+                self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
             self.cur_len[s] = self.init_lens[s]
 
     def step(self, events=None):
@@ -125,10 +225,10 @@ class DecodeBatch:
         self.cur_len += 1
         self.last = (max_len, ncow)
         tot = int(self.cur_len.sum())
-        kv = 2 * tot * self.H * self.D * 2
+        kv = 2 * tot * self.H * self.D * self.e
         nblk = int(((self.cur_len + self.BS - 1) // self.BS).sum())
-        self.kv_bytes.append(kv)
-        self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * 2 + 4 * nblk + 4 * self.S)
+        self.kv_bytes.append(kv * self.layers)
+        self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * self.e + 4 * nblk + 4 * self.S)
 
 
 def cpu_baseline(batch, units_wanted):
@@ -141,13 +241,13 @@ def cpu_baseline(batch, units_wanted):
     q = W.from_torch(batch.q, batch.dtype)
     units, seqs, kv = [], [], 0
     for s in range(batch.S):
-        if len(units) >= units_wanted:
+        if len(units) >= units_wanted or kv >= 160e6:
             break
         seqs.append(s)
         for h in range(batch.H):
-            if len(units) < units_wanted:
+            if len(units) < units_wanted and kv < 160e6:
                 units.append((s, h))
-                kv += 2 * int(lens[s]) * batch.D * 2
+                kv += 2 * int(lens[s]) * batch.D * batch.e
     prepared = {}
     for s in seqs:
         n = -(-int(lens[s]) // batch.BS)
@@ -163,9 +263,9 @@ def cpu_baseline(batch, units_wanted):
                                0, h)
         dt = time.perf_counter() - t0
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(units)} (sequence, head) units = first {len(seqs)} sequences x "
-                      f"40 heads of the same batch, {kv / 1e6:.1f} MB of K+V, float64 numpy, "
-                      f"{dt:.2f} s",
+            "sample": f"{len(units)} (sequence, head) units of the first {len(seqs)} "
+                      f"sequences of the same batch (layer 0), {kv / 1e6:.1f} MB of K+V, "
+                      f"float64 numpy, {dt:.2f} s",
             "seq_layer_per_s": len(units) / batch.H / dt}
 
 
@@ -187,38 +287,52 @@ def main():
     b.kv_bytes.clear()
     b.alg_bytes.clear()
     import ctypes
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, z in evs:          # create the events; the step driver re-records them
-        a.record()
-        z.record()
-    handles = [(ctypes.c_void_p * 2)(a.cuda_event, z.cuda_event) for a, z in evs]
+    import paged_kv_cache_306_amd as pkv
+    L = b.layers
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(args.steps)]
+    handles = []
+    for per_step in evs:      # create the events; the step driver re-records them
+        arr = (ctypes.c_void_p * (2 * L))()
+        for l, (a, z) in enumerate(per_step):
+            a.record()
+            z.record()
+            arr[2 * l], arr[2 * l + 1] = a.cuda_event, z.cuda_event
+        handles.append(arr)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         b.step(handles[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(z) for a, z in evs]
+    attn_ms = [a.elapsed_time(z) for per_step in evs for a, z in per_step]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     kv_total = float(np.sum(b.kv_bytes))
     value = kv_total / wall / 1e9
     alg_per_launch = float(np.mean(b.alg_bytes))
     achieved = alg_per_launch / attn_avg_s / 1e9
+    desc = pkv.desc_for_pool(b.k_pool)
+    split = pkv.decode_partition_tokens(desc, b.S, b.max_ctx) > 0
+    dt_name = {"f16": "F16", "bf16": "BF16", "f32": "F32"}[b.dtype]
+    kname = f"decode_partition_kernel<{dt_name},{b.D},{b.BS}>"
+    kname += " + decode_reduce_kernel (split context)" if split else " (single pass: one launch)"
+    default = args.workload == "llama13b_layer" and args.placement == "permuted"
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
         "data": "synthetic",
-        "config": {"workload": "llama13b_layer_fp16", "seqs": b.S, "heads": b.H,
-                   "head_dim": b.D, "block_size": b.BS, "context_lens": "uniform[128,2048] + growth",
-                   "pool_blocks": b.NB, "placement": args.placement, "layers": 1},
-        "seq_layer_per_s": round(b.S * args.steps / wall, 1),
+        "config": {"workload": f"{args.workload}_{b.dtype}", "description": b.sp["desc"],
+                   "seqs": b.S, "heads": b.H, "head_dim": b.D, "block_size": b.BS,
+                   "layers": L, "pool_blocks": b.NB, "placement": args.placement,
+                   "growth_tokens_before_replacement": b.growth},
+        "seq_layer_per_s": round(b.S * L * args.steps / wall, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_decode (partition + reduce launches)",
-                     "avg_launch_us": round(attn_avg_s * 1e6, 2),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if default else None,
+                     "kernel": kname, "avg_launch_us": round(attn_avg_s * 1e6, 2),
                      "alg_bytes_per_launch": int(alg_per_launch)},
     }
     if not args.no_cpu_baseline:

@@ -217,7 +217,7 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *      then exports the dense block tables and lengths, into a pinned host staging area
  *      (two areas used alternately, so the host can prepare step i+1 while step i's copy is
  *      in flight);
- *   2. one asynchronous host-to-device copy of the packed index data into d_index:
+ *   2. one asynchronous host-to-device copy of the packed index data into an area of d_index:
  *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2];
  *   3. pkv_copy_blocks over every layer when there are copy-on-write pairs;
  *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]), then
@@ -226,8 +226,12 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * ran out; PKV_EINVAL: unknown sequence) nothing is launched, and the sequences before the
  * failing one have already been extended by one slot (*num_done reports how many).
  *
- * The stepper allocates only pinned host memory and two HIP events; the caller owns the device
- * buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned) and the workspace.
+ * The stepper allocates only pinned host memory, HIP events and one copy stream (default
+ * priority) of its own; the caller owns the device buffer d_index (pkv_stepper_index_bytes
+ * bytes, 16-byte aligned: two areas used by alternate steps) and the workspace.  The upload of
+ * step i runs on the copy stream after the kernels of step i-2 and before those of step i, so
+ * it overlaps step i-1's kernels when the host runs ahead.  pkv_stepper_last_index returns the
+ * device address of the packed index data of the last step.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t recorded on `stream` just
  * before and just after each layer's attention launch (for timing).
  * ---------------------------------------------------------------------------------------*/
@@ -252,6 +256,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
                               const pkv_layer_io_t* io, void* workspace, size_t workspace_bytes,
                               void* const* attn_events, int32_t* max_len, int32_t* num_cow,
                               int32_t* num_done, pkv_stream_t stream);
+const void* pkv_stepper_last_index(const pkv_stepper_t* st);
 
 #ifdef __cplusplus
 }

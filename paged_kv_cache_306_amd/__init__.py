@@ -71,6 +71,7 @@ _SIGNATURES = {
     "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
     "pkv_stepper_destroy": (None, [_p]),
     "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
+    "pkv_stepper_last_index": (_p, [_p]),
 }
 
 
@@ -393,7 +394,9 @@ class DecodeStepper:
     def index_views(self, n: int, num_cow: int):
         """Device views of the packed index data of the last step: (tables, lens, slots, pairs)."""
         import torch
-        ints = self.d_index.view(torch.int32)
+        base = int(_lib().pkv_stepper_last_index(self._h))
+        off = (base - self.d_index.data_ptr()) // 4
+        ints = self.d_index.view(torch.int32)[off:]
         MB = self.max_blocks
         t = ints[:n * MB].view(n, MB)
         lens = ints[n * MB:n * MB + n]

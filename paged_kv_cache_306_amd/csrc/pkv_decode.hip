@@ -37,17 +37,26 @@
 namespace pkv {
 
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
+#define PKV_DECODE_WAVES 8
 #endif
 #ifndef PKV_PART_TOKENS
-#define PKV_PART_TOKENS 512
+#define PKV_PART_TOKENS 2048
+#endif
+#ifndef PKV_SINGLE_MAX
+#define PKV_SINGLE_MAX 2048
 #endif
 #ifndef PKV_CHUNK_BYTES
 #define PKV_CHUNK_BYTES 8192
 #endif
+#ifndef PKV_PIPELINE
+#define PKV_PIPELINE 1
+#endif
 
 constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// Longest run of tokens one workgroup attends: bounds the LDS copy of its block ids.
+constexpr int kMaxPartTokens = 4096;
+static_assert(PKV_PART_TOKENS <= kMaxPartTokens && PKV_SINGLE_MAX <= kMaxPartTokens, "part");
 
 template <class Ty, int D, int BS>
 struct DecodeCfg {
@@ -60,6 +69,7 @@ struct DecodeCfg {
   static constexpr int kBlocksPerChunk = kChunk / BS;
   static constexpr int kLoads = kChunk / kTPL;         // 16-byte K loads per lane per chunk
   static constexpr int kStates = kDecodeWaves * kTPL;  // softmax states per workgroup
+  static constexpr int kMaxBlocks = kMaxPartTokens / BS;
   static_assert(kLPT == 8 || kLPT == 16 || kLPT == 32, "row width");
   static_assert(BS % kTPL == 0, "a wave load must not straddle two blocks");
   static_assert(kChunk % BS == 0, "chunks hold whole blocks");
@@ -70,6 +80,50 @@ __device__ __forceinline__ int effective_len(int L, int max_len) {
   return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
 
+// One wave's online-softmax state: running max m (log2 units), running sum l, and the
+// fp32 output slice of this lane (kEPL elements of the head).
+template <class Ty, class C>
+struct RowState {
+  float m = -INFINITY, l = 0.0f;
+  float acc[C::kEPL];
+  __device__ RowState() {
+#pragma unroll
+    for (int e = 0; e < C::kEPL; ++e) acc[e] = 0.0f;
+  }
+  // Fold one chunk: kr/vr hold this lane's 16-byte slices of the chunk's K and V rows.
+  template <bool MASKED>
+  __device__ __forceinline__ void fold(const u32x4 qv, u32x4* kr, u32x4* vr, float scale_log2,
+                                       int c0, int t1, int row) {
+    float sc[C::kLoads];
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i)
+      sc[i] = group_sum<C::kLPT>(Ty::dot(qv, kr[i])) * scale_log2;
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i) {
+        const bool valid = c0 + i * C::kTPL + row < t1;
+        sc[i] = valid ? sc[i] : -INFINITY;
+        vr[i] = valid ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) mx = fmaxf(mx, sc[i]);
+    const float ms = (mx == -INFINITY) ? 0.0f : mx;
+    const float alpha = __builtin_amdgcn_exp2f(m - ms);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < C::kEPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      const float pr = __builtin_amdgcn_exp2f(sc[i] - ms);
+      l += pr;
+      Ty::axpy(acc, pr, vr[i]);
+    }
+    m = mx;
+  }
+};
+
 template <class Ty, int D, int BS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     typename Ty::store_t* __restrict__ out, const typename Ty::store_t* __restrict__ q,
@@ -79,6 +133,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   using C = DecodeCfg<Ty, D, BS>;
   using T = typename Ty::store_t;
+  __shared__ int sm_blk[C::kMaxBlocks];
+  __shared__ float sm_m[C::kStates];
+  __shared__ float sm_l[C::kStates];
+  __shared__ __attribute__((aligned(16))) float sm_acc[C::kStates][D];
 
   // flattened grid: partition fastest, then head, then sequence
   const int wg = blockIdx.x;
@@ -94,6 +152,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   const int t1 = min(L, t0 + plen);
   const int nparts = part_tokens > 0 ? (L + part_tokens - 1) / part_tokens : 1;
 
+  // This workgroup's physical block ids, read once into LDS; an id outside the pool is
+  // replaced by block 0 (in bounds) and poisons the output.
+  const int lb0 = t0 / BS;
+  const int nblk = (t1 - t0 + BS - 1) / BS;
+  const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks + lb0;
+  int bad = 0;
+  for (int i = threadIdx.x; i < nblk; i += kDecodeThreads) {
+    int pb = table[i];
+    if (static_cast<unsigned>(pb) >= static_cast<unsigned>(num_blocks)) {
+      bad = 1;
+      pb = 0;
+    }
+    sm_blk[i] = pb;
+  }
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane / C::kLPT;
@@ -103,81 +176,87 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   const u32x4 qv = load16(q + head_off + col * C::kEPL);
 
   const size_t blk_stride = static_cast<size_t>(num_heads) * BS * D;  // elements per block
-  const T* k_head = k_pool + static_cast<size_t>(h) * BS * D + col * C::kEPL;
-  const T* v_head = v_pool + static_cast<size_t>(h) * BS * D + col * C::kEPL;
-  const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
+  // Uniform (SGPR) base of head h in block 0, plus this lane's 32-bit byte offset inside a
+  // (block, head) tile: loads then take the scalar-base + vector-offset form.
+  const char* k_head = reinterpret_cast<const char*>(k_pool + static_cast<size_t>(h) * BS * D);
+  const char* v_head = reinterpret_cast<const char*>(v_pool + static_cast<size_t>(h) * BS * D);
+  const uint32_t lane_off = static_cast<uint32_t>((row * D + col * C::kEPL) * sizeof(T));
 
-  float m = -INFINITY, l = 0.0f;
-  float acc[C::kEPL];
-#pragma unroll
-  for (int e = 0; e < C::kEPL; ++e) acc[e] = 0.0f;
-  int bad = 0;
+  const int any_bad_ids = __syncthreads_or(bad);
 
-  if (t1 > t0) {
-    const int last_lb = (t1 - 1) / BS;
-    for (int c0 = t0 + wave * C::kChunk; c0 < t1; c0 += kDecodeWaves * C::kChunk) {
-      size_t boff[C::kBlocksPerChunk];
+  // issue the 16-byte K and V loads of the chunk starting at token c0
+  auto issue = [&](int c0, u32x4* kr, u32x4* vr) {
 #pragma unroll
-      for (int b = 0; b < C::kBlocksPerChunk; ++b) {
-        const int lb = min(c0 / BS + b, last_lb);
-        int pb = table[lb];
-        if (static_cast<unsigned>(pb) >= static_cast<unsigned>(num_blocks)) {
-          bad = 1;
-          pb = 0;
-        }
-        boff[b] = static_cast<size_t>(pb) * blk_stride;
+    for (int b = 0; b < C::kBlocksPerChunk; ++b) {
+      const int j = min((c0 - t0) / BS + b, nblk - 1);
+      const size_t boff =
+          static_cast<size_t>(__builtin_amdgcn_readfirstlane(sm_blk[j])) * blk_stride * sizeof(T);
+      const gptr_t kb = uniform_ptr(k_head + boff);
+      const gptr_t vb = uniform_ptr(v_head + boff);
+      constexpr int kPerBlock = BS / C::kTPL;  // wave loads per (block, head) tile
+#pragma unroll
+      for (int u = 0; u < kPerBlock; ++u) {
+        const uint32_t off = lane_off + static_cast<uint32_t>(u * C::kTPL * D * sizeof(T));
+        kr[b * kPerBlock + u] = load16(kb + off);
+        vr[b * kPerBlock + u] = load16(vb + off);
       }
-      u32x4 kr[C::kLoads], vr[C::kLoads];
-#pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) {
-        const int b = (i * C::kTPL) / BS;
-        const int o = (i * C::kTPL) % BS + row;
-        const size_t off = boff[b] + static_cast<size_t>(o) * D;
-        kr[i] = load16(k_head + off);
-        vr[i] = load16(v_head + off);
-      }
-      float sc[C::kLoads];
-#pragma unroll
-      for (int i = 0; i < C::kLoads; ++i)
-        sc[i] = group_sum<C::kLPT>(Ty::dot(qv, kr[i])) * scale_log2;
-      if (c0 + C::kChunk > t1) {
-#pragma unroll
-        for (int i = 0; i < C::kLoads; ++i) {
-          const bool valid = c0 + i * C::kTPL + row < t1;
-          sc[i] = valid ? sc[i] : -INFINITY;
-          vr[i] = valid ? vr[i] : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      float mx = m;
-#pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) mx = fmaxf(mx, sc[i]);
-      const float ms = (mx == -INFINITY) ? 0.0f : mx;
-      const float alpha = __builtin_amdgcn_exp2f(m - ms);
-      l *= alpha;
-#pragma unroll
-      for (int e = 0; e < C::kEPL; ++e) acc[e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::kLoads; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(sc[i] - ms);
-        l += pr;
-        Ty::axpy(acc, pr, vr[i]);
-      }
-      m = mx;
     }
+    // keep every load of the chunk ahead of the arithmetic that consumes it
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  RowState<Ty, C> st;
+  auto consume = [&](int c0, u32x4* kr, u32x4* vr) {
+    if (c0 + C::kChunk > t1)
+      st.template fold<true>(qv, kr, vr, scale_log2, c0, t1, row);
+    else
+      st.template fold<false>(qv, kr, vr, scale_log2, c0, t1, row);
+  };
+  constexpr int kStride = kDecodeWaves * C::kChunk;
+  if (t1 > t0) {
+#if PKV_PIPELINE
+    // Software pipeline over this wave's chunks c(k) = first + k * kStride, k < n: the loads
+    // of chunk k+1 are in flight while chunk k is folded.  The loop body issues
+    // unconditionally so the compiler waits only for the older chunk's loads.
+    u32x4 ka[C::kLoads], va[C::kLoads], kb[C::kLoads], vb[C::kLoads];
+    const int first = t0 + wave * C::kChunk;
+    const int n = first < t1 ? (t1 - first + kStride - 1) / kStride : 0;
+    if (n > 0) {
+      issue(first, ka, va);
+      int k = 0;
+      for (; k + 2 < n; k += 2) {
+        const int c = first + k * kStride;
+        issue(c + kStride, kb, vb);
+        consume(c, ka, va);
+        issue(c + 2 * kStride, ka, va);
+        consume(c + kStride, kb, vb);
+      }
+      const int c = first + k * kStride;
+      if (k + 1 < n) {
+        issue(c + kStride, kb, vb);
+        consume(c, ka, va);
+        consume(c + kStride, kb, vb);
+      } else {
+        consume(c, ka, va);
+      }
+    }
+#else
+    for (int c0 = t0 + wave * C::kChunk; c0 < t1; c0 += kStride) {
+      u32x4 kr[C::kLoads], vr[C::kLoads];
+      issue(c0, kr, vr);
+      consume(c0, kr, vr);
+    }
+#endif
   }
 
   // ---- merge the kStates (wave, row) states of this workgroup
-  __shared__ float sm_m[C::kStates];
-  __shared__ float sm_l[C::kStates];
-  __shared__ __attribute__((aligned(16))) float sm_acc[C::kStates][D];
-  const int st = wave * C::kTPL + row;
+  const int stx = wave * C::kTPL + row;
   if (col == 0) {
-    sm_m[st] = m;
-    sm_l[st] = l;
+    sm_m[stx] = st.m;
+    sm_l[stx] = st.l;
   }
 #pragma unroll
-  for (int e = 0; e < C::kEPL; ++e) sm_acc[st][col * C::kEPL + e] = acc[e];
-  const int any_bad = __syncthreads_or(bad);
+  for (int e = 0; e < C::kEPL; ++e) sm_acc[stx][col * C::kEPL + e] = st.acc[e];
+  __syncthreads();
 
   const int d = threadIdx.x;
   if (d < D) {
@@ -193,7 +272,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
       num = fmaf(w, sm_acc[j][d], num);
     }
     float o = den > 0.0f ? num / den : 0.0f;
-    if (any_bad) o = __builtin_nanf("");
+    if (any_bad_ids) o = __builtin_nanf("");
     if (nparts <= 1) {
       out[head_off + d] = Ty::store(o);
     } else {
@@ -234,16 +313,19 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 
 // ------------------------------------------------------------------ host side
 constexpr int kPartTokens = PKV_PART_TOKENS;
+constexpr int kSingleMax = PKV_SINGLE_MAX;
 
 static int effective_max_len(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
   const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;
   return static_cast<int>(std::min<int64_t>(max_context_len, cap));
 }
 
+// Contexts up to kSingleMax tokens are attended by one workgroup per (sequence, head);
+// longer ones are split into kPartTokens-token partitions plus a merge.
 static int partition_tokens(const pkv_cache_desc_t* d, int32_t num_seqs, int32_t max_len) {
   (void)d;
   (void)num_seqs;
-  return max_len > kPartTokens ? kPartTokens : 0;
+  return max_len > kSingleMax ? kPartTokens : 0;
 }
 
 struct DecodeArgs {

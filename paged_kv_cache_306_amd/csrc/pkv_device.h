@@ -120,8 +120,35 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+typedef const __attribute__((address_space(1))) char* gptr_t;  // global memory
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+
+#ifndef PKV_NT_LOADS
+#define PKV_NT_LOADS 1
+#endif
+
+// K/V tile loads: every byte is read once per decode step.
+__device__ __forceinline__ u32x4 load16(gptr_t p) {
+  const __attribute__((address_space(1))) u32x4* v =
+      reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
+#if PKV_NT_LOADS
+  return __builtin_nontemporal_load(v);
+#else
+  return *v;
+#endif
+}
+
+// A wave-uniform pointer passed through readfirstlane: the optimizer can no longer fold
+// lane-varying offsets into it, so loads from `uniform_ptr(base) + lane_offset` keep the
+// scalar-base + 32-bit vector-offset addressing form.
+__device__ __forceinline__ gptr_t uniform_ptr(const char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<gptr_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 }  // namespace pkv

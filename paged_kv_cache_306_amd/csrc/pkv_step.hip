@@ -11,16 +11,23 @@
 #include <algorithm>
 #include <new>
 
+// Two stages are used alternately.  Stage k owns a pinned host area and a device area of
+// d_index.  The upload of step i runs on the stepper's own copy stream after the kernels of
+// step i-2 (the last reader of the same device area) and before the kernels of step i, so it
+// overlaps the kernels of step i-1 whenever the host runs ahead of the device.
 struct pkv_stepper {
   pkv_alloc_t* alloc = nullptr;
   pkv_cache_desc_t desc{};
   int32_t max_seqs = 0;
   int32_t max_blocks = 0;
-  char* d_index = nullptr;
+  hipStream_t copy_stream = nullptr;
   struct Stage {
-    int32_t* host = nullptr;  // pinned: tables | lens | slots | pairs (packed for n)
-    hipEvent_t copied = nullptr;
-    bool pending = false;
+    int32_t* host = nullptr;      // pinned: tables | lens | slots | pairs (packed for n)
+    char* dev = nullptr;          // device area of the same size inside d_index
+    hipEvent_t copied = nullptr;  // recorded on the copy stream after the upload
+    hipEvent_t consumed = nullptr;  // recorded on the caller's stream after the kernels
+    bool copy_pending = false;
+    bool used = false;
   } stage[2];
   int cur = 0;
 };
@@ -36,9 +43,14 @@ size_t index_ints(int32_t n, int32_t max_blocks) {
 
 extern "C" {
 
+static size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq) {
+  return static_cast<size_t>(
+      pkv::align_up(static_cast<int64_t>(index_ints(max_seqs, max_blocks_per_seq) * 4), 256));
+}
+
 size_t pkv_stepper_index_bytes(int32_t max_seqs, int32_t max_blocks_per_seq) {
   if (max_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
-  return index_ints(max_seqs, max_blocks_per_seq) * sizeof(int32_t);
+  return 2 * stage_bytes(max_seqs, max_blocks_per_seq);
 }
 
 pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
@@ -52,12 +64,19 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   st->desc = *desc;
   st->max_seqs = max_seqs;
   st->max_blocks = max_blocks_per_seq;
-  st->d_index = static_cast<char*>(d_index);
-  const size_t bytes = pkv_stepper_index_bytes(max_seqs, max_blocks_per_seq);
-  for (auto& sg : st->stage) {
+  const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq);
+  if (hipStreamCreateWithFlags(&st->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+    st->copy_stream = nullptr;
+    pkv_stepper_destroy(st);
+    return nullptr;
+  }
+  for (int k = 0; k < 2; ++k) {
+    auto& sg = st->stage[k];
+    sg.dev = static_cast<char*>(d_index) + k * bytes;
     if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes, hipHostMallocDefault) !=
             hipSuccess ||
-        hipEventCreateWithFlags(&sg.copied, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&sg.copied, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sg.consumed, hipEventDisableTiming) != hipSuccess) {
       pkv_stepper_destroy(st);
       return nullptr;
     }
@@ -67,13 +86,16 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
 
 void pkv_stepper_destroy(pkv_stepper_t* st) {
   if (!st) return;
+  if (st->copy_stream) (void)hipStreamSynchronize(st->copy_stream);
   for (auto& sg : st->stage) {
-    if (sg.copied) {
-      if (sg.pending) (void)hipEventSynchronize(sg.copied);
-      (void)hipEventDestroy(sg.copied);
+    if (sg.consumed) {
+      if (sg.used) (void)hipEventSynchronize(sg.consumed);
+      (void)hipEventDestroy(sg.consumed);
     }
+    if (sg.copied) (void)hipEventDestroy(sg.copied);
     if (sg.host) (void)hipHostFree(sg.host);
   }
+  if (st->copy_stream) (void)hipStreamDestroy(st->copy_stream);
   delete st;
 }
 
@@ -94,10 +116,10 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
 
   st->cur ^= 1;
   auto& sg = st->stage[st->cur];
-  if (sg.pending) {
-    // the copy issued from this staging area two steps ago must have read it
+  if (sg.copy_pending) {
+    // the upload issued from this host area two steps ago must have read it
     if (hipEventSynchronize(sg.copied) != hipSuccess) return PKV_EHIP;
-    sg.pending = false;
+    sg.copy_pending = false;
   }
   const int32_t MB = st->max_blocks;
   int32_t* tables = sg.host;
@@ -114,35 +136,52 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const size_t used = (index_ints(n, MB) - 2 * static_cast<size_t>(n - *num_cow)) * sizeof(int32_t);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (hipMemcpyAsync(st->d_index, sg.host, used, hipMemcpyHostToDevice, hs) != hipSuccess ||
-      hipEventRecord(sg.copied, hs) != hipSuccess)
+  // upload after the last reader of this device area, then make the kernels wait for it
+  if ((sg.used && hipStreamWaitEvent(st->copy_stream, sg.consumed, 0) != hipSuccess) ||
+      hipMemcpyAsync(sg.dev, sg.host, used, hipMemcpyHostToDevice, st->copy_stream) !=
+          hipSuccess ||
+      hipEventRecord(sg.copied, st->copy_stream) != hipSuccess ||
+      hipStreamWaitEvent(hs, sg.copied, 0) != hipSuccess)
     return PKV_EHIP;
-  sg.pending = true;
+  sg.copy_pending = true;
 
-  const int32_t* d_tables = reinterpret_cast<const int32_t*>(st->d_index);
+  const int32_t* d_tables = reinterpret_cast<const int32_t*>(sg.dev);
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;
   const int32_t* d_slots = d_lens + n;
   const int32_t* d_pairs = d_slots + n;
 
-  if (*num_cow > 0 && L > 0) {
-    s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
-    if (s != PKV_OK) return s;
-  }
-  for (int32_t l = 0; l < L; ++l) {
-    s = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l], io->k_pools[l],
-                              io->v_pools[l], d_slots, n, stream);
-    if (s != PKV_OK) return s;
-    if (attn_events && hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
-      return PKV_EHIP;
-    s = pkv_paged_attention_decode(&st->desc, io->out[l], io->q[l], io->k_pools[l],
-                                   io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
-                                   workspace, workspace_bytes, stream);
-    if (s != PKV_OK) return s;
-    if (attn_events &&
-        hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)
-      return PKV_EHIP;
-  }
-  return PKV_OK;
+  // launches; whatever happens, mark the end of this step's reads of the device area
+  auto launch_all = [&]() -> pkv_status_t {
+    if (*num_cow > 0 && L > 0) {
+      pkv_status_t r =
+          pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
+      if (r != PKV_OK) return r;
+    }
+    for (int32_t l = 0; l < L; ++l) {
+      pkv_status_t r = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l],
+                                             io->k_pools[l], io->v_pools[l], d_slots, n, stream);
+      if (r != PKV_OK) return r;
+      if (attn_events &&
+          hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
+        return PKV_EHIP;
+      r = pkv_paged_attention_decode(&st->desc, io->out[l], io->q[l], io->k_pools[l],
+                                     io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
+                                     workspace, workspace_bytes, stream);
+      if (r != PKV_OK) return r;
+      if (attn_events &&
+          hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)
+        return PKV_EHIP;
+    }
+    return PKV_OK;
+  };
+  s = launch_all();
+  if (hipEventRecord(sg.consumed, hs) != hipSuccess) return PKV_EHIP;
+  sg.used = true;
+  return s;
+}
+
+const void* pkv_stepper_last_index(const pkv_stepper_t* st) {
+  return st ? st->stage[st->cur].dev : nullptr;
 }
 
 }  // extern "C"

@@ -76,11 +76,13 @@ def test_decode_argument_errors():
 def test_workspace_size_formula():
     d = _desc(h=40, d=128)
     assert pkv.decode_workspace_bytes(d, 64, 100) == 0        # single pass
-    part = pkv.decode_partition_tokens(d, 64, 2048)
-    parts = -(-2048 // part)
+    assert pkv.decode_partition_tokens(d, 64, 100) == 0
+    part = pkv.decode_partition_tokens(d, 64, 9000)
+    assert part > 0 and part % 32 == 0
+    parts = -(-9000 // part)
     slots = 64 * 40 * parts
     ml = -(-slots * 8 // 256) * 256
-    assert pkv.decode_workspace_bytes(d, 64, 2048) == ml + slots * 128 * 4
+    assert pkv.decode_workspace_bytes(d, 64, 9000) == ml + slots * 128 * 4
 
 
 def test_cache_op_argument_errors():

@@ -85,8 +85,10 @@ def parse():
     ap.add_argument("--workload", choices=WORKLOADS, default="llama13b_layer")
     ap.add_argument("--block-size", type=int, default=16, help="long_context only: 8, 16, 32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=320,
-                    help="(sequence, head) units the oracle baseline computes")
+    ap.add_argument("--cpu-units", type=int, default=2560,
+                    help="most (sequence, head) units the oracle baseline computes")
+    ap.add_argument("--cpu-bytes", type=float, default=1.6e9,
+                    help="most K+V bytes the oracle baseline reads (about 10 s of CPU work)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     return ap.parse_args()
@@ -231,7 +233,7 @@ class DecodeBatch:
         self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * self.e + 4 * nblk + 4 * self.S)
 
 
-def cpu_baseline(batch, units_wanted):
+def cpu_baseline(batch, units_wanted, bytes_wanted):
     """Time the float64 oracle on (sequence, head) units of the same workload."""
     import torch
     from threadpoolctl import threadpool_limits
@@ -241,11 +243,11 @@ def cpu_baseline(batch, units_wanted):
     q = W.from_torch(batch.q, batch.dtype)
     units, seqs, kv = [], [], 0
     for s in range(batch.S):
-        if len(units) >= units_wanted or kv >= 160e6:
+        if len(units) >= units_wanted or kv >= bytes_wanted:
             break
         seqs.append(s)
         for h in range(batch.H):
-            if len(units) < units_wanted and kv < 160e6:
+            if len(units) < units_wanted and kv < bytes_wanted:
                 units.append((s, h))
                 kv += 2 * int(lens[s]) * batch.D * batch.e
     prepared = {}
@@ -336,7 +338,7 @@ def main():
                      "alg_bytes_per_launch": int(alg_per_launch)},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(b, args.cpu_units)
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_units, args.cpu_bytes)
     print(json.dumps(res), flush=True)
 
 

@@ -93,11 +93,13 @@ const char* pkv_status_string(pkv_status_t status);
  *                 NULL when that size is 0.  Scratch for the split-context partials; its
  *                 contents need no initialization and are garbage afterwards.
  *
- * Long contexts are split into partitions of pkv_decode_partition_tokens(...) tokens, each
- * attended by its own workgroup; a second kernel merges the partial (max, sum, output)
- * triples.  The split depends only on (desc, num_seqs, max_context_len) and the reduction
- * order only on logical token order, so results are bit-identical run to run and for any
- * physical placement of the blocks.
+ * A sequence of at most pkv_decode_single_pass_max() tokens is attended by one workgroup per
+ * head.  When max_context_len exceeds that bound, longer sequences are split into partitions
+ * of pkv_decode_partition_tokens(...) tokens, each attended by its own workgroup, and a second
+ * kernel merges the partial (max, sum, output) triples.  The split depends only on the length
+ * and (desc, num_seqs, max_context_len), and the reduction order only on logical token order,
+ * so results are bit-identical run to run, for any physical placement of the blocks, and for
+ * any work-item order (pkv_paged_attention_decode_scheduled).
  *
  * A block id outside [0, num_blocks) in a block table is never dereferenced: that
  * (sequence, head) output is set to NaN instead.
@@ -108,12 +110,36 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs
                                   int32_t max_context_len);
 int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_seqs,
                                     int32_t max_context_len); /* 0: single pass, no split */
+int32_t pkv_decode_single_pass_max(void);
 pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
                                         const void* k_pool, const void* v_pool,
                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
                                         const int32_t* context_lens, int32_t num_seqs,
                                         int32_t max_context_len, float scale, void* workspace,
                                         size_t workspace_bytes, pkv_stream_t stream);
+
+/* The same attention with a host-built schedule: one workgroup per (work item, head) instead
+ * of one per (sequence, possible partition, head), so no workgroup is launched for a
+ * partition that does not exist and the longest work can be dispatched first.
+ *
+ * pkv_decode_schedule (host only) fills items (host out, `capacity` entries) with one entry
+ * per (sequence s, partition p) that the lengths `lens` (host, num_seqs entries, the values
+ * that will be in context_lens) produce under max_context_len, encoded s | p << 20, sorted
+ * by decreasing token count (ties in (s, p) order); a length-0 sequence gets one item.
+ * Returns the number of items, or -1 for bad arguments, capacity too small, num_seqs >= 2^20
+ * or more than 2^11 partitions per sequence.
+ * pkv_paged_attention_decode_scheduled takes those items in device memory (work_items,
+ * num_items).  The items must be built from the same lengths as context_lens: a partition
+ * left out leaves its output undefined (the kernels still stay inside every buffer).
+ * Outputs are bit-identical to pkv_paged_attention_decode's for any item order. */
+int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t* items, int32_t capacity);
+pkv_status_t pkv_paged_attention_decode_scheduled(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
+    const int32_t* work_items, int32_t num_items, void* workspace, size_t workspace_bytes,
+    pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Append new tokens' keys and values to the cache.
@@ -218,10 +244,12 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *      (two areas used alternately, so the host can prepare step i+1 while step i's copy is
  *      in flight);
  *   2. one asynchronous host-to-device copy of the packed index data into an area of d_index:
- *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2];
+ *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2] |
+ *      decode work items [num_items] (pkv_decode_schedule: longest work first);
  *   3. pkv_copy_blocks over every layer when there are copy-on-write pairs;
  *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]), then
- *      pkv_paged_attention_decode(q[l] -> out[l]) with the lengths including the new token.
+ *      pkv_paged_attention_decode_scheduled(q[l] -> out[l]) with the lengths including the
+ *      new token.
  * Everything after step 1 is asynchronous on `stream`.  If step 1 fails (PKV_ENOMEM: the pool
  * ran out; PKV_EINVAL: unknown sequence) nothing is launched, and the sequences before the
  * failing one have already been extended by one slot (*num_done reports how many).
@@ -248,7 +276,8 @@ typedef struct {
   float scale;
 } pkv_layer_io_t;
 
-size_t pkv_stepper_index_bytes(int32_t max_seqs, int32_t max_blocks_per_seq);
+size_t pkv_stepper_index_bytes(const pkv_cache_desc_t* desc, int32_t max_seqs,
+                               int32_t max_blocks_per_seq);
 pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
                                   int32_t max_seqs, int32_t max_blocks_per_seq, void* d_index);
 void pkv_stepper_destroy(pkv_stepper_t* st);

@@ -12,6 +12,7 @@ import os
 
 __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
+    "decode_schedule",
     "paged_attention_decode", "reshape_and_cache", "copy_blocks", "BlockAllocator",
     "DecodeStepper", "LIB_PATH",
 ]
@@ -50,6 +51,10 @@ _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_i32]),
     "pkv_decode_workspace_bytes": (_sz, [_pdesc, _i32, _i32]),
     "pkv_decode_partition_tokens": (_i32, [_pdesc, _i32, _i32]),
+    "pkv_decode_single_pass_max": (_i32, []),
+    "pkv_decode_schedule": (_i32, [_pdesc, _p, _i32, _i32, _p, _i32]),
+    "pkv_paged_attention_decode_scheduled": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32,
+                                                    _i32, _f32, _p, _i32, _p, _sz, _p]),
     "pkv_paged_attention_decode": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                                           _p, _sz, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
@@ -67,7 +72,7 @@ _SIGNATURES = {
     "pkv_alloc_num_free": (_i32, [_p]),
     "pkv_alloc_refcount": (_i32, [_p, _i32]),
     "pkv_alloc_wasted_slots": (_i64, [_p]),
-    "pkv_stepper_index_bytes": (_sz, [_i32, _i32]),
+    "pkv_stepper_index_bytes": (_sz, [_pdesc, _i32, _i32]),
     "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
     "pkv_stepper_destroy": (None, [_p]),
     "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
@@ -141,10 +146,27 @@ def decode_partition_tokens(desc: CacheDesc, num_seqs: int, max_context_len: int
     return int(_lib().pkv_decode_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len))
 
 
+def decode_schedule(desc: CacheDesc, lens, max_context_len: int):
+    """Host-built work items (longest first) for the given host lengths: int32 numpy array."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    S = int(lens.shape[0])
+    part = decode_partition_tokens(desc, S, max_context_len)
+    cap = max(1, S * (-(-max(max_context_len, 1) // part) if part else 1))
+    items = np.empty(cap, np.int32)
+    n = _lib().pkv_decode_schedule(ctypes.byref(desc), lens.ctypes.data_as(ctypes.c_void_p), S,
+                                   int(max_context_len), items.ctypes.data_as(ctypes.c_void_p),
+                                   cap)
+    if n < 0:
+        raise PkvError(PKV_EINVAL, "pkv_decode_schedule")
+    return items[:n].copy()
+
+
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
-                           max_context_len: int, workspace=None, stream=None):
+                           max_context_len: int, workspace=None, stream=None, work_items=None):
     """out[s, h] = softmax(scale * q[s, h] . K(s, :, h)) V(s, :, h) over the context_lens[s]
-    tokens of sequence s, gathered through block_tables (see include/pkv.h)."""
+    tokens of sequence s, gathered through block_tables (see include/pkv.h).  With
+    ``work_items`` (int32 device tensor from decode_schedule) the scheduled entry point runs."""
     import torch
     desc = desc_for_pool(k_pool)
     S = q.shape[0]
@@ -159,13 +181,19 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib().pkv_paged_attention_decode(
-        ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
-        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables",
-                                                              torch.int32),
-        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), S,
-        int(max_context_len), float(scale), ws_ptr, ws_bytes, _stream_ptr(stream))
-    _check(st, "pkv_paged_attention_decode")
+    args = (ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
+            _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32), S, int(max_context_len),
+            float(scale))
+    if work_items is None:
+        st = _lib().pkv_paged_attention_decode(*args, ws_ptr, ws_bytes, _stream_ptr(stream))
+        _check(st, "pkv_paged_attention_decode")
+    else:
+        st = _lib().pkv_paged_attention_decode_scheduled(
+            *args, _dev(work_items, "work_items", torch.int32), int(work_items.numel()), ws_ptr,
+            ws_bytes, _stream_ptr(stream))
+        _check(st, "pkv_paged_attention_decode_scheduled")
     return out
 
 
@@ -355,7 +383,8 @@ class DecodeStepper:
         self._arrs = [(ctypes.c_void_p * L)(*[t.data_ptr() for t in lst]) for lst in tensors]
         self.io = LayerIO(L, *[ctypes.cast(a, ctypes.c_void_p) for a in self._arrs], float(scale))
         dev = k_pools[0].device
-        nbytes = int(_lib().pkv_stepper_index_bytes(max_seqs, max_blocks_per_seq))
+        nbytes = int(_lib().pkv_stepper_index_bytes(ctypes.byref(self.desc), max_seqs,
+                                                     max_blocks_per_seq))
         self.d_index = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
         self.max_blocks = max_blocks_per_seq
         self.max_seqs = max_seqs
@@ -391,8 +420,9 @@ class DecodeStepper:
             raise PkvError(PKV_ENOMEM, "pkv_stepper_step (context grew past the workspace bound)")
         return self._max_len.value, self._ncow.value
 
-    def index_views(self, n: int, num_cow: int):
-        """Device views of the packed index data of the last step: (tables, lens, slots, pairs)."""
+    def index_views(self, n: int, num_cow: int, num_items: int = 0):
+        """Device views of the packed index data of the last step: (tables, lens, slots, pairs)
+        and, with num_items, the work items as a fifth view."""
         import torch
         base = int(_lib().pkv_stepper_last_index(self._h))
         off = (base - self.d_index.data_ptr()) // 4
@@ -402,4 +432,7 @@ class DecodeStepper:
         lens = ints[n * MB:n * MB + n]
         slots = ints[n * MB + n:n * MB + 2 * n]
         pairs = ints[n * MB + 2 * n:n * MB + 2 * n + 2 * num_cow].view(num_cow, 2)
+        if num_items:
+            o = n * MB + 2 * n + 2 * num_cow
+            return t, lens, slots, pairs, ints[o:o + num_items]
         return t, lens, slots, pairs

@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <vector>
 
 namespace pkv {
 
@@ -43,7 +44,7 @@ namespace pkv {
 #define PKV_PART_TOKENS 2048
 #endif
 #ifndef PKV_SINGLE_MAX
-#define PKV_SINGLE_MAX 2048
+#define PKV_SINGLE_MAX 4096
 #endif
 #ifndef PKV_CHUNK_BYTES
 #define PKV_CHUNK_BYTES 8192
@@ -74,6 +75,16 @@ struct DecodeCfg {
   static_assert(BS % kTPL == 0, "a wave load must not straddle two blocks");
   static_assert(kChunk % BS == 0, "chunks hold whole blocks");
 };
+
+// A sequence of at most kSingleMax tokens is attended by one workgroup per head; a longer
+// one is cut into partitions of part_tokens tokens whose partial results are merged.
+constexpr int kSingleMax = PKV_SINGLE_MAX;
+__host__ __device__ __forceinline__ int partition_len(int L, int part_tokens) {
+  return L <= kSingleMax ? (L > 0 ? L : 1) : part_tokens;
+}
+// Host-built work items: sequence index in the low 20 bits, partition index above.
+constexpr int kItemPartShift = 20;
+constexpr int kItemSeqMask = (1 << kItemPartShift) - 1;
 
 // Clamp a device-provided length to what the launch was sized for.
 __device__ __forceinline__ int effective_len(int L, int max_len) {
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     const typename Ty::store_t* __restrict__ k_pool, const typename Ty::store_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
     int num_heads, int num_blocks, int max_len, float scale_log2, int part_tokens, int max_parts,
-    float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    const int32_t* __restrict__ work, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
   using C = DecodeCfg<Ty, D, BS>;
   using T = typename Ty::store_t;
   __shared__ int sm_blk[C::kMaxBlocks];
@@ -138,19 +149,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   __shared__ float sm_l[C::kStates];
   __shared__ __attribute__((aligned(16))) float sm_acc[C::kStates][D];
 
-  // flattened grid: partition fastest, then head, then sequence
-  const int wg = blockIdx.x;
-  const int p = wg % max_parts;
-  const int sh = wg / max_parts;
-  const int h = sh % num_heads;
-  const int s = sh / num_heads;
+  // Flattened grid, head fastest: the workgroups of one (sequence, partition) run side by
+  // side and read adjacent head tiles of the same blocks.  Work item j is either listed by
+  // the host (sequence | partition << 20, longest first) or enumerated as (j / max_parts,
+  // j % max_parts).
+  const int h = blockIdx.x % num_heads;
+  const int j = blockIdx.x / num_heads;
+  int s, p;
+  if (work) {
+    const int item = work[j];
+    s = item & kItemSeqMask;
+    p = item >> kItemPartShift;
+  } else {
+    s = j / max_parts;
+    p = j % max_parts;
+  }
 
   const int L = effective_len(context_lens[s], max_len);
-  const int plen = part_tokens > 0 ? part_tokens : (L > 0 ? L : 1);
+  const int plen = partition_len(L, part_tokens);
   const int t0 = p * plen;
   if (p > 0 && t0 >= L) return;  // uniform across the workgroup
   const int t1 = min(L, t0 + plen);
-  const int nparts = part_tokens > 0 ? (L + part_tokens - 1) / part_tokens : 1;
+  const int nparts = (L + plen - 1) / plen;
 
   // This workgroup's physical block ids, read once into LDS; an id outside the pool is
   // replaced by block 0 (in bounds) and poisons the output.
@@ -296,7 +316,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
   const int h = blockIdx.x % num_heads;
   const int s = blockIdx.x / num_heads;
   const int L = effective_len(context_lens[s], max_len);
-  const int nparts = (L + part_tokens - 1) / part_tokens;
+  const int plen = partition_len(L, part_tokens);
+  const int nparts = (L + plen - 1) / plen;
   if (nparts <= 1) return;  // written by the partition kernel
   const size_t base = (static_cast<size_t>(s) * num_heads + h) * max_parts;
   const int d = threadIdx.x;
@@ -313,19 +334,22 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 
 // ------------------------------------------------------------------ host side
 constexpr int kPartTokens = PKV_PART_TOKENS;
-constexpr int kSingleMax = PKV_SINGLE_MAX;
 
 static int effective_max_len(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
   const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;
   return static_cast<int>(std::min<int64_t>(max_context_len, cap));
 }
 
-// Contexts up to kSingleMax tokens are attended by one workgroup per (sequence, head);
-// longer ones are split into kPartTokens-token partitions plus a merge.
+// 0 when every sequence fits one workgroup (max_len <= kSingleMax); otherwise the length of
+// the partitions longer sequences are cut into.
 static int partition_tokens(const pkv_cache_desc_t* d, int32_t num_seqs, int32_t max_len) {
   (void)d;
   (void)num_seqs;
   return max_len > kSingleMax ? kPartTokens : 0;
+}
+
+static int max_partitions(int max_len, int part) {
+  return part > 0 ? (max_len + part - 1) / part : 1;
 }
 
 struct DecodeArgs {
@@ -343,6 +367,8 @@ struct DecodeArgs {
   float scale_log2;
   int part_tokens;
   int max_parts;
+  const int32_t* work;  // device work items or null
+  int num_items;
   float* ws_ml;
   float* ws_o;
   hipStream_t stream;
@@ -351,13 +377,16 @@ struct DecodeArgs {
 template <class Ty, int D, int BS>
 static void launch_decode(const DecodeArgs& a) {
   using T = typename Ty::store_t;
-  const int64_t wgs = static_cast<int64_t>(a.num_seqs) * a.num_heads * a.max_parts;
-  hipLaunchKernelGGL((decode_partition_kernel<Ty, D, BS>), dim3(static_cast<unsigned>(wgs)),
-                     dim3(kDecodeThreads), 0, a.stream, static_cast<T*>(a.out),
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
-                     static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks, a.context_lens,
-                     a.num_heads, a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts,
-                     a.ws_ml, a.ws_o);
+  const int64_t items =
+      a.work ? a.num_items : static_cast<int64_t>(a.num_seqs) * a.max_parts;
+  const int64_t wgs = items * a.num_heads;
+  if (wgs > 0)
+    hipLaunchKernelGGL((decode_partition_kernel<Ty, D, BS>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(kDecodeThreads), 0, a.stream, static_cast<T*>(a.out),
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+                       static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks,
+                       a.context_lens, a.num_heads, a.num_blocks, a.max_len, a.scale_log2,
+                       a.part_tokens, a.max_parts, a.work, a.ws_ml, a.ws_o);
   if (a.part_tokens > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
     hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)), dim3(D),
@@ -385,49 +414,31 @@ static pkv_status_t dispatch_d(int dim, int bs, const DecodeArgs& a) {
   return PKV_EUNSUPPORTED;
 }
 
-}  // namespace pkv
-
-using namespace pkv;
-
-extern "C" {
-
-int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_seqs,
-                                    int32_t max_context_len) {
-  if (!desc || num_seqs < 0 || max_context_len < 0) return 0;
-  return partition_tokens(desc, num_seqs, max_context_len);
-}
-
-size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs,
-                                  int32_t max_context_len) {
-  if (!desc || num_seqs <= 0 || max_context_len <= 0 || desc->head_dim <= 0 ||
-      desc->num_heads <= 0)
-    return 0;
-  const int part = partition_tokens(desc, num_seqs, max_context_len);
-  if (part == 0) return 0;
-  const int64_t parts = (static_cast<int64_t>(max_context_len) + part - 1) / part;
-  const int64_t slots = static_cast<int64_t>(num_seqs) * desc->num_heads * parts;
-  const int64_t ml = align_up(slots * 2 * 4, 256);
-  return static_cast<size_t>(ml + slots * desc->head_dim * 4);
-}
-
-pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
-                                        const void* k_pool, const void* v_pool,
-                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                        const int32_t* context_lens, int32_t num_seqs,
-                                        int32_t max_context_len, float scale, void* workspace,
-                                        size_t workspace_bytes, pkv_stream_t stream) {
+static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len, float scale, const int32_t* work,
+                                int32_t num_items, void* workspace, size_t workspace_bytes,
+                                pkv_stream_t stream) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale))
     return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
+  if (num_seqs > kItemSeqMask + 1) return PKV_EUNSUPPORTED;
 
   const int max_len = effective_max_len(max_context_len, max_blocks_per_seq, desc->block_size);
   const int part = partition_tokens(desc, num_seqs, max_len);
-  const int max_parts = part > 0 ? (max_len + part - 1) / part : 1;
-  const int64_t wgs = static_cast<int64_t>(num_seqs) * desc->num_heads * max_parts;
-  if (wgs > INT32_MAX) return PKV_EUNSUPPORTED;
+  const int max_parts = max_partitions(max_len, part);
+  if (work) {
+    if (num_items < 0 || static_cast<int64_t>(num_items) > static_cast<int64_t>(num_seqs) * max_parts)
+      return PKV_EINVAL;
+    if (static_cast<int64_t>(num_items) * desc->num_heads > INT32_MAX) return PKV_EUNSUPPORTED;
+  } else if (static_cast<int64_t>(num_seqs) * desc->num_heads * max_parts > INT32_MAX) {
+    return PKV_EUNSUPPORTED;
+  }
 
   DecodeArgs a{};
   if (part > 0) {
@@ -452,6 +463,8 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.part_tokens = part;
   a.max_parts = max_parts;
+  a.work = work;
+  a.num_items = num_items;
   a.stream = static_cast<hipStream_t>(stream);
 
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
@@ -463,6 +476,89 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
   }
   if (st != PKV_OK) return st;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                    int32_t max_context_len) {
+  if (!desc || num_seqs < 0 || max_context_len < 0) return 0;
+  return partition_tokens(desc, num_seqs, max_context_len);
+}
+
+int32_t pkv_decode_single_pass_max(void) { return kSingleMax; }
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs,
+                                  int32_t max_context_len) {
+  if (!desc || num_seqs <= 0 || max_context_len <= 0 || desc->head_dim <= 0 ||
+      desc->num_heads <= 0)
+    return 0;
+  const int part = partition_tokens(desc, num_seqs, max_context_len);
+  if (part == 0) return 0;
+  const int64_t parts = max_partitions(max_context_len, part);
+  const int64_t slots = static_cast<int64_t>(num_seqs) * desc->num_heads * parts;
+  const int64_t ml = align_up(slots * 2 * 4, 256);
+  return static_cast<size_t>(ml + slots * desc->head_dim * 4);
+}
+
+int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t* items, int32_t capacity) {
+  if (!desc || num_seqs < 0 || max_context_len < 0 || capacity < 0 ||
+      (num_seqs > 0 && (!lens || !items)) || num_seqs > kItemSeqMask + 1)
+    return -1;
+  const int part = partition_tokens(desc, num_seqs, max_context_len);
+  struct Item {
+    int32_t tokens;
+    int32_t code;
+  };
+  std::vector<Item> list;
+  list.reserve(static_cast<size_t>(num_seqs));
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int L = lens[s] < 0 ? 0 : std::min(lens[s], max_context_len);
+    const int plen = partition_len(L, part);
+    const int n = (L + plen - 1) / plen;
+    if (n == 0) {
+      list.push_back({0, s});  // length 0: one workgroup writes the zero vector
+      continue;
+    }
+    if (n - 1 > (INT32_MAX >> kItemPartShift)) return -1;
+    for (int p = 0; p < n; ++p)
+      list.push_back({std::min(plen, L - p * plen), s | (p << kItemPartShift)});
+  }
+  if (static_cast<int64_t>(list.size()) > capacity) return -1;
+  // longest work first; ties keep (sequence, partition) order
+  std::stable_sort(list.begin(), list.end(),
+                   [](const Item& x, const Item& y) { return x.tokens > y.tokens; });
+  for (size_t i = 0; i < list.size(); ++i) items[i] = list[i].code;
+  return static_cast<int32_t>(list.size());
+}
+
+pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t max_context_len, float scale, void* workspace,
+                                        size_t workspace_bytes, pkv_stream_t stream) {
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, nullptr, 0, workspace, workspace_bytes,
+                     stream);
+}
+
+pkv_status_t pkv_paged_attention_decode_scheduled(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
+    const int32_t* work_items, int32_t num_items, void* workspace, size_t workspace_bytes,
+    pkv_stream_t stream) {
+  if (!work_items && num_items != 0) return PKV_EINVAL;
+  if (!work_items) return PKV_EINVAL;
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, work_items, num_items, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

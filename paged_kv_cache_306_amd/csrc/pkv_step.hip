@@ -20,6 +20,7 @@ struct pkv_stepper {
   pkv_cache_desc_t desc{};
   int32_t max_seqs = 0;
   int32_t max_blocks = 0;
+  int32_t max_items = 0;  // decode work items per step, at most
   hipStream_t copy_stream = nullptr;
   struct Stage {
     int32_t* host = nullptr;      // pinned: tables | lens | slots | pairs (packed for n)
@@ -34,23 +35,34 @@ struct pkv_stepper {
 
 namespace {
 
-size_t index_ints(int32_t n, int32_t max_blocks) {
-  // tables [n][max_blocks], lens [n], slots [n], pairs [n][2]
-  return static_cast<size_t>(n) * max_blocks + 4 * static_cast<size_t>(n);
+// Most decode work items n sequences with tables of max_blocks entries can produce.
+int32_t max_work_items(const pkv_cache_desc_t* d, int32_t n, int32_t max_blocks) {
+  const int64_t cap = static_cast<int64_t>(max_blocks) * d->block_size;
+  const int32_t max_ctx = static_cast<int32_t>(std::min<int64_t>(cap, INT32_MAX));
+  const int32_t part = pkv_decode_partition_tokens(d, n, max_ctx);
+  const int64_t parts = part > 0 ? (max_ctx + part - 1) / part : 1;
+  return static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(n) * parts, INT32_MAX / 8));
+}
+
+size_t index_ints(int32_t n, int32_t max_blocks, int32_t max_items) {
+  // tables [n][max_blocks], lens [n], slots [n], pairs [n][2], work items [max_items]
+  return static_cast<size_t>(n) * max_blocks + 4 * static_cast<size_t>(n) + max_items;
 }
 
 }  // namespace
 
 extern "C" {
 
-static size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq) {
-  return static_cast<size_t>(
-      pkv::align_up(static_cast<int64_t>(index_ints(max_seqs, max_blocks_per_seq) * 4), 256));
+static size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_items) {
+  return static_cast<size_t>(pkv::align_up(
+      static_cast<int64_t>(index_ints(max_seqs, max_blocks_per_seq, max_items) * 4), 256));
 }
 
-size_t pkv_stepper_index_bytes(int32_t max_seqs, int32_t max_blocks_per_seq) {
-  if (max_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
-  return 2 * stage_bytes(max_seqs, max_blocks_per_seq);
+size_t pkv_stepper_index_bytes(const pkv_cache_desc_t* desc, int32_t max_seqs,
+                               int32_t max_blocks_per_seq) {
+  if (pkv::check_desc(desc) != PKV_OK || max_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
+  return 2 * stage_bytes(max_seqs, max_blocks_per_seq,
+                         max_work_items(desc, max_seqs, max_blocks_per_seq));
 }
 
 pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
@@ -64,7 +76,8 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   st->desc = *desc;
   st->max_seqs = max_seqs;
   st->max_blocks = max_blocks_per_seq;
-  const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq);
+  st->max_items = max_work_items(desc, max_seqs, max_blocks_per_seq);
+  const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq, st->max_items);
   if (hipStreamCreateWithFlags(&st->copy_stream, hipStreamNonBlocking) != hipSuccess) {
     st->copy_stream = nullptr;
     pkv_stepper_destroy(st);
@@ -132,8 +145,12 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   s = pkv_alloc_export(st->alloc, seqs, n, MB, tables, lens);
   if (s != PKV_OK) return s;
   *max_len = *std::max_element(lens, lens + n);
+  int32_t* items = pairs + 2 * static_cast<size_t>(*num_cow);
+  const int32_t num_items = pkv_decode_schedule(&st->desc, lens, n, *max_len, items, st->max_items);
+  if (num_items < 0) return PKV_EINVAL;
 
-  const size_t used = (index_ints(n, MB) - 2 * static_cast<size_t>(n - *num_cow)) * sizeof(int32_t);
+  const size_t used = (static_cast<size_t>(n) * MB + 2 * static_cast<size_t>(n) +
+                       2 * static_cast<size_t>(*num_cow) + num_items) * sizeof(int32_t);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   // upload after the last reader of this device area, then make the kernels wait for it
@@ -149,6 +166,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;
   const int32_t* d_slots = d_lens + n;
   const int32_t* d_pairs = d_slots + n;
+  const int32_t* d_items = d_pairs + 2 * static_cast<size_t>(*num_cow);
 
   // launches; whatever happens, mark the end of this step's reads of the device area
   auto launch_all = [&]() -> pkv_status_t {
@@ -164,9 +182,9 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       if (attn_events &&
           hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
         return PKV_EHIP;
-      r = pkv_paged_attention_decode(&st->desc, io->out[l], io->q[l], io->k_pools[l],
-                                     io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
-                                     workspace, workspace_bytes, stream);
+      r = pkv_paged_attention_decode_scheduled(
+          &st->desc, io->out[l], io->q[l], io->k_pools[l], io->v_pools[l], d_tables, MB, d_lens,
+          n, *max_len, io->scale, d_items, num_items, workspace, workspace_bytes, stream);
       if (r != PKV_OK) return r;
       if (attn_events &&
           hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)

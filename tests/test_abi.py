@@ -65,12 +65,49 @@ def test_decode_argument_errors():
     assert _decode(_desc(), S=0) == pkv.PKV_OK                    # nothing to do
     # a split launch needs workspace
     d = _desc()
-    assert pkv.decode_partition_tokens(d, 2, 4096) > 0
-    need = pkv.decode_workspace_bytes(d, 2, 4096)
+    big = pkv.lib().pkv_decode_single_pass_max() + 1000
+    assert pkv.decode_partition_tokens(d, 2, big) > 0
+    need = pkv.decode_workspace_bytes(d, 2, big)
     assert need > 0
-    assert _decode(d, mb=256, maxlen=4096, ws=None, wsb=0) == pkv.PKV_ENOMEM
-    assert _decode(d, mb=256, maxlen=4096, ws=FAKE, wsb=need - 1) == pkv.PKV_ENOMEM
-    assert _decode(d, mb=256, maxlen=4096, ws=ctypes.c_void_p(0x1004), wsb=need) == pkv.PKV_EINVAL
+    mb = -(-big // 16)
+    assert _decode(d, mb=mb, maxlen=big, ws=None, wsb=0) == pkv.PKV_ENOMEM
+    assert _decode(d, mb=mb, maxlen=big, ws=FAKE, wsb=need - 1) == pkv.PKV_ENOMEM
+    assert _decode(d, mb=mb, maxlen=big, ws=ctypes.c_void_p(0x1004), wsb=need) == pkv.PKV_EINVAL
+    # the scheduled entry point needs a work list, and no more items than partitions
+    lib = pkv.lib()
+    args = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1)
+    assert lib.pkv_paged_attention_decode_scheduled(*args, None, 0, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, 3, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, -1, None, 0, None) == pkv.PKV_EINVAL
+
+
+def test_decode_schedule_covers_every_partition_longest_first():
+    import numpy as np
+    d = _desc(h=40, d=128)
+    single = pkv.lib().pkv_decode_single_pass_max()
+    lens = np.array([0, 1, 17, single, single + 1, 3 * single + 5, 900, single * 2], np.int32)
+    max_len = int(lens.max())
+    part = pkv.decode_partition_tokens(d, len(lens), max_len)
+    items = pkv.decode_schedule(d, lens, max_len)
+    seqs, parts = items & ((1 << 20) - 1), items >> 20
+    want = []
+    for s, L in enumerate(lens.tolist()):
+        plen = max(L, 1) if L <= single else part
+        n = max(1, -(-L // plen))
+        want += [(s, p) for p in range(n)]
+    assert sorted(zip(seqs.tolist(), parts.tolist())) == sorted(want)
+    tokens = [min(max(lens[s], 1) if lens[s] <= single else part,
+                  lens[s] - p * (part if lens[s] > single else 0)) for s, p in zip(seqs, parts)]
+    assert tokens == sorted(tokens, reverse=True)
+    # without any long sequence everything is one item per sequence, longest first
+    short = np.array([5, 300, 2, 300, 40], np.int32)
+    it = pkv.decode_schedule(d, short, 300)
+    assert it.tolist() == [1, 3, 4, 0, 2]
+    # too small a buffer and bad sizes are errors
+    buf = np.empty(2, np.int32)
+    assert pkv.lib().pkv_decode_schedule(ctypes.byref(d), short.ctypes.data_as(ctypes.c_void_p),
+                                         5, 300, buf.ctypes.data_as(ctypes.c_void_p), 2) == -1
+    assert pkv.lib().pkv_decode_schedule(ctypes.byref(d), None, 5, 300, None, 8) == -1
 
 
 def test_workspace_size_formula():

@@ -68,7 +68,7 @@ SHAPES = [(dt, D, BS) for dt in ("f32", "f16", "bf16") for D in (64, 128) for BS
 @pytest.mark.parametrize("dtype,D,BS", SHAPES, ids=lambda v: str(v))
 def test_ragged_multi_partition(dtype, D, BS):
     dev = device()
-    lens = [0, 1, BS - 1, BS, BS + 1, 511, 512, 513, 1300, 2100]
+    lens = [0, 1, BS - 1, BS, BS + 1, 511, 512, 513, 1300, 2100, 4095, 4096, 4097, 9000]
     S, H = len(lens), 3
     q, kp, vp, tables, lens = make_case(7 + D + BS, S, H, D, BS, lens, dtype)
     scale = float(np.float32(1 / math.sqrt(D)))
@@ -76,6 +76,33 @@ def test_ragged_multi_partition(dtype, D, BS):
     ref = oracle.paged_attention_decode(q, kp, vp, tables, lens, scale, dtype)
     check_close(oracle.decode(got, dtype), ref, dtype, f"{dtype} D{D} BS{BS}")
     assert not oracle.decode(got[0], dtype).any(), "length 0 must give zeros"
+
+
+@pytest.mark.parametrize("dtype,D,BS", [("f16", 128, 16), ("bf16", 64, 8), ("f32", 128, 32)])
+def test_scheduled_decode_bit_identical(dtype, D, BS):
+    """The host-built work list (longest first, or shuffled) gives the same bits as the
+    enumerated grid, in single-pass and split sequences alike."""
+    import torch
+    dev = device()
+    lens = [3, 4096, 4097, 700, 0, 12000, 2048, 33]
+    S, H = len(lens), 4
+    q, kp, vp, tables, lens = make_case(91 + D, S, H, D, BS, lens, dtype)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    plain = run_decode(q, kp, vp, tables, lens, scale, dtype, dev)
+    desc = pkv.CacheDesc(kp.shape[0], H, BS, D, {"f32": 0, "f16": 1, "bf16": 2}[dtype])
+    items = pkv.decode_schedule(desc, lens, int(lens.max()))
+    shuffled = W.rng(5).permutation(items).astype(np.int32)
+    for order in (items, shuffled):
+        qt, kt, vt = to_dev(q, dtype, dev), to_dev(kp, dtype, dev), to_dev(vp, dtype, dev)
+        out = torch.empty_like(qt)
+        pkv.paged_attention_decode(out, qt, kt, vt, torch.from_numpy(tables).to(dev),
+                                   torch.from_numpy(lens).to(dev), scale, int(lens.max()),
+                                   work_items=torch.from_numpy(order).to(dev))
+        torch.cuda.synchronize()
+        got = W.from_torch(out, dtype)
+        assert np.array_equal(got.view(np.uint8), plain.view(np.uint8))
+    ref = oracle.paged_attention_decode(q, kp, vp, tables, lens, scale, dtype)
+    check_close(oracle.decode(plain, dtype), ref, dtype, f"{dtype} D{D} BS{BS}")
 
 
 def test_placement_invariance_and_determinism():

@@ -66,7 +66,10 @@ def test_small_two_layer_step_with_copy_on_write():
 
     mslots, mpairs, _ = m.append_slots(seqs.tolist())
     assert ncow == len(mpairs) == 3          # 0's partial block shared by 3, 1's by 2
-    tables, lens, slots, pairs = [x.cpu().numpy() for x in st.index_views(S, ncow)]
+    n_items = len(pkv.decode_schedule(st.desc, np.array([m.seq_len(int(s)) for s in seqs]),
+                                      max_len))
+    tables, lens, slots, pairs, items = [x.cpu().numpy() for x in st.index_views(S, ncow, n_items)]
+    assert items.tolist() == pkv.decode_schedule(st.desc, lens, max_len).tolist()
     assert slots.tolist() == mslots
     assert [tuple(p) for p in pairs.tolist()] == mpairs
     assert lens.tolist() == [m.seq_len(int(s)) for s in seqs] and max_len == lens.max()

@@ -83,7 +83,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--placement", choices=["permuted", "contiguous"], default="permuted")
     ap.add_argument("--workload", choices=WORKLOADS, default="llama13b_layer")
-    ap.add_argument("--block-size", type=int, default=16, help="long_context only: 8, 16, 32")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="block size of the llama13b_layer / long_context workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="block size x placement sweep of the llama13b_layer and long_context "
+                         "workloads: one JSON line per configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=2560,
                     help="most (sequence, head) units the oracle baseline computes")
@@ -115,9 +119,11 @@ def workload_spec(name: str, seed: int, block_size: int, placement: str):
     import workloads as W
     if name == "llama13b_layer":
         w = W.llama13b_layer(seed)
-        spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
-                    lens=w.lens.astype(np.int64), NB=w.num_blocks, growth=64, groups=0,
-                    desc="64 seqs, 40 heads, head_dim 128, BS 16, lengths U[128,2048], fp16")
+        need = sum(W.nblocks_for(int(L), block_size) for L in w.lens)
+        spec = dict(S=w.S, H=w.H, D=w.D, BS=block_size, dtype=w.dtype, scale=w.scale, layers=1,
+                    lens=w.lens.astype(np.int64), NB=int(math.ceil(1.2 * need)), growth=64,
+                    groups=0, desc=f"64 seqs, 40 heads, head_dim 128, BS {block_size}, lengths "
+                                   "U[128,2048], fp16")
     elif name == "long_context":
         w = W.long_context(seed=4, block_size=block_size)
         spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
@@ -271,6 +277,37 @@ def cpu_baseline(batch, units_wanted, bytes_wanted):
             "seq_layer_per_s": len(units) / batch.H / dt}
 
 
+def sweep(args):
+    """Block-size x placement microbenchmark: attention throughput and KV waste."""
+    import torch
+    dev = torch.device("cuda:0")
+    for wl in ("llama13b_layer", "long_context"):
+        for bs in (8, 16, 32):
+            for placement in ("permuted", "contiguous"):
+                args.workload, args.block_size, args.placement = wl, bs, placement
+                b = DecodeBatch(args, dev)
+                for _ in range(args.warmup):
+                    b.step()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    b.step()
+                torch.cuda.synchronize()
+                wall = time.perf_counter() - t0
+                used = int(sum(b.alloc.block_table(int(s)).__len__() for s in b.seq_ids))
+                waste = b.alloc.wasted_slots()
+                kv = float(np.mean(b.kv_bytes[-args.steps:]))
+                print(json.dumps({
+                    "sweep": "block_size x placement", "workload": f"{wl}_{b.dtype}",
+                    "block_size": bs, "placement": placement,
+                    "ms_per_step": round(wall / args.steps * 1e3, 4),
+                    "kv_GBs": round(kv * args.steps / wall / 1e9, 1),
+                    "allocated_slots": used * bs, "wasted_slots": int(waste),
+                    "waste_frac": round(waste / max(1, used * bs), 5)}), flush=True)
+                del b
+                torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -279,6 +316,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.sweep:
+        sweep(args)
         return
     import torch
     dev = torch.device("cuda:0")

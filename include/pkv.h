@@ -128,18 +128,29 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
  * by decreasing token count (ties in (s, p) order); a length-0 sequence gets one item.
  * Returns the number of items, or -1 for bad arguments, capacity too small, num_seqs >= 2^20
  * or more than 2^11 partitions per sequence.
+ * pkv_decode_schedule_grouped does the same but keeps sequences with equal group_keys (host,
+ * num_seqs entries; e.g. each sequence's first physical block, equal for sequences that share
+ * a prefix) adjacent: groups are ordered by their longest item, and inside a group items go
+ * partition by partition, so the members read their shared blocks at the same time.
  * pkv_paged_attention_decode_scheduled takes those items in device memory (work_items,
  * num_items).  The items must be built from the same lengths as context_lens: a partition
  * left out leaves its output undefined (the kernels still stay inside every buffer).
- * Outputs are bit-identical to pkv_paged_attention_decode's for any item order. */
+ * flags: 0, or PKV_DECODE_SHARED_KV when sequences of the batch share blocks -- K/V are then
+ * read with ordinary (cache-allocating) loads so a block shared by a group is fetched from
+ * HBM once, instead of the nontemporal loads used for K/V read by one sequence only.
+ * Outputs are bit-identical to pkv_paged_attention_decode's for any item order and flags. */
+#define PKV_DECODE_SHARED_KV 1u
 int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, int32_t num_seqs,
                             int32_t max_context_len, int32_t* items, int32_t capacity);
+int32_t pkv_decode_schedule_grouped(const pkv_cache_desc_t* desc, const int32_t* lens,
+                                    const int32_t* group_keys, int32_t num_seqs,
+                                    int32_t max_context_len, int32_t* items, int32_t capacity);
 pkv_status_t pkv_paged_attention_decode_scheduled(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
-    const int32_t* work_items, int32_t num_items, void* workspace, size_t workspace_bytes,
-    pkv_stream_t stream);
+    const int32_t* work_items, int32_t num_items, uint32_t flags, void* workspace,
+    size_t workspace_bytes, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Append new tokens' keys and values to the cache.
@@ -196,6 +207,18 @@ pkv_status_t pkv_copy_blocks(const pkv_cache_desc_t* desc, void* const* k_pools,
  *                         replaces it in this sequence's table and (src, dst) is reported
  *                         for pkv_copy_blocks; the last holder writes in place.
  *   free_seq(seq)         drop one reference from each block; blocks at zero are freed
+ *   add_seq_cached(seq, tokens, len)  prefix cache ("Advanced Features" -> "Prefix Caching":
+ *                         cached prefix blocks are reused by later requests): a full prompt
+ *                         block is keyed by its block_size token ids and the key of the block
+ *                         before it; the leading full blocks found in the cache are shared
+ *                         (one more reference each), the rest are fresh and the fresh full
+ *                         blocks are entered in the cache (the caller fills their K/V before
+ *                         any later lookup relies on them).  *cached_tokens = tokens whose K/V
+ *                         is already present.  The trailing partial block is never cached.
+ *                         A cached block whose last reference goes is parked, not freed;
+ *                         blocks come from the plain free list first, then by evicting the
+ *                         block parked longest ago (which leaves the cache).
+ * num_free counts plain free and parked blocks.
  * Errors: PKV_EINVAL for an unknown or duplicate sequence id or a null argument;
  * PKV_ENOMEM when the pool has no free block -- the state is then left unchanged.
  * ---------------------------------------------------------------------------------------*/
@@ -226,6 +249,9 @@ pkv_status_t pkv_alloc_export(const pkv_alloc_t* a, const int64_t* seqs, int32_t
                               int32_t max_blocks, int32_t* tables, int32_t* lens);
 int32_t pkv_alloc_seq_len(const pkv_alloc_t* a, int64_t seq); /* -1 if unknown */
 int32_t pkv_alloc_num_free(const pkv_alloc_t* a);
+pkv_status_t pkv_alloc_add_seq_cached(pkv_alloc_t* a, int64_t seq, const int32_t* tokens,
+                                      int32_t len, int32_t* cached_tokens);
+int32_t pkv_alloc_num_cached(const pkv_alloc_t* a); /* blocks in the prefix cache */
 int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block); /* -1 if out of range */
 /* Unused slots of blocks in use: per block, block_size minus the most tokens any sequence
  * keeps in it ("Memory Efficiency": 100 tokens in 16-token blocks waste 12 slots). */
@@ -245,7 +271,9 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *      in flight);
  *   2. one asynchronous host-to-device copy of the packed index data into an area of d_index:
  *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2] |
- *      decode work items [num_items] (pkv_decode_schedule: longest work first);
+ *      decode work items [num_items] -- longest work first (pkv_decode_schedule) or, when
+ *      sequences share their first block, grouped by it (pkv_decode_schedule_grouped) and
+ *      decoded with PKV_DECODE_SHARED_KV;
  *   3. pkv_copy_blocks over every layer when there are copy-on-write pairs;
  *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]), then
  *      pkv_paged_attention_decode_scheduled(q[l] -> out[l]) with the lengths including the

@@ -26,8 +26,21 @@ Readings where the pages are silent:
   * a write that starts a new block never copies anything, even if earlier blocks are shared;
   * wasted slots = for every physical block in use, block_size minus the largest number of
     valid tokens any sequence keeps in it.
+
+Prefix cache ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" ->
+"Prefix Caching": the KV blocks of a shared prompt prefix are cached by the first request and
+reused by later ones, which skip recomputing it).  Readings:
+  * a full prompt block is identified by its own block_size token ids together with the
+    identity of the block before it (so equal token runs after different prefixes differ);
+    identities are fresh numbers that are never reused;
+  * the trailing partial block of a prompt is never cached;
+  * a cached block whose last reference goes away is kept, parked in the order it was parked;
+    new blocks come from the plain free list first and only then by evicting the block parked
+    longest ago; a cache hit on a parked block takes it back.
 """
 from __future__ import annotations
+
+from collections import OrderedDict
 
 
 class OutOfBlocks(Exception):
@@ -47,12 +60,22 @@ class BlockManager:
         self.ref = [0] * num_blocks
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.cache: dict[tuple, int] = {}     # (parent identity, tokens) -> block
+        self.ident = [0] * num_blocks         # identity of a cached block, 0 if not cached
+        self.key_of: dict[int, tuple] = {}
+        self.parked: OrderedDict[int, None] = OrderedDict()   # oldest first
+        self._next_ident = 1
 
     # -- free list ---------------------------------------------------------------------
     def _take(self) -> int:
-        if not self._free:
+        if self._free:
+            b = self._free.pop()
+        elif self.parked:
+            b, _ = self.parked.popitem(last=False)      # parked longest ago
+            del self.cache[self.key_of.pop(b)]
+            self.ident[b] = 0
+        else:
             raise OutOfBlocks()
-        b = self._free.pop()
         assert self.ref[b] == 0
         self.ref[b] = 1
         return b
@@ -61,7 +84,10 @@ class BlockManager:
         assert self.ref[b] > 0
         self.ref[b] -= 1
         if self.ref[b] == 0:
-            self._free.append(b)
+            if self.ident[b]:
+                self.parked[b] = None
+            else:
+                self._free.append(b)
 
     # -- sequences ---------------------------------------------------------------------
     def add_seq(self, seq: int, length: int) -> None:
@@ -69,10 +95,48 @@ class BlockManager:
         if seq in self.tables or length < 0:
             raise ValueError("bad sequence")
         n = -(-length // self.block_size)
-        if n > len(self._free):
+        if n > self.num_free():
             raise OutOfBlocks()
         self.tables[seq] = [self._take() for _ in range(n)]
         self.lens[seq] = length
+
+    def add_seq_cached(self, seq: int, tokens) -> int:
+        """A new sequence whose prompt is ``tokens``: its leading full blocks that are in the
+        prefix cache are shared (one more reference each); the rest are fresh, and the fresh
+        full blocks are entered in the cache.  Returns the number of prompt tokens whose K/V
+        is already present (the cached blocks' tokens)."""
+        if seq in self.tables:
+            raise ValueError("bad sequence")
+        tokens = [int(t) for t in tokens]
+        BS = self.block_size
+        full, n = len(tokens) // BS, -(-len(tokens) // BS)
+        hits, parent = [], 0
+        for j in range(full):
+            b = self.cache.get((parent, tuple(tokens[j * BS:(j + 1) * BS])))
+            if b is None:
+                break
+            hits.append(b)
+            parent = self.ident[b]
+        if n - len(hits) > self.num_free() - sum(1 for b in hits if b in self.parked):
+            raise OutOfBlocks()
+        table = []
+        for b in hits:
+            self.parked.pop(b, None)
+            self.ref[b] += 1
+            table.append(b)
+        for j in range(len(hits), n):
+            b = self._take()
+            table.append(b)
+            if j < full:
+                key = (parent, tuple(tokens[j * BS:(j + 1) * BS]))
+                self.cache[key] = b
+                self.key_of[b] = key
+                self.ident[b] = self._next_ident
+                self._next_ident += 1
+                parent = self.ident[b]
+        self.tables[seq] = table
+        self.lens[seq] = len(tokens)
+        return len(hits) * BS
 
     def fork(self, parent: int, child: int) -> None:
         """The child shares every block of the parent; each gains one reference."""
@@ -132,7 +196,11 @@ class BlockManager:
 
     # -- queries -----------------------------------------------------------------------
     def num_free(self) -> int:
-        return len(self._free)
+        """Blocks that can be handed out: plain free ones and parked cached ones."""
+        return len(self._free) + len(self.parked)
+
+    def num_cached(self) -> int:
+        return len(self.cache)
 
     def block_table(self, seq: int) -> list[int]:
         return list(self.tables[seq])

@@ -53,8 +53,10 @@ _SIGNATURES = {
     "pkv_decode_partition_tokens": (_i32, [_pdesc, _i32, _i32]),
     "pkv_decode_single_pass_max": (_i32, []),
     "pkv_decode_schedule": (_i32, [_pdesc, _p, _i32, _i32, _p, _i32]),
+    "pkv_decode_schedule_grouped": (_i32, [_pdesc, _p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_decode_scheduled": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32,
-                                                    _i32, _f32, _p, _i32, _p, _sz, _p]),
+                                                    _i32, _f32, _p, _i32, ctypes.c_uint32, _p,
+                                                    _sz, _p]),
     "pkv_paged_attention_decode": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                                           _p, _sz, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
@@ -72,6 +74,8 @@ _SIGNATURES = {
     "pkv_alloc_num_free": (_i32, [_p]),
     "pkv_alloc_refcount": (_i32, [_p, _i32]),
     "pkv_alloc_wasted_slots": (_i64, [_p]),
+    "pkv_alloc_add_seq_cached": (_i32, [_p, _i64, _p, _i32, _pi32]),
+    "pkv_alloc_num_cached": (_i32, [_p]),
     "pkv_stepper_index_bytes": (_sz, [_pdesc, _i32, _i32]),
     "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
     "pkv_stepper_destroy": (None, [_p]),
@@ -146,24 +150,38 @@ def decode_partition_tokens(desc: CacheDesc, num_seqs: int, max_context_len: int
     return int(_lib().pkv_decode_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len))
 
 
-def decode_schedule(desc: CacheDesc, lens, max_context_len: int):
-    """Host-built work items (longest first) for the given host lengths: int32 numpy array."""
+PKV_DECODE_SHARED_KV = 1
+
+
+def decode_schedule(desc: CacheDesc, lens, max_context_len: int, group_keys=None):
+    """Host-built work items for the given host lengths (int32 numpy array): longest first,
+    or with ``group_keys`` grouped by key (sequences sharing a prefix side by side)."""
     import numpy as np
     lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
     S = int(lens.shape[0])
     part = decode_partition_tokens(desc, S, max_context_len)
     cap = max(1, S * (-(-max(max_context_len, 1) // part) if part else 1))
     items = np.empty(cap, np.int32)
-    n = _lib().pkv_decode_schedule(ctypes.byref(desc), lens.ctypes.data_as(ctypes.c_void_p), S,
-                                   int(max_context_len), items.ctypes.data_as(ctypes.c_void_p),
-                                   cap)
+    if group_keys is None:
+        n = _lib().pkv_decode_schedule(ctypes.byref(desc), lens.ctypes.data_as(ctypes.c_void_p),
+                                       S, int(max_context_len),
+                                       items.ctypes.data_as(ctypes.c_void_p), cap)
+    else:
+        keys = np.ascontiguousarray(np.asarray(group_keys, dtype=np.int32))
+        if keys.shape != (S,):
+            raise ValueError("one group key per sequence")
+        n = _lib().pkv_decode_schedule_grouped(
+            ctypes.byref(desc), lens.ctypes.data_as(ctypes.c_void_p),
+            keys.ctypes.data_as(ctypes.c_void_p), S, int(max_context_len),
+            items.ctypes.data_as(ctypes.c_void_p), cap)
     if n < 0:
         raise PkvError(PKV_EINVAL, "pkv_decode_schedule")
     return items[:n].copy()
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
-                           max_context_len: int, workspace=None, stream=None, work_items=None):
+                           max_context_len: int, workspace=None, stream=None, work_items=None,
+                           shared_kv: bool = False):
     """out[s, h] = softmax(scale * q[s, h] . K(s, :, h)) V(s, :, h) over the context_lens[s]
     tokens of sequence s, gathered through block_tables (see include/pkv.h).  With
     ``work_items`` (int32 device tensor from decode_schedule) the scheduled entry point runs."""
@@ -187,12 +205,14 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
             _dev(context_lens, "context_lens", torch.int32), S, int(max_context_len),
             float(scale))
     if work_items is None:
+        if shared_kv:
+            raise ValueError("shared_kv needs a work list (the scheduled entry point)")
         st = _lib().pkv_paged_attention_decode(*args, ws_ptr, ws_bytes, _stream_ptr(stream))
         _check(st, "pkv_paged_attention_decode")
     else:
         st = _lib().pkv_paged_attention_decode_scheduled(
-            *args, _dev(work_items, "work_items", torch.int32), int(work_items.numel()), ws_ptr,
-            ws_bytes, _stream_ptr(stream))
+            *args, _dev(work_items, "work_items", torch.int32), int(work_items.numel()),
+            PKV_DECODE_SHARED_KV if shared_kv else 0, ws_ptr, ws_bytes, _stream_ptr(stream))
         _check(st, "pkv_paged_attention_decode_scheduled")
     return out
 
@@ -262,6 +282,20 @@ class BlockAllocator:
 
     def add_seq(self, seq: int, length: int):
         _check(_lib().pkv_alloc_add_seq(self._h, seq, length), "pkv_alloc_add_seq")
+
+    def add_seq_cached(self, seq: int, tokens) -> int:
+        """New sequence with prompt ``tokens``; shares cached prefix blocks.  Returns the
+        number of prompt tokens whose K/V is already in the cache."""
+        import numpy as np
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        cached = _i32()
+        _check(_lib().pkv_alloc_add_seq_cached(self._h, seq, t.ctypes.data_as(ctypes.c_void_p),
+                                               int(t.shape[0]), ctypes.byref(cached)),
+               "pkv_alloc_add_seq_cached")
+        return cached.value
+
+    def num_cached(self) -> int:
+        return int(_lib().pkv_alloc_num_cached(self._h))
 
     def fork(self, parent: int, child: int):
         _check(_lib().pkv_alloc_fork(self._h, parent, child), "pkv_alloc_fork")

@@ -8,10 +8,19 @@
 // Per decode step the scheduler calls pkv_alloc_append_slots once for the whole batch; the
 // slots go to pkv_reshape_and_cache and the (src, dst) pairs to pkv_copy_blocks, which must
 // run first on the same stream.
+//
+// Prefix cache ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" ->
+// "Prefix Caching": the KV blocks of a common prefix are kept and reused by later requests).
+// A full prompt block is keyed by (key id of the previous block, its block_size token ids);
+// key ids are never reused, so an entry whose chain was evicted can never match again.  An
+// unreferenced cached block is not freed but parked in least-recently-freed order; blocks are
+// handed out from the plain free list first and only then by evicting the oldest parked one.
 #include "pkv.h"
 
 #include <algorithm>
 #include <cstring>
+#include <list>
+#include <map>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -27,14 +36,53 @@ struct pkv_alloc {
   };
   std::unordered_map<int64_t, Seq> seqs;
 
+  // prefix cache
+  using Key = std::pair<int64_t, std::vector<int32_t>>;  // (parent key id, tokens)
+  std::map<Key, int32_t> index;                           // key -> block
+  std::vector<int64_t> key_id;                            // per block; 0 = not cached
+  std::vector<std::map<Key, int32_t>::iterator> key_of;   // per cached block
+  std::list<int32_t> parked;                              // unreferenced cached, oldest first
+  std::vector<std::list<int32_t>::iterator> park_pos;
+  std::vector<char> is_parked;
+  int64_t next_key = 1;
+
+  int32_t available() const {
+    return static_cast<int32_t>(free_stack.size() + parked.size());
+  }
+  void uncache(int32_t b) {
+    index.erase(key_of[b]);
+    key_id[b] = 0;
+  }
   int32_t take() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {  // evict the least recently parked cached block
+      b = parked.front();
+      parked.pop_front();
+      is_parked[b] = 0;
+      uncache(b);
+    }
     ref[b] = 1;
     return b;
   }
   void drop(int32_t b) {
-    if (--ref[b] == 0) free_stack.push_back(b);
+    if (--ref[b] == 0) {
+      if (key_id[b] != 0) {
+        park_pos[b] = parked.insert(parked.end(), b);
+        is_parked[b] = 1;
+      } else {
+        free_stack.push_back(b);
+      }
+    }
+  }
+  void reuse(int32_t b) {  // a cache hit: one more reference
+    if (is_parked[b]) {
+      parked.erase(park_pos[b]);
+      is_parked[b] = 0;
+    }
+    ++ref[b];
   }
 };
 
@@ -47,6 +95,10 @@ pkv_alloc_t* pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int3
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->ref.assign(num_blocks, 0);
+  a->key_id.assign(num_blocks, 0);
+  a->key_of.resize(num_blocks);
+  a->park_pos.resize(num_blocks);
+  a->is_parked.assign(num_blocks, 0);
   a->free_stack.resize(num_blocks);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -70,7 +122,7 @@ void pkv_alloc_destroy(pkv_alloc_t* a) { delete a; }
 pkv_status_t pkv_alloc_add_seq(pkv_alloc_t* a, int64_t seq, int32_t len) {
   if (!a || len < 0 || a->seqs.count(seq)) return PKV_EINVAL;
   int64_t n = (static_cast<int64_t>(len) + a->block_size - 1) / a->block_size;
-  if (n > static_cast<int64_t>(a->free_stack.size())) return PKV_ENOMEM;
+  if (n > a->available()) return PKV_ENOMEM;
   pkv_alloc::Seq s;
   s.len = len;
   s.table.reserve(static_cast<size_t>(n));
@@ -100,10 +152,10 @@ pkv_status_t pkv_alloc_append_slot(pkv_alloc_t* a, int64_t seq, int32_t* slot, i
   const int32_t off = s.len % a->block_size;
   int32_t src = -1, dst = -1;
   if (j == static_cast<int32_t>(s.table.size())) {
-    if (a->free_stack.empty()) return PKV_ENOMEM;
+    if (a->available() == 0) return PKV_ENOMEM;
     s.table.push_back(a->take());
   } else if (a->ref[s.table[j]] > 1) {
-    if (a->free_stack.empty()) return PKV_ENOMEM;
+    if (a->available() == 0) return PKV_ENOMEM;
     src = s.table[j];
     dst = a->take();
     --a->ref[src];
@@ -182,8 +234,57 @@ int32_t pkv_alloc_seq_len(const pkv_alloc_t* a, int64_t seq) {
   return it == a->seqs.end() ? -1 : it->second.len;
 }
 
-int32_t pkv_alloc_num_free(const pkv_alloc_t* a) {
-  return a ? static_cast<int32_t>(a->free_stack.size()) : -1;
+int32_t pkv_alloc_num_free(const pkv_alloc_t* a) { return a ? a->available() : -1; }
+
+int32_t pkv_alloc_num_cached(const pkv_alloc_t* a) {
+  return a ? static_cast<int32_t>(a->index.size()) : -1;
+}
+
+pkv_status_t pkv_alloc_add_seq_cached(pkv_alloc_t* a, int64_t seq, const int32_t* tokens,
+                                      int32_t len, int32_t* cached_tokens) {
+  if (!a || len < 0 || (len > 0 && !tokens) || !cached_tokens || a->seqs.count(seq))
+    return PKV_EINVAL;
+  const int32_t BS = a->block_size;
+  const int32_t full = len / BS;
+  const int32_t n = (len + BS - 1) / BS;
+  // 1. the longest chain of cached full blocks
+  std::vector<int32_t> hits;
+  int64_t parent = 0;
+  for (int32_t j = 0; j < full; ++j) {
+    pkv_alloc::Key key(parent, std::vector<int32_t>(tokens + static_cast<size_t>(j) * BS,
+                                                    tokens + static_cast<size_t>(j + 1) * BS));
+    auto it = a->index.find(key);
+    if (it == a->index.end()) break;
+    hits.push_back(it->second);
+    parent = a->key_id[it->second];
+  }
+  // 2. room for the rest (a hit on a parked block takes it off the parked list)
+  int32_t parked_hits = 0;
+  for (int32_t b : hits) parked_hits += a->is_parked[b] ? 1 : 0;
+  if (n - static_cast<int32_t>(hits.size()) > a->available() - parked_hits) return PKV_ENOMEM;
+  pkv_alloc::Seq s;
+  s.len = len;
+  s.table.reserve(static_cast<size_t>(n));
+  for (int32_t b : hits) {
+    a->reuse(b);
+    s.table.push_back(b);
+  }
+  // 3. fresh blocks; full ones are registered (the caller fills them before any later lookup)
+  for (int32_t j = static_cast<int32_t>(hits.size()); j < n; ++j) {
+    const int32_t b = a->take();
+    s.table.push_back(b);
+    if (j < full) {
+      pkv_alloc::Key key(parent, std::vector<int32_t>(tokens + static_cast<size_t>(j) * BS,
+                                                      tokens + static_cast<size_t>(j + 1) * BS));
+      auto ins = a->index.emplace(std::move(key), b);
+      a->key_of[b] = ins.first;
+      a->key_id[b] = a->next_key++;
+      parent = a->key_id[b];
+    }
+  }
+  *cached_tokens = static_cast<int32_t>(hits.size()) * BS;
+  a->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
 }
 
 int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block) {

@@ -135,7 +135,7 @@ struct RowState {
   }
 };
 
-template <class Ty, int D, int BS>
+template <class Ty, int D, int BS, bool NT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     typename Ty::store_t* __restrict__ out, const typename Ty::store_t* __restrict__ q,
     const typename Ty::store_t* __restrict__ k_pool, const typename Ty::store_t* __restrict__ v_pool,
@@ -217,8 +217,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
 #pragma unroll
       for (int u = 0; u < kPerBlock; ++u) {
         const uint32_t off = lane_off + static_cast<uint32_t>(u * C::kTPL * D * sizeof(T));
-        kr[b * kPerBlock + u] = load16(kb + off);
-        vr[b * kPerBlock + u] = load16(vb + off);
+        kr[b * kPerBlock + u] = load16<NT>(kb + off);
+        vr[b * kPerBlock + u] = load16<NT>(vb + off);
       }
     }
     // keep every load of the chunk ahead of the arithmetic that consumes it
@@ -369,6 +369,7 @@ struct DecodeArgs {
   int max_parts;
   const int32_t* work;  // device work items or null
   int num_items;
+  bool shared_kv;       // ordinary (cache-allocating) loads instead of nontemporal ones
   float* ws_ml;
   float* ws_o;
   hipStream_t stream;
@@ -380,13 +381,15 @@ static void launch_decode(const DecodeArgs& a) {
   const int64_t items =
       a.work ? a.num_items : static_cast<int64_t>(a.num_seqs) * a.max_parts;
   const int64_t wgs = items * a.num_heads;
+  auto kernel = a.shared_kv ? decode_partition_kernel<Ty, D, BS, false>
+                            : decode_partition_kernel<Ty, D, BS, true>;
   if (wgs > 0)
-    hipLaunchKernelGGL((decode_partition_kernel<Ty, D, BS>), dim3(static_cast<unsigned>(wgs)),
-                       dim3(kDecodeThreads), 0, a.stream, static_cast<T*>(a.out),
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
-                       static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks,
-                       a.context_lens, a.num_heads, a.num_blocks, a.max_len, a.scale_log2,
-                       a.part_tokens, a.max_parts, a.work, a.ws_ml, a.ws_o);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
+                       a.stream, static_cast<T*>(a.out), static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
+                       a.block_tables, a.max_blocks, a.context_lens, a.num_heads, a.num_blocks,
+                       a.max_len, a.scale_log2, a.part_tokens, a.max_parts, a.work, a.ws_ml,
+                       a.ws_o);
   if (a.part_tokens > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
     hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)), dim3(D),
@@ -419,11 +422,12 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, int32_t num_seqs,
                                 int32_t max_context_len, float scale, const int32_t* work,
-                                int32_t num_items, void* workspace, size_t workspace_bytes,
-                                pkv_stream_t stream) {
+                                int32_t num_items, uint32_t flags, void* workspace,
+                                size_t workspace_bytes, pkv_stream_t stream) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
-  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale))
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale) ||
+      (flags & ~static_cast<uint32_t>(PKV_DECODE_SHARED_KV)))
     return PKV_EINVAL;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_EINVAL;
@@ -465,6 +469,7 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
   a.max_parts = max_parts;
   a.work = work;
   a.num_items = num_items;
+  a.shared_kv = (flags & PKV_DECODE_SHARED_KV) != 0;
   a.stream = static_cast<hipStream_t>(stream);
 
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
@@ -505,16 +510,33 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs
   return static_cast<size_t>(ml + slots * desc->head_dim * 4);
 }
 
-int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t* items, int32_t capacity) {
+int32_t pkv_decode_schedule_grouped(const pkv_cache_desc_t* desc, const int32_t* lens,
+                                    const int32_t* group_keys, int32_t num_seqs,
+                                    int32_t max_context_len, int32_t* items, int32_t capacity) {
   if (!desc || num_seqs < 0 || max_context_len < 0 || capacity < 0 ||
       (num_seqs > 0 && (!lens || !items)) || num_seqs > kItemSeqMask + 1)
     return -1;
   const int part = partition_tokens(desc, num_seqs, max_context_len);
   struct Item {
-    int32_t tokens;
-    int32_t code;
+    int32_t tokens;  // tokens this item attends
+    int32_t rank;    // group's largest item (keys given) or the item's own tokens
+    int32_t key;     // first sequence of its group
+    int32_t p;       // partition
+    int32_t code;    // s | p << kItemPartShift
   };
+  // group leader = first sequence with the same key (sequences sharing prefix blocks)
+  std::vector<int32_t> leader(static_cast<size_t>(num_seqs));
+  if (group_keys) {
+    std::vector<std::pair<int32_t, int32_t>> kv;
+    kv.reserve(static_cast<size_t>(num_seqs));
+    for (int32_t s = 0; s < num_seqs; ++s) kv.push_back({group_keys[s], s});
+    std::sort(kv.begin(), kv.end());
+    for (size_t i = 0; i < kv.size(); ++i)
+      leader[kv[i].second] = (i > 0 && kv[i].first == kv[i - 1].first)
+                                 ? leader[kv[i - 1].second] : kv[i].second;
+  } else {
+    for (int32_t s = 0; s < num_seqs; ++s) leader[s] = s;
+  }
   std::vector<Item> list;
   list.reserve(static_cast<size_t>(num_seqs));
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -522,19 +544,36 @@ int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, i
     const int plen = partition_len(L, part);
     const int n = (L + plen - 1) / plen;
     if (n == 0) {
-      list.push_back({0, s});  // length 0: one workgroup writes the zero vector
+      list.push_back({0, 0, leader[s], 0, s});  // length 0: one workgroup writes zeros
       continue;
     }
     if (n - 1 > (INT32_MAX >> kItemPartShift)) return -1;
     for (int p = 0; p < n; ++p)
-      list.push_back({std::min(plen, L - p * plen), s | (p << kItemPartShift)});
+      list.push_back({std::min(plen, L - p * plen), 0, leader[s], p, s | (p << kItemPartShift)});
   }
   if (static_cast<int64_t>(list.size()) > capacity) return -1;
-  // longest work first; ties keep (sequence, partition) order
-  std::stable_sort(list.begin(), list.end(),
-                   [](const Item& x, const Item& y) { return x.tokens > y.tokens; });
+  if (group_keys) {
+    std::vector<int32_t> best(static_cast<size_t>(num_seqs), 0);
+    for (const Item& it : list) best[it.key] = std::max(best[it.key], it.tokens);
+    for (Item& it : list) it.rank = best[it.key];
+  } else {
+    for (Item& it : list) it.rank = it.tokens;
+  }
+  // longest groups (or items) first; inside a group, partition by partition so the members
+  // read their shared blocks together
+  std::stable_sort(list.begin(), list.end(), [](const Item& x, const Item& y) {
+    if (x.rank != y.rank) return x.rank > y.rank;
+    if (x.key != y.key) return x.key < y.key;
+    return x.p < y.p;
+  });
   for (size_t i = 0; i < list.size(); ++i) items[i] = list[i].code;
   return static_cast<int32_t>(list.size());
+}
+
+int32_t pkv_decode_schedule(const pkv_cache_desc_t* desc, const int32_t* lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t* items, int32_t capacity) {
+  return pkv_decode_schedule_grouped(desc, lens, nullptr, num_seqs, max_context_len, items,
+                                     capacity);
 }
 
 pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out, const void* q,
@@ -544,7 +583,7 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
                                         int32_t max_context_len, float scale, void* workspace,
                                         size_t workspace_bytes, pkv_stream_t stream) {
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-                     num_seqs, max_context_len, scale, nullptr, 0, workspace, workspace_bytes,
+                     num_seqs, max_context_len, scale, nullptr, 0, 0u, workspace, workspace_bytes,
                      stream);
 }
 
@@ -552,12 +591,11 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len, float scale,
-    const int32_t* work_items, int32_t num_items, void* workspace, size_t workspace_bytes,
-    pkv_stream_t stream) {
-  if (!work_items && num_items != 0) return PKV_EINVAL;
+    const int32_t* work_items, int32_t num_items, uint32_t flags, void* workspace,
+    size_t workspace_bytes, pkv_stream_t stream) {
   if (!work_items) return PKV_EINVAL;
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
-                     num_seqs, max_context_len, scale, work_items, num_items, workspace,
+                     num_seqs, max_context_len, scale, work_items, num_items, flags, workspace,
                      workspace_bytes, stream);
 }
 

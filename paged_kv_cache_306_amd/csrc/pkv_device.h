@@ -126,19 +126,16 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-#ifndef PKV_NT_LOADS
-#define PKV_NT_LOADS 1
-#endif
-
-// K/V tile loads: every byte is read once per decode step.
+// K/V tile loads.  NT: nontemporal (streaming) loads, for K/V that each sequence reads alone
+// once per step; otherwise ordinary loads, so sequences that share blocks hit in L2.
+template <bool NT>
 __device__ __forceinline__ u32x4 load16(gptr_t p) {
   const __attribute__((address_space(1))) u32x4* v =
       reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
-#if PKV_NT_LOADS
-  return __builtin_nontemporal_load(v);
-#else
-  return *v;
-#endif
+  if constexpr (NT)
+    return __builtin_nontemporal_load(v);
+  else
+    return *v;
 }
 
 // A wave-uniform pointer passed through readfirstlane: the optimizer can no longer fold

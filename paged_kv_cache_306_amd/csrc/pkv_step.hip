@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 
 // Two stages are used alternately.  Stage k owns a pinned host area and a device area of
 // d_index.  The upload of step i runs on the stepper's own copy stream after the kernels of
@@ -22,6 +23,7 @@ struct pkv_stepper {
   int32_t max_blocks = 0;
   int32_t max_items = 0;  // decode work items per step, at most
   hipStream_t copy_stream = nullptr;
+  std::vector<int32_t> keys, sorted_keys;  // per-step scratch for the sharing test
   struct Stage {
     int32_t* host = nullptr;      // pinned: tables | lens | slots | pairs (packed for n)
     char* dev = nullptr;          // device area of the same size inside d_index
@@ -145,9 +147,21 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   s = pkv_alloc_export(st->alloc, seqs, n, MB, tables, lens);
   if (s != PKV_OK) return s;
   *max_len = *std::max_element(lens, lens + n);
+  // Sequences whose first physical block is the same share a prefix: schedule them side by
+  // side and read K/V with cache-allocating loads; otherwise longest first, nontemporal.
+  st->keys.resize(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) st->keys[i] = lens[i] > 0 ? tables[static_cast<size_t>(i) * MB] : -1 - i;
+  st->sorted_keys.assign(st->keys.begin(), st->keys.end());
+  std::sort(st->sorted_keys.begin(), st->sorted_keys.end());
+  const bool shared =
+      std::adjacent_find(st->sorted_keys.begin(), st->sorted_keys.end()) != st->sorted_keys.end();
   int32_t* items = pairs + 2 * static_cast<size_t>(*num_cow);
-  const int32_t num_items = pkv_decode_schedule(&st->desc, lens, n, *max_len, items, st->max_items);
+  const int32_t num_items =
+      shared ? pkv_decode_schedule_grouped(&st->desc, lens, st->keys.data(), n, *max_len, items,
+                                           st->max_items)
+             : pkv_decode_schedule(&st->desc, lens, n, *max_len, items, st->max_items);
   if (num_items < 0) return PKV_EINVAL;
+  const uint32_t decode_flags = shared ? PKV_DECODE_SHARED_KV : 0u;
 
   const size_t used = (static_cast<size_t>(n) * MB + 2 * static_cast<size_t>(n) +
                        2 * static_cast<size_t>(*num_cow) + num_items) * sizeof(int32_t);
@@ -184,7 +198,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
         return PKV_EHIP;
       r = pkv_paged_attention_decode_scheduled(
           &st->desc, io->out[l], io->q[l], io->k_pools[l], io->v_pools[l], d_tables, MB, d_lens,
-          n, *max_len, io->scale, d_items, num_items, workspace, workspace_bytes, stream);
+          n, *max_len, io->scale, d_items, num_items, decode_flags, workspace, workspace_bytes,
+          stream);
       if (r != PKV_OK) return r;
       if (attn_events &&
           hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)

@@ -33,8 +33,22 @@ int main(int argc, char** argv) {
   int64_t next = 0;
   std::vector<int32_t> table(4096);
   for (int step = 0; step < steps; ++step) {
-    const int op = static_cast<int>(rng() % 10);
-    if (op < 2 || live.empty()) {
+    const int op = static_cast<int>(rng() % 12);
+    if (op >= 10) {  // prompt from a small vocabulary so prefixes repeat and hit the cache
+      std::vector<int32_t> toks(static_cast<size_t>(1 + rng() % (3 * BS)));
+      for (auto& t : toks) t = static_cast<int32_t>(rng() % 3);
+      int32_t cached = -1;
+      pkv_status_t st =
+          pkv_alloc_add_seq_cached(a, next, toks.data(), static_cast<int32_t>(toks.size()), &cached);
+      if (st == PKV_OK) {
+        live.push_back(next);
+        if (cached < 0 || cached % BS || cached > static_cast<int32_t>(toks.size()))
+          return fail("cached tokens", step);
+      } else if (st != PKV_ENOMEM) {
+        return fail("add_seq_cached status", step);
+      }
+      ++next;
+    } else if (op < 2 || live.empty()) {
       int32_t len = static_cast<int32_t>(rng() % (4 * BS));
       pkv_status_t st = pkv_alloc_add_seq(a, next, len);
       if (st == PKV_OK) live.push_back(next);
@@ -86,6 +100,7 @@ int main(int argc, char** argv) {
     }
     if (sum != entries) return fail("ref sum", step);
     if (used + pkv_alloc_num_free(a) != NB) return fail("free + used", step);
+    if (pkv_alloc_num_cached(a) < 0 || pkv_alloc_num_cached(a) > NB) return fail("cached", step);
     if (pkv_alloc_wasted_slots(a) < 0) return fail("waste", step);
   }
   // error paths

@@ -76,9 +76,10 @@ def test_decode_argument_errors():
     # the scheduled entry point needs a work list, and no more items than partitions
     lib = pkv.lib()
     args = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 64, 0.1)
-    assert lib.pkv_paged_attention_decode_scheduled(*args, None, 0, None, 0, None) == pkv.PKV_EINVAL
-    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, 3, None, 0, None) == pkv.PKV_EINVAL
-    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, -1, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, None, 0, 0, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, 3, 0, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, -1, 0, None, 0, None) == pkv.PKV_EINVAL
+    assert lib.pkv_paged_attention_decode_scheduled(*args, FAKE, 1, 6, None, 0, None) == pkv.PKV_EINVAL
 
 
 def test_decode_schedule_covers_every_partition_longest_first():
@@ -103,6 +104,16 @@ def test_decode_schedule_covers_every_partition_longest_first():
     short = np.array([5, 300, 2, 300, 40], np.int32)
     it = pkv.decode_schedule(d, short, 300)
     assert it.tolist() == [1, 3, 4, 0, 2]
+    # grouped: equal keys stay adjacent, groups by their longest member, partition by partition
+    keys = np.array([7, 3, 7, 3, 9], np.int32)
+    it = pkv.decode_schedule(d, short, 300, group_keys=keys)
+    assert it.tolist() == [1, 3, 4, 0, 2]   # groups by longest member: 300, 40, 5
+    lens2 = np.array([single + 10, 40, single + 300], np.int32)
+    it2 = pkv.decode_schedule(d, lens2, int(lens2.max()), group_keys=np.array([5, 5, 5]))
+    s2, p2 = (it2 & ((1 << 20) - 1)).tolist(), (it2 >> 20).tolist()
+    assert list(zip(s2, p2))[:3] == [(0, 0), (1, 0), (2, 0)] and sorted(zip(s2, p2)) == sorted(
+        [(0, p) for p in range(-(-(single + 10) // part))] + [(1, 0)] +
+        [(2, p) for p in range(-(-(single + 300) // part))])
     # too small a buffer and bad sizes are errors
     buf = np.empty(2, np.int32)
     assert pkv.lib().pkv_decode_schedule(ctypes.byref(d), short.ctypes.data_as(ctypes.c_void_p),

@@ -135,3 +135,54 @@ def test_errors():
             a.append_slot(1)
     assert e.value.status == pkv.PKV_ENOMEM and a.seq_len(1) == 8
     assert a.refcount(-1) == -1 and a.seq_len(42) == -1
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_matches_the_model(seed):
+    g = W.rng(300 + seed)
+    NB, BS = 64, 4
+    order = g.permutation(NB)
+    a = pkv.BlockAllocator(NB, BS, free_order=order)
+    m = oracle.BlockManager(NB, BS, free_order=order)
+    prompts = [g.integers(0, 5, size=int(g.integers(4, 20))).tolist() for _ in range(4)]
+    live, next_id = [], 0
+    for step in range(300):
+        op = g.random()
+        if op < 0.35 or not live:
+            toks = list(prompts[int(g.integers(len(prompts)))])
+            toks = toks[:int(g.integers(1, len(toks) + 1))] + g.integers(0, 5, size=int(
+                g.integers(0, 9))).tolist()
+            try:
+                want = m.add_seq_cached(next_id, toks)
+                ok = True
+            except oracle.OutOfBlocks:
+                ok = False
+            if ok:
+                assert a.add_seq_cached(next_id, toks) == want
+                live.append(next_id)
+            else:
+                with pytest.raises(pkv.PkvError):
+                    a.add_seq_cached(next_id, toks)
+            next_id += 1
+        elif op < 0.5:
+            p = int(g.choice(live))
+            m.fork(p, next_id)
+            a.fork(p, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op < 0.7:
+            s = int(live.pop(int(g.integers(len(live)))))
+            m.free_seq(s)
+            a.free_seq(s)
+        else:
+            batch = [int(x) for x in g.choice(live, size=min(len(live), 3), replace=False)]
+            mslots, mpairs, mdone = m.append_slots(batch)
+            if mdone == len(batch):
+                slots, pairs = a.append_slots(batch)
+                assert slots.tolist() == mslots
+                assert [tuple(p) for p in pairs.tolist()] == mpairs
+            else:
+                with pytest.raises(pkv.PkvError):
+                    a.append_slots(batch)
+        _same_state(a, m, live)
+        assert a.num_cached() == m.num_cached()

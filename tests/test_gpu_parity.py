@@ -80,8 +80,9 @@ def test_ragged_multi_partition(dtype, D, BS):
 
 @pytest.mark.parametrize("dtype,D,BS", [("f16", 128, 16), ("bf16", 64, 8), ("f32", 128, 32)])
 def test_scheduled_decode_bit_identical(dtype, D, BS):
-    """The host-built work list (longest first, or shuffled) gives the same bits as the
-    enumerated grid, in single-pass and split sequences alike."""
+    """The host-built work list (longest first, grouped, or shuffled; nontemporal or
+    cache-allocating loads) gives the same bits as the enumerated grid, in single-pass and
+    split sequences alike."""
     import torch
     dev = device()
     lens = [3, 4096, 4097, 700, 0, 12000, 2048, 33]
@@ -92,12 +93,14 @@ def test_scheduled_decode_bit_identical(dtype, D, BS):
     desc = pkv.CacheDesc(kp.shape[0], H, BS, D, {"f32": 0, "f16": 1, "bf16": 2}[dtype])
     items = pkv.decode_schedule(desc, lens, int(lens.max()))
     shuffled = W.rng(5).permutation(items).astype(np.int32)
-    for order in (items, shuffled):
+    grouped = pkv.decode_schedule(desc, lens, int(lens.max()),
+                                  group_keys=np.array([0, 1, 0, 1, 2, 0, 1, 2], np.int32))
+    for order, shared in ((items, False), (shuffled, False), (grouped, True), (shuffled, True)):
         qt, kt, vt = to_dev(q, dtype, dev), to_dev(kp, dtype, dev), to_dev(vp, dtype, dev)
         out = torch.empty_like(qt)
         pkv.paged_attention_decode(out, qt, kt, vt, torch.from_numpy(tables).to(dev),
                                    torch.from_numpy(lens).to(dev), scale, int(lens.max()),
-                                   work_items=torch.from_numpy(order).to(dev))
+                                   work_items=torch.from_numpy(order).to(dev), shared_kv=shared)
         torch.cuda.synchronize()
         got = W.from_torch(out, dtype)
         assert np.array_equal(got.view(np.uint8), plain.view(np.uint8))
@@ -255,3 +258,51 @@ def test_long_context_full_size(BS):
     w = W.long_context(block_size=BS)
     units = [(s, h) for s in range(w.S) for h in (0, 17, 39)]
     _run_full(w, dev, 700 + BS, units)
+
+
+def test_pool_above_4_gib_uses_64_bit_offsets():
+    """Pools of 4.6 GB each: blocks near the top of the pool sit past 2^32 bytes, so any
+    32-bit offset would read, write or copy the wrong block."""
+    import torch
+    dev = device()
+    H, D, BS, dt = 40, 128, 16, "f16"
+    NB = 28000                                   # 28000 * 163840 B = 4.59 GB per pool
+    hi = np.arange(NB - 400, NB, dtype=np.int32)   # byte offsets >= 4.52e9 > 2^32
+    g = W.rng(4242)
+    lens = np.array([1000, 33, 4000, 200], np.int32)
+    tables = np.full((4, 250), -1, np.int32)
+    pick = g.permutation(hi)
+    k = 0
+    for s, L in enumerate(lens):
+        n = W.nblocks_for(L, BS)
+        tables[s, :n] = pick[k:k + n]
+        k += n
+    kp = W.device_normal((NB, H, BS, D), dt, 1, dev)
+    vp = W.device_normal((NB, H, BS, D), dt, 2, dev)
+    q_np = W.normal_values(g, (4, H, D), dt)
+    units = [(s, h) for s in range(4) for h in (0, 19, 39)]
+    ref = sampled_oracle(q_np, kp, vp, tables, lens, units, dt, 0.088)
+    q = to_dev(q_np, dt, dev)
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode(out, q, kp, vp, torch.from_numpy(tables).to(dev),
+                               torch.from_numpy(lens).to(dev), 0.088, int(lens.max()))
+    torch.cuda.synchronize()
+    got = W.from_torch(out, dt)
+    check_close(np.stack([oracle.decode(got[s, h], dt) for s, h in units]),
+                np.stack([ref[u] for u in units]), dt, "pool > 4 GiB")
+    # append into the last block of the pool and copy it down to block 3
+    kn = W.normal_values(g, (2, H, D), dt)
+    vn = W.normal_values(g, (2, H, D), dt)
+    slots = np.array([(NB - 1) * BS + 5, 7 * BS + 1], np.int32)
+    pkv.reshape_and_cache(to_dev(kn, dt, dev), to_dev(vn, dt, dev), kp, vp,
+                          torch.from_numpy(slots).to(dev))
+    pkv.copy_blocks([kp], [vp], torch.from_numpy(np.array([[NB - 1, 3]], np.int32)).to(dev))
+    torch.cuda.synchronize()
+    top_k = W.from_torch(kp[NB - 1], dt)
+    assert np.array_equal(top_k[:, 5].view(np.uint16), kn[0].view(np.uint16))
+    assert np.array_equal(W.from_torch(kp[3], dt).view(np.uint16), top_k.view(np.uint16))
+    assert np.array_equal(W.from_torch(vp[3], dt).view(np.uint16),
+                          W.from_torch(vp[NB - 1], dt).view(np.uint16))
+    assert np.array_equal(W.from_torch(vp[7], dt)[:, 1].view(np.uint16), vn[1].view(np.uint16))
+    del kp, vp
+    torch.cuda.empty_cache()

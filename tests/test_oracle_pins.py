@@ -473,3 +473,44 @@ def test_block_manager_free_and_out_of_blocks():
     assert bm.block_table(5) == [0, 1, 2, 3]
     with pytest.raises(ValueError):
         bm.free_seq(99)
+
+
+# ============================================================================ prefix cache
+def test_prefix_cache_model_follows_the_pages_pattern():
+    """"Prefix Caching": the first request with a system prompt computes and caches its KV
+    blocks; later requests with the same prompt reuse them and skip recomputing; another
+    prompt shares nothing; only full blocks are cached."""
+    BS = 4
+    bm = oracle.BlockManager(40, BS)
+    system = list(range(100, 112))                     # 3 full blocks
+    assert bm.add_seq_cached(1, system + [7, 8]) == 0  # first request: nothing cached yet
+    assert bm.num_cached() == 3                        # the partial 4th block is not cached
+    assert bm.add_seq_cached(2, system + [9]) == 12    # second request reuses 3 blocks
+    assert bm.block_table(2)[:3] == bm.block_table(1)[:3]
+    assert bm.block_table(2)[3] != bm.block_table(1)[3]
+    assert [bm.ref[b] for b in bm.block_table(1)[:3]] == [2, 2, 2]
+    # same tokens after a different first block are a different prefix
+    other = [555, 556, 557, 558] + system[4:]
+    assert bm.add_seq_cached(3, other) == 0
+    # a prompt diverging inside block 2 reuses blocks 0 and 1 only
+    assert bm.add_seq_cached(4, system[:8] + [0, 0, 0, 0]) == 8
+    _invariants(bm)
+
+
+def test_prefix_cache_parks_then_evicts_oldest():
+    BS = 2
+    bm = oracle.BlockManager(6, BS)
+    bm.add_seq_cached(1, [1, 2, 3, 4])        # blocks cached: (1,2), (3,4)
+    bm.add_seq_cached(2, [5, 6])              # (5,6)
+    bm.free_seq(1)                            # parks (3,4) then (1,2) (reverse logical order)
+    bm.free_seq(2)                            # parks (5,6)
+    assert bm.num_free() == 6 and bm.num_cached() == 3
+    assert bm.add_seq_cached(3, [1, 2, 3, 4]) == 4   # hit on parked blocks revives them
+    assert bm.num_cached() == 3 and list(bm.parked) == [bm.cache[(0, (5, 6))]]
+    bm.add_seq(4, 6)   # 3 plain free blocks are used first: nothing evicted
+    assert bm.num_cached() == 3
+    bm.add_seq(5, 1)   # now the parked (5,6) block is evicted
+    assert bm.num_cached() == 2 and (0, (5, 6)) not in bm.cache
+    with pytest.raises(oracle.OutOfBlocks):
+        bm.add_seq(6, 1)
+    _invariants(bm)

@@ -190,6 +190,29 @@ pkv_status_t pkv_copy_blocks(const pkv_cache_desc_t* desc, void* const* k_pools,
                              int32_t num_pairs, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Copy blocks between two pools of the same shape -- out of HBM into a pinned host swap pool
+ * and back -- for preemption by swapping ("PagedAttention: Efficient LLM Serving with vLLM",
+ * "vLLM: The Serving Engine": swap the KV cache to CPU memory when the GPU is full and resume
+ * later; the aipaper.jasonlin.tech page, "Key contributions": with small blocks, swapping
+ * means many small transfers).
+ *
+ * For every layer l and pair p with (src, dst) = (pairs[2p], pairs[2p+1]):
+ *     dst_k[l][dst] = src_k[l][src] and dst_v[l][dst] = src_v[l][src]     (bit-exact)
+ * All pairs of all layers are copied by one kernel launch (per 64 layers), not one transfer per
+ * block.  Each pool pointer, and pairs, may be device memory or pinned host memory
+ * (hipHostMalloc; e.g. a torch pin_memory tensor), which the kernel reaches over PCIe; pageable
+ * host memory is refused (PKV_EINVAL).  The descriptors must agree in everything but
+ * num_blocks.  A pair with src outside [0, src num_blocks) or dst outside [0, dst num_blocks)
+ * is skipped.  Destinations must be distinct.
+ *   src_k/src_v/dst_k/dst_v  host arrays of num_layers pool pointers
+ *   pairs                    int32 [num_pairs][2], device or pinned host memory
+ */
+pkv_status_t pkv_swap_blocks(const pkv_cache_desc_t* src_desc, const pkv_cache_desc_t* dst_desc,
+                             const void* const* src_k, const void* const* src_v,
+                             void* const* dst_k, void* const* dst_v, int32_t num_layers,
+                             const int32_t* pairs, int32_t num_pairs, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Host block manager: on-demand allocation, reference counts, copy-on-write decisions.
  * Plain C++, no device calls; one instance is used by one thread.
  * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
@@ -252,6 +275,19 @@ int32_t pkv_alloc_num_free(const pkv_alloc_t* a);
 pkv_status_t pkv_alloc_add_seq_cached(pkv_alloc_t* a, int64_t seq, const int32_t* tokens,
                                       int32_t len, int32_t* cached_tokens);
 int32_t pkv_alloc_num_cached(const pkv_alloc_t* a); /* blocks in the prefix cache */
+/* Preemption by swapping ("PagedAttention: Efficient LLM Serving with vLLM", "vLLM: The
+ * Serving Engine": swap the KV cache to CPU memory when the GPU is full, resume later).
+ * Moves sequences seqs[0..n-1] from block manager `from` to block manager `to` (same
+ * block_size; e.g. the HBM pool's and a pinned host pool's): each distinct block they use gets
+ * one block of `to` in first-use order (a block shared among them stays shared), tables and
+ * lengths move over, `from` drops their references, and the (block in from, block in to)
+ * pairs go to pairs (host out, room for 2 * capacity int32) for pkv_swap_blocks.
+ * PKV_EINVAL if a sequence is unknown in `from`, already in `to`, listed twice, or shares a
+ * block with a sequence not in the list (move the whole group), or capacity is too small;
+ * PKV_ENOMEM if `to` has too few free blocks.  On error nothing changes. */
+pkv_status_t pkv_alloc_move_seqs(pkv_alloc_t* from, pkv_alloc_t* to, const int64_t* seqs,
+                                 int32_t n, int32_t* pairs, int32_t capacity,
+                                 int32_t* num_pairs);
 int32_t pkv_alloc_refcount(const pkv_alloc_t* a, int32_t block); /* -1 if out of range */
 /* Unused slots of blocks in use: per block, block_size minus the most tokens any sequence
  * keeps in it ("Memory Efficiency": 100 tokens in 16-token blocks waste 12 slots). */

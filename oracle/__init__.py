@@ -8,7 +8,8 @@ shares no code with it: every step of the product path runs in the HIP library.
 Modules:
   storage        exact decoding of f32 / f16 / bf16 storage bits to float64
   attention      gather through the block table, then textbook softmax(q K^T * scale) V
-  cache_ops      reshape_and_cache (append a token's K/V into its slot) and copy_blocks
+  cache_ops      reshape_and_cache (append a token's K/V into its slot), copy_blocks and
+                 swap_blocks (block copies within a pool or between HBM and host pools)
   block_manager  block allocation with reference counts and copy-on-write
 
 Every function is pinned by ``tests/test_oracle_pins.py`` (closed forms, a library
@@ -16,12 +17,12 @@ reduction, invariances, the pages' worked examples); none is "parity unpinned".
 """
 from .storage import decode, decode_bits_f16, decode_bits_bf16
 from .attention import gather_sequence, attend, paged_attention_decode, decode_unit
-from .cache_ops import reshape_and_cache, copy_blocks
+from .cache_ops import reshape_and_cache, copy_blocks, swap_blocks
 from .block_manager import BlockManager, OutOfBlocks
 
 __all__ = [
     "decode", "decode_bits_f16", "decode_bits_bf16",
     "gather_sequence", "attend", "paged_attention_decode", "decode_unit",
-    "reshape_and_cache", "copy_blocks",
+    "reshape_and_cache", "copy_blocks", "swap_blocks",
     "BlockManager", "OutOfBlocks",
 ]

@@ -194,6 +194,42 @@ class BlockManager:
             self._drop(b)
         del self.lens[seq]
 
+    def move_seqs(self, to: "BlockManager", seqs):
+        """Swap out / in: move the sequences to another manager; each distinct block they use
+        gets one block there in first-use order.  Returns the (here, there) pairs.  Refused
+        (ValueError) if a block is also used by a sequence not in the list."""
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs) or any(s not in self.tables or s in to.tables
+                                               for s in seqs):
+            raise ValueError("bad sequence")
+        if to.block_size != self.block_size:
+            raise ValueError("block sizes differ")
+        order, uses = [], {}
+        for s in seqs:
+            for b in self.tables[s]:
+                if b not in uses:
+                    order.append(b)
+                    uses[b] = 0
+                uses[b] += 1
+        if any(uses[b] != self.ref[b] for b in order):
+            raise ValueError("a block is shared with a sequence that is not moved")
+        if len(order) > to.num_free():
+            raise OutOfBlocks()
+        mapping = {}
+        for b in order:
+            d = to._take()
+            to.ref[d] = 0
+            mapping[b] = d
+        for s in seqs:
+            table = self.tables.pop(s)
+            to.tables[s] = [mapping[b] for b in table]
+            to.lens[s] = self.lens.pop(s)
+            for b in table:
+                to.ref[mapping[b]] += 1
+            for b in reversed(table):
+                self._drop(b)
+        return [(b, mapping[b]) for b in order]
+
     # -- queries -----------------------------------------------------------------------
     def num_free(self) -> int:
         """Blocks that can be handed out: plain free ones and parked cached ones."""

@@ -60,3 +60,19 @@ def copy_blocks(pools, pairs):
             cb[dst] = pb[src]
         out.append(c)
     return out
+
+
+def swap_blocks(src_pools, dst_pools, pairs):
+    """Return copies of the destination pools with dst[d] = src[s] for each (s, d) pair, in
+    every layer: the byte copy that moves blocks between HBM and host swap memory."""
+    pairs = np.asarray(pairs, np.int64).reshape(-1, 2)
+    dsts = pairs[:, 1].tolist()
+    assert len(set(dsts)) == len(dsts), "duplicate destination"
+    out = []
+    for sp, dp in zip(src_pools, dst_pools):
+        c = dp.copy()
+        cb, sb = _bits(c), _bits(np.ascontiguousarray(sp))
+        for s, d in pairs.tolist():
+            cb[d] = sb[s]
+        out.append(c)
+    return out

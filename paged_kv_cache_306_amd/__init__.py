@@ -14,7 +14,7 @@ __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
     "decode_schedule",
     "paged_attention_decode", "reshape_and_cache", "copy_blocks", "BlockAllocator",
-    "DecodeStepper", "LIB_PATH",
+    "DecodeStepper", "swap_blocks", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -76,6 +76,8 @@ _SIGNATURES = {
     "pkv_alloc_wasted_slots": (_i64, [_p]),
     "pkv_alloc_add_seq_cached": (_i32, [_p, _i64, _p, _i32, _pi32]),
     "pkv_alloc_num_cached": (_i32, [_p]),
+    "pkv_alloc_move_seqs": (_i32, [_p, _p, _p, _i32, _p, _i32, _pi32]),
+    "pkv_swap_blocks": (_i32, [_pdesc, _pdesc, _p, _p, _p, _p, _i32, _p, _i32, _p]),
     "pkv_stepper_index_bytes": (_sz, [_pdesc, _i32, _i32]),
     "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
     "pkv_stepper_destroy": (None, [_p]),
@@ -256,6 +258,39 @@ def copy_blocks(k_pools, v_pools, pairs, stream=None):
     _check(st, "pkv_copy_blocks")
 
 
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None):
+    """dst[l][d] = src[l][s] for every (s, d) row of ``pairs`` and every layer l, K and V.
+    Pools (lists, one per layer) may be device tensors or pinned host tensors; ``pairs`` an
+    int32 [n][2] device or pinned host tensor."""
+    import torch
+    L = len(src_k)
+    if not (len(src_v) == len(dst_k) == len(dst_v) == L) or L == 0:
+        raise ValueError("one pool per layer in every list")
+    for p in list(src_k) + list(src_v) + list(dst_k) + list(dst_v):
+        if not p.is_contiguous():
+            raise ValueError("pools must be contiguous")
+        if p.shape[1:] != src_k[0].shape[1:] or p.dtype != src_k[0].dtype:
+            raise ValueError("pools must share everything but the block count")
+        if not (p.is_cuda or p.is_pinned()):
+            raise ValueError("pools must be device or pinned host tensors")
+    for p in list(src_v):
+        if p.shape != src_k[0].shape:
+            raise ValueError("source pools must share one shape")
+    for p in list(dst_v):
+        if p.shape != dst_k[0].shape:
+            raise ValueError("destination pools must share one shape")
+    if pairs.dtype != torch.int32 or (pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2)):
+        raise ValueError("pairs must be int32 [n][2]")
+    n = pairs.shape[0] if pairs.numel() else 0
+    sd, dd = desc_for_pool(src_k[0]), desc_for_pool(dst_k[0])
+    arr = lambda lst: (ctypes.c_void_p * L)(*[t.data_ptr() for t in lst])
+    st = _lib().pkv_swap_blocks(ctypes.byref(sd), ctypes.byref(dd), arr(src_k), arr(src_v),
+                                arr(dst_k), arr(dst_v), L,
+                                ctypes.c_void_p(pairs.data_ptr() if n else 0), n,
+                                _stream_ptr(stream))
+    _check(st, "pkv_swap_blocks")
+
+
 # ----------------------------------------------------------------------------- allocator
 class BlockAllocator:
     """Host block manager (plain C++ inside libpkv): on-demand blocks, reference counts and
@@ -296,6 +331,20 @@ class BlockAllocator:
 
     def num_cached(self) -> int:
         return int(_lib().pkv_alloc_num_cached(self._h))
+
+    def move_seqs(self, to: "BlockAllocator", seqs):
+        """Move sequences to another block manager (swap out / swap in); returns the
+        (block here, block there) pairs as int32 numpy [n][2] for swap_blocks."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        cap = int(sum(len(self.block_table(int(s))) for s in seqs)) if len(seqs) else 0
+        pairs = np.empty((max(cap, 1), 2), np.int32)
+        npairs = _i32()
+        _check(_lib().pkv_alloc_move_seqs(self._h, to._h, seqs.ctypes.data_as(ctypes.c_void_p),
+                                          int(seqs.shape[0]),
+                                          pairs.ctypes.data_as(ctypes.c_void_p), cap,
+                                          ctypes.byref(npairs)), "pkv_alloc_move_seqs")
+        return pairs[:npairs.value].copy()
 
     def fork(self, parent: int, child: int):
         _check(_lib().pkv_alloc_fork(self._h, parent, child), "pkv_alloc_fork")

@@ -236,6 +236,56 @@ int32_t pkv_alloc_seq_len(const pkv_alloc_t* a, int64_t seq) {
 
 int32_t pkv_alloc_num_free(const pkv_alloc_t* a) { return a ? a->available() : -1; }
 
+pkv_status_t pkv_alloc_move_seqs(pkv_alloc_t* from, pkv_alloc_t* to, const int64_t* seqs,
+                                 int32_t n, int32_t* pairs, int32_t capacity,
+                                 int32_t* num_pairs) {
+  if (!from || !to || from == to || n < 0 || (n > 0 && !seqs) || !num_pairs || capacity < 0 ||
+      from->block_size != to->block_size)
+    return PKV_EINVAL;
+  *num_pairs = 0;
+  // every listed sequence exists in `from`, none in `to`, no duplicates
+  std::unordered_map<int64_t, int> listed;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!from->seqs.count(seqs[i]) || to->seqs.count(seqs[i]) || listed.count(seqs[i]))
+      return PKV_EINVAL;
+    listed[seqs[i]] = i;
+  }
+  // distinct blocks in first-use order, and their references from the listed sequences
+  std::vector<int32_t> order;
+  std::unordered_map<int32_t, int32_t> refs_listed;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t b : from->seqs[seqs[i]].table)
+      if (refs_listed[b]++ == 0) order.push_back(b);
+  for (const auto& kv : refs_listed)
+    if (kv.second != from->ref[kv.first]) return PKV_EINVAL;  // shared with an unlisted seq
+  const int32_t m = static_cast<int32_t>(order.size());
+  if (m > capacity || (m > 0 && !pairs)) return PKV_EINVAL;
+  if (m > to->available()) return PKV_ENOMEM;
+  std::unordered_map<int32_t, int32_t> map;
+  for (int32_t k = 0; k < m; ++k) {
+    const int32_t d = to->take();
+    to->ref[d] = 0;  // set below from the moved tables
+    map[order[k]] = d;
+    pairs[2 * k] = order[k];
+    pairs[2 * k + 1] = d;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = from->seqs.find(seqs[i]);
+    pkv_alloc::Seq moved;
+    moved.len = it->second.len;
+    for (int32_t b : it->second.table) {
+      moved.table.push_back(map[b]);
+      ++to->ref[map[b]];
+    }
+    const std::vector<int32_t>& t = it->second.table;
+    for (auto b = t.rbegin(); b != t.rend(); ++b) from->drop(*b);
+    from->seqs.erase(it);
+    to->seqs.emplace(seqs[i], std::move(moved));
+  }
+  *num_pairs = m;
+  return PKV_OK;
+}
+
 int32_t pkv_alloc_num_cached(const pkv_alloc_t* a) {
   return a ? static_cast<int32_t>(a->index.size()) : -1;
 }

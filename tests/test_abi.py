@@ -151,6 +151,21 @@ def test_cache_op_argument_errors():
     assert lib.pkv_copy_blocks(ctypes.byref(d), arr, arr, 2, FAKE, 0, None) == pkv.PKV_OK
 
 
+def test_swap_argument_errors():
+    lib = pkv.lib()
+    d, d2 = _desc(), _desc(nb=4)
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    nul = (ctypes.c_void_p * 2)(0x1000, None)
+    sw = lib.pkv_swap_blocks
+    assert sw(ctypes.byref(d), ctypes.byref(_desc(d=64)), arr, arr, arr, arr, 2, FAKE, 1, None) == pkv.PKV_EINVAL
+    assert sw(ctypes.byref(d), ctypes.byref(_desc(bs=8)), arr, arr, arr, arr, 2, FAKE, 1, None) == pkv.PKV_EINVAL
+    assert sw(ctypes.byref(d), ctypes.byref(d2), arr, arr, arr, arr, -1, FAKE, 1, None) == pkv.PKV_EINVAL
+    assert sw(ctypes.byref(d), ctypes.byref(d2), arr, arr, arr, arr, 2, None, 1, None) == pkv.PKV_EINVAL
+    assert sw(ctypes.byref(d), ctypes.byref(d2), arr, arr, arr, arr, 2, FAKE, 0, None) == pkv.PKV_OK
+    assert sw(None, ctypes.byref(d2), arr, arr, arr, arr, 2, FAKE, 1, None) == pkv.PKV_EINVAL
+    assert sw(ctypes.byref(d), ctypes.byref(d2), None, arr, arr, arr, 2, FAKE, 1, None) == pkv.PKV_EINVAL
+
+
 def test_binding_requires_device_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 2, 128, dtype=torch.float16)

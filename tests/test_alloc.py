@@ -186,3 +186,78 @@ def test_prefix_cache_matches_the_model(seed):
                     a.append_slots(batch)
         _same_state(a, m, live)
         assert a.num_cached() == m.num_cached()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_move_seqs_matches_the_model(seed):
+    g = W.rng(500 + seed)
+    BS = 8
+    og, oc = g.permutation(48), g.permutation(40)
+    a_gpu, a_cpu = pkv.BlockAllocator(48, BS, free_order=og), pkv.BlockAllocator(40, BS, free_order=oc)
+    m_gpu, m_cpu = oracle.BlockManager(48, BS, free_order=og), oracle.BlockManager(40, BS, free_order=oc)
+    groups = {}          # root id -> member ids (forks share blocks within a group)
+    where = {}           # root -> "gpu" | "cpu"
+    nxt = 0
+    for step in range(200):
+        op = g.random()
+        on_gpu = [r for r in groups if where[r] == "gpu"]
+        on_cpu = [r for r in groups if where[r] == "cpu"]
+        if op < 0.3:
+            L = int(g.integers(1, 3 * BS))
+            try:
+                m_gpu.add_seq(nxt, L)
+            except oracle.OutOfBlocks:
+                with pytest.raises(pkv.PkvError):
+                    a_gpu.add_seq(nxt, L)
+                nxt += 1
+                continue
+            a_gpu.add_seq(nxt, L)
+            members = [nxt]
+            for _ in range(int(g.integers(0, 3))):
+                nxt += 1
+                m_gpu.fork(members[0], nxt)
+                a_gpu.fork(members[0], nxt)
+                members.append(nxt)
+            groups[members[0]] = members
+            where[members[0]] = "gpu"
+            nxt += 1
+        elif op < 0.5 and on_gpu:
+            r = on_gpu[int(g.integers(len(on_gpu)))]
+            batch = groups[r]
+            ms, mp, md = m_gpu.append_slots(batch)
+            if md == len(batch):
+                s, p = a_gpu.append_slots(batch)
+                assert s.tolist() == ms and [tuple(x) for x in p.tolist()] == mp
+            else:
+                with pytest.raises(pkv.PkvError):
+                    a_gpu.append_slots(batch)
+        elif op < 0.75 and (on_gpu or on_cpu):
+            pool = on_gpu + on_cpu
+            r = pool[int(g.integers(len(pool)))]
+            src_m, dst_m = (m_gpu, m_cpu) if where[r] == "gpu" else (m_cpu, m_gpu)
+            src_a, dst_a = (a_gpu, a_cpu) if where[r] == "gpu" else (a_cpu, a_gpu)
+            try:
+                want = src_m.move_seqs(dst_m, groups[r])
+            except oracle.OutOfBlocks:
+                with pytest.raises(pkv.PkvError):
+                    src_a.move_seqs(dst_a, groups[r])
+                continue
+            got = src_a.move_seqs(dst_a, groups[r])
+            assert [tuple(x) for x in got.tolist()] == want
+            where[r] = "cpu" if where[r] == "gpu" else "gpu"
+            # a partial group is refused while one of its blocks is still shared
+            first = groups[r][0]
+            if len(groups[r]) > 1 and any(dst_m.ref[b] > 1 for b in dst_m.block_table(first)):
+                with pytest.raises(pkv.PkvError):
+                    dst_a.move_seqs(src_a, groups[r][:1])
+        elif groups:
+            r = list(groups)[int(g.integers(len(groups)))]
+            mm, aa = (m_gpu, a_gpu) if where[r] == "gpu" else (m_cpu, a_cpu)
+            for s in groups.pop(r):
+                mm.free_seq(s)
+                aa.free_seq(s)
+            del where[r]
+        live_gpu = [s for r in groups if where[r] == "gpu" for s in groups[r]]
+        live_cpu = [s for r in groups if where[r] == "cpu" for s in groups[r]]
+        _same_state(a_gpu, m_gpu, live_gpu)
+        _same_state(a_cpu, m_cpu, live_cpu)

@@ -514,3 +514,48 @@ def test_prefix_cache_parks_then_evicts_oldest():
     with pytest.raises(oracle.OutOfBlocks):
         bm.add_seq(6, 1)
     _invariants(bm)
+
+
+# ============================================================================ swapping
+def test_swap_model_moves_groups_and_keeps_sharing():
+    """Preemption by swapping ("vLLM: The Serving Engine": swap KV to CPU when the GPU is
+    full, resume later): a group moved out and back keeps its token-to-slot structure, its
+    shared blocks stay shared, and a partial group is refused."""
+    BS = 4
+    gpu = oracle.BlockManager(20, BS, free_order=W.rng(3).permutation(20))
+    cpu = oracle.BlockManager(12, BS)
+    gpu.add_seq(1, 10)
+    gpu.fork(1, 2)
+    gpu.append_slot(2)                         # copy-on-write of the shared partial block
+    gpu.add_seq(3, 5)
+    with pytest.raises(ValueError):
+        gpu.move_seqs(cpu, [1])                # block 0/1 still shared with seq 2
+    before = {s: gpu.block_table(s) for s in (1, 2)}
+    out = gpu.move_seqs(cpu, [1, 2])
+    assert len(out) == 4                       # 2 shared + 2 private last blocks
+    assert [cpu.ref[d] for _, d in out[:2]] == [2, 2]
+    assert gpu.num_free() == 20 - len(gpu.block_table(3)) and 1 not in gpu.tables
+    fwd = dict(out)
+    for s in (1, 2):
+        assert cpu.block_table(s) == [fwd[b] for b in before[s]]
+        assert cpu.seq_len(s) == (10 if s == 1 else 11)
+    back = cpu.move_seqs(gpu, [1, 2])
+    bwd = dict(back)
+    # the composite map old gpu block -> new gpu block is one-to-one on the moved blocks
+    composite = {b: bwd[fwd[b]] for b in fwd}
+    assert len(set(composite.values())) == len(composite)
+    for s in (1, 2):
+        assert gpu.block_table(s) == [composite[b] for b in before[s]]
+    _invariants(gpu)
+    _invariants(cpu)
+    assert cpu.num_free() == 12
+
+
+def test_swap_blocks_copies_across_pools():
+    g = W.rng(33)
+    src = [W.normal_values(g, (6, 2, 4, 8), "bf16") for _ in range(2)]
+    dst = [W.normal_values(g, (3, 2, 4, 8), "bf16") for _ in range(2)]
+    out = oracle.swap_blocks(src, dst, [[5, 0], [1, 2]])
+    for s, d, o in zip(src, dst, out):
+        assert np.array_equal(o[0], s[5]) and np.array_equal(o[2], s[1])
+        assert np.array_equal(o[1], d[1])

@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--workload", choices=WORKLOADS, default="llama13b_layer")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="block size of the llama13b_layer / long_context workloads")
+    ap.add_argument("--swap", action="store_true",
+                    help="swap-out / swap-in bandwidth between HBM and a pinned host pool for "
+                         "block sizes 8, 16, 32: one JSON line per configuration")
     ap.add_argument("--sweep", action="store_true",
                     help="block size x placement sweep of the llama13b_layer and long_context "
                          "workloads: one JSON line per configuration")
@@ -308,6 +311,62 @@ def sweep(args):
                 torch.cuda.empty_cache()
 
 
+def swap_bench(args, layers: int = 8, tokens: int = 16384):
+    """Preemption by swapping: move `tokens` tokens per layer of LLaMA-13B-shaped fp16 K/V
+    (scattered blocks) to a pinned host pool and back with one pkv_swap_blocks call each way;
+    a single contiguous copy of the same byte count gives the PCIe reference."""
+    import torch
+    import paged_kv_cache_306_amd as pkv
+    import workloads as W
+    dev = torch.device("cuda:0")
+    H, D = 40, 128
+    for bs in (8, 16, 32):
+        n = tokens // bs
+        nb_dev, nb_host = n * 2, n
+        g = W.rng(77 + bs)
+        dk = [W.device_normal((nb_dev, H, bs, D), "f16", 10 * l + 1, dev) for l in range(layers)]
+        dv = [W.device_normal((nb_dev, H, bs, D), "f16", 10 * l + 2, dev) for l in range(layers)]
+        hk = [torch.empty((nb_host, H, bs, D), dtype=torch.float16).pin_memory() for _ in range(layers)]
+        hv = [torch.empty((nb_host, H, bs, D), dtype=torch.float16).pin_memory() for _ in range(layers)]
+        src = g.permutation(nb_dev)[:n].astype(np.int32)
+        out_pairs = torch.from_numpy(np.stack([src, g.permutation(n).astype(np.int32)], 1)).to(dev)
+        in_pairs = torch.from_numpy(np.stack([np.arange(n, dtype=np.int32),
+                                              g.permutation(nb_dev)[:n].astype(np.int32)], 1)).to(dev)
+        nbytes = 2 * layers * n * H * bs * D * 2
+        res = {"swap": "HBM <-> pinned host", "block_size": bs, "layers": layers,
+               "blocks_per_layer": n, "bytes_each_way": nbytes}
+        for name, fn in (("out", lambda: pkv.swap_blocks(dk, dv, hk, hv, out_pairs)),
+                         ("in", lambda: pkv.swap_blocks(hk, hv, dk, dv, in_pairs))):
+            fn()
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            times = []
+            for _ in range(5):
+                a.record()
+                fn()
+                z.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(z) / 1e3)
+            t = float(np.median(times))
+            res[f"swap_{name}_ms"] = round(t * 1e3, 3)
+            res[f"swap_{name}_GBs"] = round(nbytes / t / 1e9, 2)
+        # one contiguous copy of the same size each way (the PCIe reference)
+        flat_d = torch.empty(nbytes // 2, dtype=torch.float16, device=dev)
+        flat_h = torch.empty(nbytes // 2, dtype=torch.float16).pin_memory()
+        for name, (dst, srct) in (("d2h", (flat_h, flat_d)), ("h2d", (flat_d, flat_h))):
+            dst.copy_(srct, non_blocking=True)
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(srct, non_blocking=True)
+            z.record()
+            torch.cuda.synchronize()
+            res[f"contiguous_{name}_GBs"] = round(nbytes / (a.elapsed_time(z) / 1e3) / 1e9, 2)
+        print(json.dumps(res), flush=True)
+        del dk, dv, hk, hv, flat_d, flat_h
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -319,6 +378,9 @@ def main():
         return
     if args.sweep:
         sweep(args)
+        return
+    if args.swap:
+        swap_bench(args)
         return
     import torch
     dev = torch.device("cuda:0")

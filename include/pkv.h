@@ -303,26 +303,27 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * pkv_stepper_step(seqs[0..n-1]) does, in order:
  *   1. pkv_alloc_append_slots on the stepper's block manager (one new slot per sequence),
  *      then exports the dense block tables and lengths, into a pinned host staging area
- *      (two areas used alternately, so the host can prepare step i+1 while step i's copy is
- *      in flight);
- *   2. one asynchronous host-to-device copy of the packed index data into an area of d_index:
+ *      (two areas used alternately, so the host can prepare step i+1 while step i runs);
+ *   2. one prologue kernel on `stream` pulls the packed index data from the pinned area (over
+ *      PCIe) into an area of d_index and, when there are no copy-on-write pairs, also
+ *      appends the first layer's new K/V:
  *      int32 tables [n][max_blocks_per_seq] | lens [n] | slots [n] | cow pairs [num_cow][2] |
  *      decode work items [num_items] -- longest work first (pkv_decode_schedule) or, when
  *      sequences share their first block, grouped by it (pkv_decode_schedule_grouped) and
  *      decoded with PKV_DECODE_SHARED_KV;
  *   3. pkv_copy_blocks over every layer when there are copy-on-write pairs;
- *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]), then
+ *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]) (done by the
+ *      prologue for layer 0 when there was no copy), then
  *      pkv_paged_attention_decode_scheduled(q[l] -> out[l]) with the lengths including the
  *      new token.
  * Everything after step 1 is asynchronous on `stream`.  If step 1 fails (PKV_ENOMEM: the pool
  * ran out; PKV_EINVAL: unknown sequence) nothing is launched, and the sequences before the
  * failing one have already been extended by one slot (*num_done reports how many).
  *
- * The stepper allocates only pinned host memory, HIP events and one copy stream (default
- * priority) of its own; the caller owns the device buffer d_index (pkv_stepper_index_bytes
- * bytes, 16-byte aligned: two areas used by alternate steps) and the workspace.  The upload of
- * step i runs on the copy stream after the kernels of step i-2 and before those of step i, so
- * it overlaps step i-1's kernels when the host runs ahead.  pkv_stepper_last_index returns the
+ * The stepper allocates only pinned host memory and HIP events of its own; the caller owns the
+ * device buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned: two areas used by
+ * alternate steps) and the workspace.  The host refills a staging area only after the
+ * prologue that read it (two steps earlier) has run.  pkv_stepper_last_index returns the
  * device address of the packed index data of the last step.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t recorded on `stream` just
  * before and just after each layer's attention launch (for timing).

@@ -1,9 +1,11 @@
 // Decode-step driver: one decode iteration of a batch over every layer in one host call
 // ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
-// steps 1-5).  Host code only: the block manager decides slots and copy-on-write pairs, the
-// packed index data goes to the device in one asynchronous copy, then the cache-write and
-// attention kernels are launched per layer on the caller's stream.
+// steps 1-5).  The block manager decides slots and copy-on-write pairs on the host; the
+// packed index data (tables | lens | slots | pairs | work items) is written into pinned
+// host memory and pulled to the device by the step's first kernel, which also appends the
+// first layer's new K/V -- no copy engine, no second stream, no cross-queue wait.
 #include "pkv.h"
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -12,30 +14,51 @@
 #include <new>
 #include <vector>
 
-// Two stages are used alternately.  Stage k owns a pinned host area and a device area of
-// d_index.  The upload of step i runs on the stepper's own copy stream after the kernels of
-// step i-2 (the last reader of the same device area) and before the kernels of step i, so it
-// overlaps the kernels of step i-1 whenever the host runs ahead of the device.
-struct pkv_stepper {
-  pkv_alloc_t* alloc = nullptr;
-  pkv_cache_desc_t desc{};
-  int32_t max_seqs = 0;
-  int32_t max_blocks = 0;
-  int32_t max_items = 0;  // decode work items per step, at most
-  hipStream_t copy_stream = nullptr;
-  std::vector<int32_t> keys, sorted_keys;  // per-step scratch for the sharing test
-  struct Stage {
-    int32_t* host = nullptr;      // pinned: tables | lens | slots | pairs (packed for n)
-    char* dev = nullptr;          // device area of the same size inside d_index
-    hipEvent_t copied = nullptr;  // recorded on the copy stream after the upload
-    hipEvent_t consumed = nullptr;  // recorded on the caller's stream after the kernels
-    bool copy_pending = false;
-    bool used = false;
-  } stage[2];
-  int cur = 0;
-};
-
 namespace {
+
+constexpr int kPrologueThreads = 256;
+constexpr int kCopyVecsPerThread = 4;
+
+// Workgroups [0, copy_wgs) copy idx_vecs 16-byte vectors of index data from pinned host
+// memory (device-mapped) to the device index area.  The remaining workgroups, when
+// row_vecs > 0, write token i's K/V rows of the first layer at slot slots_host[i] -- the
+// same copy as reshape_and_cache_kernel, reading the slot straight from host memory.
+__global__ __launch_bounds__(kPrologueThreads) void step_prologue_kernel(
+    const pkv::u32x4* __restrict__ idx_src, pkv::u32x4* __restrict__ idx_dst, int idx_vecs,
+    int copy_wgs, const int32_t* __restrict__ slots_host, const pkv::u32x4* __restrict__ k,
+    const pkv::u32x4* __restrict__ v, pkv::u32x4* __restrict__ k_pool,
+    pkv::u32x4* __restrict__ v_pool, int64_t total_vecs, int row_vecs, int num_heads,
+    int block_size, int64_t num_slots) {
+  if (static_cast<int>(blockIdx.x) < copy_wgs) {
+    const int base = blockIdx.x * kPrologueThreads * kCopyVecsPerThread + threadIdx.x;
+    pkv::u32x4 r[kCopyVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kCopyVecsPerThread; ++u) {
+      const int i = base + u * kPrologueThreads;
+      if (i < idx_vecs) r[u] = idx_src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyVecsPerThread; ++u) {
+      const int i = base + u * kPrologueThreads;
+      if (i < idx_vecs) idx_dst[i] = r[u];
+    }
+    return;
+  }
+  const int64_t gid =
+      static_cast<int64_t>(blockIdx.x - copy_wgs) * kPrologueThreads + threadIdx.x;
+  if (gid >= total_vecs) return;
+  const int64_t row = gid / row_vecs;  // token * num_heads + head
+  const int c = static_cast<int>(gid - row * row_vecs);
+  const int64_t tok = row / num_heads;
+  const int h = static_cast<int>(row - tok * num_heads);
+  const int32_t slot = slots_host[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int off = slot - static_cast<int32_t>(blk) * block_size;
+  const int64_t dst = ((blk * num_heads + h) * block_size + off) * row_vecs + c;
+  k_pool[dst] = k[gid];
+  v_pool[dst] = v[gid];
+}
 
 // Most decode work items n sequences with tables of max_blocks entries can produce.
 int32_t max_work_items(const pkv_cache_desc_t* d, int32_t n, int32_t max_blocks) {
@@ -51,14 +74,35 @@ size_t index_ints(int32_t n, int32_t max_blocks, int32_t max_items) {
   return static_cast<size_t>(n) * max_blocks + 4 * static_cast<size_t>(n) + max_items;
 }
 
-}  // namespace
-
-extern "C" {
-
-static size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_items) {
+size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_items) {
   return static_cast<size_t>(pkv::align_up(
       static_cast<int64_t>(index_ints(max_seqs, max_blocks_per_seq, max_items) * 4), 256));
 }
+
+}  // namespace
+
+// Two stages are used alternately.  Stage k owns a pinned host area and a device area of
+// d_index.  The prologue of step i reads the host area of its stage; the host refills that
+// area at step i+2 only after the event recorded behind that prologue has fired.  The device
+// area is rewritten at step i+2 by a kernel on the same stream, so step i's readers are done.
+struct pkv_stepper {
+  pkv_alloc_t* alloc = nullptr;
+  pkv_cache_desc_t desc{};
+  int32_t max_seqs = 0;
+  int32_t max_blocks = 0;
+  int32_t max_items = 0;                   // decode work items per step, at most
+  std::vector<int32_t> keys, sorted_keys;  // per-step scratch for the sharing test
+  struct Stage {
+    int32_t* host = nullptr;        // pinned: tables | lens | slots | pairs | items
+    const char* host_dev = nullptr; // the same memory as the device sees it
+    char* dev = nullptr;            // device area of the same size inside d_index
+    hipEvent_t read = nullptr;      // recorded behind the prologue that read `host`
+    bool pending = false;
+  } stage[2];
+  int cur = 0;
+};
+
+extern "C" {
 
 size_t pkv_stepper_index_bytes(const pkv_cache_desc_t* desc, int32_t max_seqs,
                                int32_t max_blocks_per_seq) {
@@ -80,37 +124,32 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   st->max_blocks = max_blocks_per_seq;
   st->max_items = max_work_items(desc, max_seqs, max_blocks_per_seq);
   const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq, st->max_items);
-  if (hipStreamCreateWithFlags(&st->copy_stream, hipStreamNonBlocking) != hipSuccess) {
-    st->copy_stream = nullptr;
-    pkv_stepper_destroy(st);
-    return nullptr;
-  }
   for (int k = 0; k < 2; ++k) {
     auto& sg = st->stage[k];
     sg.dev = static_cast<char*>(d_index) + k * bytes;
-    if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes, hipHostMallocDefault) !=
+    void* dptr = nullptr;
+    if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes, hipHostMallocMapped) !=
             hipSuccess ||
-        hipEventCreateWithFlags(&sg.copied, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&sg.consumed, hipEventDisableTiming) != hipSuccess) {
+        hipHostGetDevicePointer(&dptr, sg.host, 0) != hipSuccess ||
+        hipEventCreateWithFlags(&sg.read, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
       pkv_stepper_destroy(st);
       return nullptr;
     }
+    sg.host_dev = static_cast<const char*>(dptr);
   }
   return st;
 }
 
 void pkv_stepper_destroy(pkv_stepper_t* st) {
   if (!st) return;
-  if (st->copy_stream) (void)hipStreamSynchronize(st->copy_stream);
   for (auto& sg : st->stage) {
-    if (sg.consumed) {
-      if (sg.used) (void)hipEventSynchronize(sg.consumed);
-      (void)hipEventDestroy(sg.consumed);
+    if (sg.read) {
+      if (sg.pending) (void)hipEventSynchronize(sg.read);
+      (void)hipEventDestroy(sg.read);
     }
-    if (sg.copied) (void)hipEventDestroy(sg.copied);
     if (sg.host) (void)hipHostFree(sg.host);
   }
-  if (st->copy_stream) (void)hipStreamDestroy(st->copy_stream);
   delete st;
 }
 
@@ -128,13 +167,20 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int32_t L = io->num_layers;
   if (L > 0 && (!io->k_pools || !io->v_pools || !io->q || !io->k_new || !io->v_new || !io->out))
     return PKV_EINVAL;
+  for (int32_t l = 0; l < L; ++l)
+    if (!io->k_pools[l] || !io->v_pools[l] || !io->k_new[l] || !io->v_new[l] ||
+        reinterpret_cast<uintptr_t>(io->k_new[l]) % 16 ||
+        reinterpret_cast<uintptr_t>(io->v_new[l]) % 16 ||
+        reinterpret_cast<uintptr_t>(io->k_pools[l]) % 16 ||
+        reinterpret_cast<uintptr_t>(io->v_pools[l]) % 16)
+      return PKV_EINVAL;
 
   st->cur ^= 1;
   auto& sg = st->stage[st->cur];
-  if (sg.copy_pending) {
-    // the upload issued from this host area two steps ago must have read it
-    if (hipEventSynchronize(sg.copied) != hipSuccess) return PKV_EHIP;
-    sg.copy_pending = false;
+  if (sg.pending) {
+    // the prologue that read this host area two steps ago must be done with it
+    if (hipEventSynchronize(sg.read) != hipSuccess) return PKV_EHIP;
+    sg.pending = false;
   }
   const int32_t MB = st->max_blocks;
   int32_t* tables = sg.host;
@@ -150,7 +196,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   // Sequences whose first physical block is the same share a prefix: schedule them side by
   // side and read K/V with cache-allocating loads; otherwise longest first, nontemporal.
   st->keys.resize(static_cast<size_t>(n));
-  for (int32_t i = 0; i < n; ++i) st->keys[i] = lens[i] > 0 ? tables[static_cast<size_t>(i) * MB] : -1 - i;
+  for (int32_t i = 0; i < n; ++i)
+    st->keys[i] = lens[i] > 0 ? tables[static_cast<size_t>(i) * MB] : -1 - i;
   st->sorted_keys.assign(st->keys.begin(), st->keys.end());
   std::sort(st->sorted_keys.begin(), st->sorted_keys.end());
   const bool shared =
@@ -163,18 +210,37 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   if (num_items < 0) return PKV_EINVAL;
   const uint32_t decode_flags = shared ? PKV_DECODE_SHARED_KV : 0u;
 
-  const size_t used = (static_cast<size_t>(n) * MB + 2 * static_cast<size_t>(n) +
-                       2 * static_cast<size_t>(*num_cow) + num_items) * sizeof(int32_t);
+  const size_t used_ints = static_cast<size_t>(n) * MB + 2 * static_cast<size_t>(n) +
+                           2 * static_cast<size_t>(*num_cow) + num_items;
+  const int idx_vecs = static_cast<int>((used_ints * 4 + 15) / 16);
+  const int copy_wgs = (idx_vecs + kPrologueThreads * kCopyVecsPerThread - 1) /
+                       (kPrologueThreads * kCopyVecsPerThread);
+  // The first layer's append rides in the prologue unless copy-on-write copies must land
+  // first (a copy would overwrite the new token in its destination block).
+  const bool fuse_append = L > 0 && *num_cow == 0;
+  const int row_vecs = st->desc.head_dim * pkv::dtype_bytes(st->desc.dtype) / 16;
+  const int64_t total_vecs =
+      fuse_append ? static_cast<int64_t>(n) * st->desc.num_heads * row_vecs : 0;
+  const int64_t append_wgs = (total_vecs + kPrologueThreads - 1) / kPrologueThreads;
+  if (copy_wgs + append_wgs > INT32_MAX) return PKV_EUNSUPPORTED;
+
   hipStream_t hs = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  // upload after the last reader of this device area, then make the kernels wait for it
-  if ((sg.used && hipStreamWaitEvent(st->copy_stream, sg.consumed, 0) != hipSuccess) ||
-      hipMemcpyAsync(sg.dev, sg.host, used, hipMemcpyHostToDevice, st->copy_stream) !=
-          hipSuccess ||
-      hipEventRecord(sg.copied, st->copy_stream) != hipSuccess ||
-      hipStreamWaitEvent(hs, sg.copied, 0) != hipSuccess)
+  const int32_t* slots_host_dev =
+      reinterpret_cast<const int32_t*>(sg.host_dev) + static_cast<size_t>(n) * MB + n;
+  hipLaunchKernelGGL(
+      step_prologue_kernel, dim3(static_cast<unsigned>(copy_wgs + append_wgs)),
+      dim3(kPrologueThreads), 0, hs, reinterpret_cast<const pkv::u32x4*>(sg.host_dev),
+      reinterpret_cast<pkv::u32x4*>(sg.dev), idx_vecs, copy_wgs, slots_host_dev,
+      fuse_append ? static_cast<const pkv::u32x4*>(io->k_new[0]) : nullptr,
+      fuse_append ? static_cast<const pkv::u32x4*>(io->v_new[0]) : nullptr,
+      fuse_append ? static_cast<pkv::u32x4*>(io->k_pools[0]) : nullptr,
+      fuse_append ? static_cast<pkv::u32x4*>(io->v_pools[0]) : nullptr, total_vecs, row_vecs,
+      st->desc.num_heads, st->desc.block_size,
+      static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size);
+  if (hipGetLastError() != hipSuccess || hipEventRecord(sg.read, hs) != hipSuccess)
     return PKV_EHIP;
-  sg.copy_pending = true;
+  sg.pending = true;
 
   const int32_t* d_tables = reinterpret_cast<const int32_t*>(sg.dev);
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;
@@ -182,35 +248,29 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int32_t* d_pairs = d_slots + n;
   const int32_t* d_items = d_pairs + 2 * static_cast<size_t>(*num_cow);
 
-  // launches; whatever happens, mark the end of this step's reads of the device area
-  auto launch_all = [&]() -> pkv_status_t {
-    if (*num_cow > 0 && L > 0) {
-      pkv_status_t r =
-          pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
-      if (r != PKV_OK) return r;
+  if (*num_cow > 0 && L > 0) {
+    s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
+    if (s != PKV_OK) return s;
+  }
+  for (int32_t l = 0; l < L; ++l) {
+    if (!(l == 0 && fuse_append)) {
+      s = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l], io->k_pools[l],
+                                io->v_pools[l], d_slots, n, stream);
+      if (s != PKV_OK) return s;
     }
-    for (int32_t l = 0; l < L; ++l) {
-      pkv_status_t r = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l],
-                                             io->k_pools[l], io->v_pools[l], d_slots, n, stream);
-      if (r != PKV_OK) return r;
-      if (attn_events &&
-          hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
-        return PKV_EHIP;
-      r = pkv_paged_attention_decode_scheduled(
-          &st->desc, io->out[l], io->q[l], io->k_pools[l], io->v_pools[l], d_tables, MB, d_lens,
-          n, *max_len, io->scale, d_items, num_items, decode_flags, workspace, workspace_bytes,
-          stream);
-      if (r != PKV_OK) return r;
-      if (attn_events &&
-          hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)
-        return PKV_EHIP;
-    }
-    return PKV_OK;
-  };
-  s = launch_all();
-  if (hipEventRecord(sg.consumed, hs) != hipSuccess) return PKV_EHIP;
-  sg.used = true;
-  return s;
+    if (attn_events &&
+        hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
+      return PKV_EHIP;
+    s = pkv_paged_attention_decode_scheduled(&st->desc, io->out[l], io->q[l], io->k_pools[l],
+                                             io->v_pools[l], d_tables, MB, d_lens, n, *max_len,
+                                             io->scale, d_items, num_items, decode_flags,
+                                             workspace, workspace_bytes, stream);
+    if (s != PKV_OK) return s;
+    if (attn_events &&
+        hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)
+      return PKV_EHIP;
+  }
+  return PKV_OK;
 }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {

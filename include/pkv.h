@@ -153,6 +153,58 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
     size_t workspace_bytes, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Multi-query paged attention: several new tokens of each sequence at once.
+ * ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" -> "Prefix
+ * Caching": a request whose prompt prefix is cached only computes the rest of its prompt;
+ * same page, "Speculative Decoding Integration": draft tokens checked by the target model;
+ * "The PagedAttention Algorithm", step 5: keys and values are gathered through the block
+ * table.)
+ *
+ * Sequence s holds L_s = context_lens[s] tokens in the cache (clamped to max_context_len and
+ * to max_blocks_per_seq * block_size); the last n_s = query_start[s+1] - query_start[s] of
+ * them are its new tokens, whose K/V must already be in their slots (pkv_reshape_and_cache).
+ * New token i (q row query_start[s] + i) sits at position P = L_s - n_s + i and attends to
+ * positions 0 .. P only:
+ *     out[query_start[s] + i][h] = softmax_t(scale * <q[query_start[s] + i][h], K_t>) V_t,
+ *                                  t = 0 .. P, K_t, V_t read through block_tables[s]
+ * A sequence with n_s = 1 is single-query decode; n_s = 0 contributes no rows.
+ *
+ *   out, q        device, [T][num_heads][head_dim], dtype, contiguous, 16-byte aligned;
+ *                 T = query_start[num_seqs]; out is written, q is read
+ *   k_pool,v_pool device, pool layout above, 16-byte aligned; read only
+ *   block_tables  device, int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  device, int32 [num_seqs]
+ *   query_start   device, int32 [num_seqs + 1], nondecreasing from 0
+ *   max_query_len host: at least every n_s (rows of a longer sequence past it stay unwritten)
+ *   work_items    NULL (one workgroup per (sequence, 64-token tile, head) of max_query_len),
+ *                 or device items from pkv_multi_query_schedule (num_items of them)
+ * Storage types f16 and bf16 only (the products run on 16-bit matrix-core instructions):
+ * PKV_EUNSUPPORTED for f32.  Scores and outputs accumulate in fp32; the probabilities enter
+ * the second product as fp16 (f16), or as a bf16 pair hi + lo (bf16).  A block id outside [0, num_blocks) among a
+ * tile's keys is never dereferenced: that tile's outputs are NaN; so are the rows of a
+ * sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned pointers, negative
+ * sizes, non-finite scale, bad num_items), PKV_EUNSUPPORTED, PKV_EHIP or PKV_OK.
+ *
+ * pkv_multi_query_schedule (host only): one item per (sequence s, tile of
+ * pkv_multi_query_tile() new tokens) from host copies of query_start and context_lens,
+ * encoded s | tile << 20; sequences that read the most keys first, a sequence's tiles
+ * adjacent (the one reading the most keys first) so they share its K/V in L2.  Returns the
+ * number of items, or -1 for bad arguments, capacity too small, a decreasing query_start,
+ * num_seqs > 2^20 or more than 2^11 tiles per sequence.  Outputs are bit-identical for any
+ * item order.
+ */
+int32_t pkv_multi_query_tile(void);
+int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t* items,
+                                 int32_t capacity);
+pkv_status_t pkv_paged_attention_multi_query(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+    int32_t max_query_len, int32_t max_context_len, float scale, const int32_t* work_items,
+    int32_t num_items, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Append new tokens' keys and values to the cache.
  * ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
  * step 2: generated tokens fill the current block.)

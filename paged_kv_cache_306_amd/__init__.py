@@ -59,6 +59,10 @@ _SIGNATURES = {
                                                     _sz, _p]),
     "pkv_paged_attention_decode": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                                           _p, _sz, _p]),
+    "pkv_multi_query_tile": (_i32, []),
+    "pkv_multi_query_schedule": (_i32, [_p, _p, _i32, _i32, _p, _i32]),
+    "pkv_paged_attention_multi_query": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p, _i32,
+                                               _i32, _i32, _f32, _p, _i32, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
     "pkv_copy_blocks": (_i32, [_pdesc, _p, _p, _i32, _p, _i32, _p]),
     "pkv_alloc_create": (_p, [_i32, _i32, _p]),
@@ -216,6 +220,63 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
             *args, _dev(work_items, "work_items", torch.int32), int(work_items.numel()),
             PKV_DECODE_SHARED_KV if shared_kv else 0, ws_ptr, ws_bytes, _stream_ptr(stream))
         _check(st, "pkv_paged_attention_decode_scheduled")
+    return out
+
+
+def multi_query_tile() -> int:
+    """New tokens per workgroup tile of the multi-query kernel."""
+    return int(_lib().pkv_multi_query_tile())
+
+
+def multi_query_schedule(query_start, context_lens, max_context_len: int):
+    """Host-built work items (int32 numpy) for multi-query attention from host copies of
+    query_start [S+1] and context_lens [S]: one per (sequence, tile) with new tokens."""
+    import numpy as np
+    qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    S = int(cl.shape[0])
+    if qs.shape != (S + 1,):
+        raise ValueError("query_start needs num_seqs + 1 entries")
+    tile = multi_query_tile()
+    n = np.diff(qs.astype(np.int64))
+    cap = max(1, int(np.sum(np.maximum(-(-n // tile), 0))))
+    items = np.empty(cap, np.int32)
+    k = _lib().pkv_multi_query_schedule(qs.ctypes.data_as(ctypes.c_void_p),
+                                        cl.ctypes.data_as(ctypes.c_void_p), S,
+                                        int(max_context_len),
+                                        items.ctypes.data_as(ctypes.c_void_p), cap)
+    if k < 0:
+        raise PkvError(PKV_EINVAL, "pkv_multi_query_schedule")
+    return items[:k].copy()
+
+
+def paged_attention_multi_query(out, q, k_pool, v_pool, block_tables, context_lens, query_start,
+                                scale: float, max_query_len: int, max_context_len: int,
+                                work_items=None, stream=None):
+    """Several new tokens per sequence: row query_start[s] + i of q attends to positions
+    0 .. context_lens[s] - n_s + i of sequence s, read through block_tables (include/pkv.h).
+    q/out: [T][H][D]; query_start: int32 device [S+1]; ``work_items``: int32 device tensor from
+    multi_query_schedule, or None for the plain grid."""
+    import torch
+    desc = desc_for_pool(k_pool)
+    S = context_lens.shape[0]
+    if q.shape != out.shape or q.dim() != 3 or q.shape[1:] != (desc.num_heads, desc.head_dim):
+        raise ValueError("q/out shape mismatch")
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool/v_pool mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("block_tables/query_start shape mismatch")
+    work = (_dev(work_items, "work_items", torch.int32) if work_items is not None
+            else ctypes.c_void_p(0))
+    st = _lib().pkv_paged_attention_multi_query(
+        ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, int(max_query_len),
+        int(max_context_len), float(scale), work,
+        int(work_items.numel()) if work_items is not None else 0, _stream_ptr(stream))
+    _check(st, "pkv_paged_attention_multi_query")
     return out
 
 

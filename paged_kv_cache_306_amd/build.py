@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["pkv_decode.hip", "pkv_cache_ops.hip", "pkv_step.hip"]
+HIP_SOURCES = ["pkv_decode.hip", "pkv_multi_query.hip", "pkv_cache_ops.hip", "pkv_step.hip"]
 CXX_SOURCES = ["pkv_alloc.cpp"]
 ARCH = "gfx950"
 

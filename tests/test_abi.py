@@ -121,6 +121,63 @@ def test_decode_schedule_covers_every_partition_longest_first():
     assert pkv.lib().pkv_decode_schedule(ctypes.byref(d), None, 5, 300, None, 8) == -1
 
 
+def _mq(desc, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, cl=FAKE, qs=FAKE, S=2, maxq=64,
+             maxlen=64, scale=0.1, work=None, nitems=0)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attention_multi_query(
+        ctypes.byref(desc) if desc is not None else None, a["out"], a["q"], a["k"], a["v"],
+        a["bt"], a["mb"], a["cl"], a["qs"], a["S"], a["maxq"], a["maxlen"], a["scale"],
+        a["work"], a["nitems"], None)
+
+
+def test_multi_query_argument_errors():
+    assert _mq(None) == pkv.PKV_EINVAL
+    assert _mq(_desc(dt=0)) == pkv.PKV_EUNSUPPORTED                # f32: no 16-bit products
+    assert _mq(_desc(d=96)) == pkv.PKV_EUNSUPPORTED
+    assert _mq(_desc(bs=12)) == pkv.PKV_EUNSUPPORTED
+    assert _mq(_desc(), qs=None) == pkv.PKV_EINVAL
+    assert _mq(_desc(), out=None) == pkv.PKV_EINVAL
+    assert _mq(_desc(), q=ctypes.c_void_p(0x1008)) == pkv.PKV_EINVAL    # not 16-byte aligned
+    assert _mq(_desc(), S=-1) == pkv.PKV_EINVAL
+    assert _mq(_desc(), maxq=-1) == pkv.PKV_EINVAL
+    assert _mq(_desc(), mb=0) == pkv.PKV_EINVAL
+    assert _mq(_desc(), scale=float("inf")) == pkv.PKV_EINVAL
+    assert _mq(_desc(), work=FAKE, nitems=2 * 1 + 1) == pkv.PKV_EINVAL   # 2 seqs x 1 tile
+    assert _mq(_desc(), work=FAKE, nitems=-1) == pkv.PKV_EINVAL
+    assert _mq(_desc(), maxq=64 * 2048 + 1) == pkv.PKV_EUNSUPPORTED     # tiles past 2^11
+    assert _mq(_desc(), S=0) == pkv.PKV_OK                               # nothing to do
+    assert _mq(_desc(), maxq=0) == pkv.PKV_OK
+
+
+def test_multi_query_schedule_covers_every_tile_by_sequence():
+    import numpy as np
+    tile = pkv.multi_query_tile()
+    assert tile == 64
+    n = np.array([3, 0, 200, 64, 65, 1], np.int64)
+    ctx = np.array([1000, 50, 200, 5000, 65, 1], np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    items = pkv.multi_query_schedule(qs, ctx, 6000)
+    seqs, tiles = (items & ((1 << 20) - 1)).tolist(), (items >> 20).tolist()
+    want = [(s, t) for s in range(len(n)) for t in range(-(-int(n[s]) // tile))]
+    assert sorted(zip(seqs, tiles)) == sorted(want)
+    # sequences by the keys their last token sees (5000, 1000, 200, 65, 1); tiles adjacent,
+    # the tile whose last token sees the most keys first
+    assert seqs == [3, 0, 2, 2, 2, 2, 4, 4, 5]
+    assert tiles[2:6] == [3, 2, 1, 0] and tiles[6:8] == [1, 0]
+    # max_context_len clamps the key counts: sequence 3 drops to 200 keys, after sequence 2
+    items2 = pkv.multi_query_schedule(qs, ctx, 200)
+    assert (items2 & ((1 << 20) - 1)).tolist()[:2] == [0, 2]
+    lib = pkv.lib()
+    buf = np.zeros(16, np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    bad_qs = np.array([0, 5, 3], np.int32)                        # decreasing
+    assert lib.pkv_multi_query_schedule(ptr(bad_qs), ptr(ctx), 2, 100, ptr(buf), 16) == -1
+    assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 6, 6000, ptr(buf), 8) == -1   # 9 items
+    assert lib.pkv_multi_query_schedule(None, ptr(ctx), 6, 6000, ptr(buf), 16) == -1
+    assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 0, 6000, ptr(buf), 0) == 0
+
+
 def test_workspace_size_formula():
     d = _desc(h=40, d=128)
     assert pkv.decode_workspace_bytes(d, 64, 100) == 0        # single pass

@@ -1,0 +1,180 @@
+"""Parity of multi-query paged attention (through the C ABI binding) with the float64 oracle.
+
+Small cases mix every shape of new-token run: a whole prompt (n = L), prefix-cache hits with
+short and long user turns, runs of exactly one tile, one tile plus one, several tiles, a few
+draft tokens after a long context, single tokens (decode), and sequences with no new token;
+each in f16 and bf16, head sizes 64 and 128, block sizes 8, 16 and 32.  Slots and blocks no
+sequence uses hold NaN, so a stray read shows up.  The full-size case is the chat workload
+after a prefix-cache hit (64 requests, 4 shared 1024-token system prompts, user turns
+U[16,512]), checked on sampled rows.
+
+Tolerance: max abs error <= 2e-3 (fp16 / bf16 outputs), widened to one bfloat16 ulp where
+|ref| >= 0.5, as for decode.  The probabilities enter the output product as fp16 (relative
+error <= 2^-11) or as a bfloat16 hi + lo pair (<= 2^-16), so they add at most 2^-11 times the
+weighted mean of |V| (< 2.5e-4 for these N(0,1) values) on top of fp32 accumulation and the
+final rounding to the storage type.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_306_amd as pkv
+import workloads as W
+from gpu_util import check_close, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (context length, new tokens) per sequence
+RAGGED = [(1, 1), (2, 1), (17, 17), (100, 37), (300, 64), (301, 65), (530, 130), (40, 0),
+          (1000, 3), (64, 64), (129, 1), (257, 200)]
+
+
+def make_mq_case(seed, H, D, BS, pairs, dtype, pool_factor=1.3):
+    g = W.rng(seed)
+    ctx = np.array([c for c, _ in pairs], np.int32)
+    new = np.array([n for _, n in pairs], np.int32)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    tables, nb = W.permuted_block_tables(g, ctx, BS, pool_factor=pool_factor)
+    q = W.normal_values(g, (int(qs[-1]), H, D), dtype)
+    kp = W.normal_values(g, (nb, H, BS, D), dtype)
+    vp = W.normal_values(g, (nb, H, BS, D), dtype)
+    W.poison_unused(kp, tables, ctx, BS, dtype)
+    W.poison_unused(vp, tables, ctx, BS, dtype)
+    return q, kp, vp, tables, ctx, qs
+
+
+def run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, items=None, max_len=None,
+           dev_ctx=None):
+    """Run the HIP kernel; rows it does not write stay NaN."""
+    import torch
+    qd = to_dev(q, dtype, dev)
+    kd = to_dev(kp, dtype, dev)
+    vd = to_dev(vp, dtype, dev)
+    bt = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+    cl = torch.from_numpy(np.ascontiguousarray(ctx if dev_ctx is None else dev_ctx,
+                                               np.int32)).to(dev)
+    qsd = torch.from_numpy(np.ascontiguousarray(qs, np.int32)).to(dev)
+    out = torch.full_like(qd, float("nan"))
+    maxq = int(np.diff(qs).max()) if len(ctx) else 0
+    ml = int(np.max(ctx)) if max_len is None else max_len
+    wi = None if items is None else torch.from_numpy(np.ascontiguousarray(items, np.int32)).to(dev)
+    pkv.paged_attention_multi_query(out, qd, kd, vd, bt, cl, qsd, scale, maxq, ml, work_items=wi)
+    torch.cuda.synchronize()
+    return W.from_torch(out, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("BS", [8, 16, 32])
+def test_multi_query_ragged_matches_oracle(dtype, D, BS):
+    dev = device()
+    H = 4
+    seed = 3000 + BS * 10 + D + (1 if dtype == "bf16" else 0)
+    q, kp, vp, tables, ctx, qs = make_mq_case(seed, H, D, BS, RAGGED, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    got = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev)
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, dtype)
+    err = check_close(oracle.decode(got, dtype), ref, dtype, f"mq {dtype} D{D} BS{BS}")
+    print(f"multi-query {dtype} D{D} BS{BS}: {int(qs[-1])} rows, max abs err {err:.3g}")
+
+
+def test_multi_query_schedule_is_bit_identical_to_the_grid():
+    dev = device()
+    q, kp, vp, tables, ctx, qs = make_mq_case(3101, 4, 128, 16, RAGGED, "f16")
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    plain = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev)
+    items = pkv.multi_query_schedule(qs, ctx, int(ctx.max()))
+    sched = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev, items=items)
+    shuffled = items.copy()
+    W.rng(7).shuffle(shuffled)
+    shuf = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev, items=shuffled)
+    assert np.array_equal(plain.view(np.uint16), sched.view(np.uint16))
+    assert np.array_equal(plain.view(np.uint16), shuf.view(np.uint16))
+
+
+def test_multi_query_single_tokens_are_decode():
+    """One new token per sequence: the same outputs as the oracle's decode."""
+    dev = device()
+    pairs = [(L, 1) for L in (1, 15, 16, 17, 200, 999, 2048)]
+    q, kp, vp, tables, ctx, qs = make_mq_case(3102, 8, 128, 16, pairs, "bf16")
+    scale = 0.09
+    got = run_mq(q, kp, vp, tables, ctx, qs, scale, "bf16", dev)
+    ref = oracle.paged_attention_decode(q, kp, vp, tables, ctx, scale, "bf16")
+    check_close(oracle.decode(got, "bf16"), ref, "bf16", "mq as decode")
+
+
+def test_multi_query_bad_block_and_bad_lengths_give_nan_rows():
+    """A block id outside the pool is never dereferenced: that sequence's rows are NaN; a
+    sequence with more new tokens than context is NaN too; the others are unaffected."""
+    dev = device()
+    pairs = [(100, 37), (300, 70), (50, 10), (80, 5)]
+    q, kp, vp, tables, ctx, qs = make_mq_case(3103, 4, 128, 16, pairs, "f16")
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    tables = tables.copy()
+    tables[1, 0] = kp.shape[0] + 7          # every tile of sequence 1 reads block 0
+    dev_ctx = ctx.copy()
+    dev_ctx[2] = 9                          # 10 new tokens but a context of 9
+    got = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev, dev_ctx=dev_ctx)
+    got = oracle.decode(got, "f16")
+    assert np.isnan(got[qs[1]:qs[2]]).all()
+    assert np.isnan(got[qs[2]:qs[3]]).all()
+    keep = np.r_[qs[0]:qs[1], qs[3]:qs[4]]
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, "f16",
+                                             units=[(s, i, h) for s in (0, 3)
+                                                    for i in range(int(qs[s + 1] - qs[s]))
+                                                    for h in range(4)])
+    check_close(got[keep], ref[keep], "f16", "mq unaffected rows")
+
+
+def test_multi_query_clamps_context_to_max_len():
+    """A context length above max_context_len reads as max_context_len."""
+    dev = device()
+    pairs = [(120, 20), (64, 64), (90, 1)]
+    q, kp, vp, tables, ctx, qs = make_mq_case(3104, 2, 64, 8, pairs, "f16")
+    dev_ctx = ctx.copy()
+    dev_ctx[0] = 5000                       # clamped to max_len = 120
+    got = run_mq(q, kp, vp, tables, ctx, qs, 0.125, "f16", dev, max_len=120, dev_ctx=dev_ctx)
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, 0.125, "f16")
+    check_close(oracle.decode(got, "f16"), ref, "f16", "mq clamp")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multi_query_prefix_hit_full_size_sampled(dtype):
+    """64 chat requests after a prefix-cache hit (LLaMA-13B shapes), scheduled launch;
+    sampled rows (first, tile edges, last of several requests, every head) vs the oracle
+    on the blocks read back from the device."""
+    import torch
+    dev = device()
+    w = W.prefix_hit(dtype=dtype)
+    qs = w.extra["query_start"]
+    T = int(qs[-1])
+    q = W.device_normal((T, w.H, w.D), dtype, 61, dev)
+    kp = W.device_normal((w.num_blocks, w.H, w.BS, w.D), dtype, 62, dev)
+    vp = W.device_normal((w.num_blocks, w.H, w.BS, w.D), dtype, 63, dev)
+    W.poison_unused_device(kp, w.tables, w.lens, w.BS)
+    W.poison_unused_device(vp, w.tables, w.lens, w.BS)
+    bt = torch.from_numpy(w.tables).to(dev)
+    cl = torch.from_numpy(w.lens).to(dev)
+    qsd = torch.from_numpy(qs).to(dev)
+    items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len)).to(dev)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale,
+                                    int(np.diff(qs).max()), w.max_len, work_items=items)
+    torch.cuda.synchronize()
+    got = oracle.decode(W.from_torch(out, dtype), dtype)
+    assert np.isfinite(got).all()
+    q_np = W.from_torch(q, dtype)
+    for s in (0, 17, 33, 63):
+        n = int(qs[s + 1] - qs[s])
+        nbk = W.nblocks_for(int(w.lens[s]), w.BS)
+        idx = torch.from_numpy(w.tables[s, :nbk].astype(np.int64)).to(dev)
+        kc = W.from_torch(kp.index_select(0, idx), dtype)
+        vc = W.from_torch(vp.index_select(0, idx), dtype)
+        tab = np.arange(nbk, dtype=np.int32)[None, :]
+        rows = sorted({0, min(63, n - 1), min(64, n - 1), n - 1})
+        qsub = q_np[qs[s]:qs[s + 1]]
+        for i in rows:
+            for h in range(w.H):
+                ref = oracle.multi_query_unit(qsub, kc, vc, tab, w.lens[s:s + 1],
+                                              np.array([0, n]), w.scale, dtype, 0, i, h)
+                check_close(got[qs[s] + i, h], ref, dtype, f"prefix hit s{s} i{i} h{h}")

@@ -252,6 +252,26 @@ def long_context(seed: int = 4, block_size: int = 16) -> DecodeShape:
                        lens, tables, nb, float(np.float32(1.0 / math.sqrt(128))), seed)
 
 
+def prefix_hit(seed: int = 6, requests: int = 64, prompts: int = 4, system_len: int = 1024,
+               user_lo: int = 16, user_hi: int = 512, block_size: int = 16,
+               dtype: str = "f16") -> DecodeShape:
+    """Chat requests after a prefix-cache hit, LLaMA-13B shapes (40 heads, head_dim 128): each
+    request starts with one of ``prompts`` system prompts of ``system_len`` tokens whose
+    blocks are cached and shared by every request with that prompt (consecutive requests
+    share one), then brings a user turn of uniform [user_lo, user_hi] new tokens.  ``lens``
+    are the context lengths (prompt + user turn); ``extra["query_start"]`` packs the new
+    tokens (the user turns), int32 [requests + 1]."""
+    g = rng(seed)
+    user = uniform_lens(g, requests, user_lo, user_hi)
+    tables, lens, nb = shared_prefix_tables(g, prompts, requests // prompts, system_len, user,
+                                            block_size, pool_factor=1.05)
+    qs = np.concatenate([[0], np.cumsum(user)]).astype(np.int32)
+    return DecodeShape(f"prefix_hit_{dtype}", requests, 40, 128, block_size, dtype, lens,
+                       tables, nb, float(np.float32(1.0 / math.sqrt(128))), seed,
+                       extra={"query_start": qs, "prompts": prompts, "system_len": system_len,
+                              "user_range": (user_lo, user_hi)})
+
+
 def full_step_lens(seed: int = 5, S: int = 512) -> np.ndarray:
     """40-layer step: 512 context lengths, lognormal (mean 600, sigma 0.8), clipped to
     [1, 2048]."""

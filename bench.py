@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="block size x placement sweep of the llama13b_layer and long_context "
                          "workloads: one JSON line per configuration")
+    ap.add_argument("--dtype", choices=("f16", "bf16"), default="f16",
+                    help="storage type of the prefix_hit workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=2560,
                     help="most (sequence, head) units the oracle baseline computes")
@@ -116,7 +118,8 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
-WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "full_step_40")
+WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "full_step_40", "prefix_hit")
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16 matrix peak
 
 
 def workload_spec(name: str, seed: int, block_size: int, placement: str):
@@ -419,6 +422,124 @@ def prefix_cache_bench(args, requests: int = 512, prompts: int = 4, system_len: 
         "host": "the machine bench.py ran on"}), flush=True)
 
 
+def multi_query_bench(args):
+    """Chat requests after a prefix-cache hit: per step, the user turns' new K/V are appended
+    in one pkv_reshape_and_cache call, then every new token attends (one
+    pkv_paged_attention_multi_query launch on a host-built schedule)."""
+    import torch
+    import paged_kv_cache_306_amd as pkv
+    import workloads as W
+    dev = torch.device("cuda:0")
+    w = W.prefix_hit(dtype=args.dtype)
+    qs = w.extra["query_start"]
+    T, H, D, BS, dt = int(qs[-1]), w.H, w.D, w.BS, w.dtype
+    new = np.diff(qs).astype(np.int64)
+    # slots of the new tokens: the last n_s positions of each context
+    slots = np.concatenate([
+        w.tables[s, (np.arange(w.lens[s] - new[s], w.lens[s]) // BS)].astype(np.int64) * BS
+        + np.arange(w.lens[s] - new[s], w.lens[s]) % BS for s in range(w.S)]).astype(np.int32)
+    kp = W.device_normal((w.num_blocks, H, BS, D), dt, 71, dev)
+    vp = W.device_normal((w.num_blocks, H, BS, D), dt, 72, dev)
+    q = W.device_normal((T, H, D), dt, 73, dev)
+    kn = W.device_normal((T, H, D), dt, 74, dev)
+    vn = W.device_normal((T, H, D), dt, 75, dev)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.tables).to(dev)
+    cl = torch.from_numpy(w.lens).to(dev)
+    qsd = torch.from_numpy(qs).to(dev)
+    sl = torch.from_numpy(slots).to(dev)
+    items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len)).to(dev)
+    maxq = int(new.max())
+    # algorithmic work: token i of sequence s sees P + 1 = L_s - n_s + i + 1 keys; per key and
+    # head 2 D flops for the score and 2 D for the output
+    keys = int(sum(int(new[s]) * (int(w.lens[s]) - int(new[s])) + int(new[s]) * (int(new[s]) + 1) // 2
+                   for s in range(w.S)))
+    flops = 4.0 * D * H * keys
+
+    def step():
+        pkv.reshape_and_cache(kn, vn, kp, vp, sl)
+        pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len,
+                                        work_items=items)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, z in evs:
+        pkv.reshape_and_cache(kn, vn, kp, vp, sl)
+        a.record()
+        pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len,
+                                        work_items=items)
+        z.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = float(np.mean([a.elapsed_time(z) for a, z in evs])) / 1e3
+    peak = MFMA_PEAK_TFLOPS[dt]
+    achieved = flops / launch_s / 1e12
+    value = flops * args.steps / wall / 1e12
+    res = {
+        "metric": "multi-query paged attention TFLOP/s after a prefix-cache hit, LLaMA-13B "
+                  "shape", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": f"prefix_hit_{dt}",
+                   "description": f"{w.S} requests, {w.extra['prompts']} shared system prompts "
+                                  f"of {w.extra['system_len']} cached tokens, user turns "
+                                  f"U{list(w.extra['user_range'])} new tokens, 40 heads, "
+                                  "head_dim 128, BS 16",
+                   "requests": w.S, "new_tokens": T, "keys_seen": keys, "heads": H,
+                   "head_dim": D, "block_size": BS, "pool_blocks": w.num_blocks},
+        "new_tokens_per_s": round(T * args.steps / wall, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": f"multi_query_kernel<{dt.upper()},{D},{BS}>",
+                     "avg_launch_us": round(launch_s * 1e6, 2),
+                     "alg_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = multi_query_cpu_baseline(w, q, kp, vp, dt)
+    print(json.dumps(res), flush=True)
+
+
+def multi_query_cpu_baseline(w, q, kp, vp, dt, seconds: float = 8.0):
+    """The float64 oracle on (request, new token, head) units of the same batch, one thread,
+    for about ``seconds``: rows of the first requests, all heads."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import workloads as W
+    qs = w.extra["query_start"]
+    q_np = W.from_torch(q, dt)
+    done, flops, units = 0.0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for s in range(w.S):
+            n = int(qs[s + 1] - qs[s])
+            nbk = W.nblocks_for(int(w.lens[s]), w.BS)
+            idx = torch.from_numpy(w.tables[s, :nbk].astype(np.int64)).to(kp.device)
+            kc = W.from_torch(kp.index_select(0, idx), dt)
+            vc = W.from_torch(vp.index_select(0, idx), dt)
+            tab = np.arange(nbk, dtype=np.int32)[None, :]
+            qsub = q_np[qs[s]:qs[s + 1]]
+            for i in range(n):
+                t0 = time.perf_counter()
+                for h in range(w.H):
+                    oracle.multi_query_unit(qsub, kc, vc, tab, w.lens[s:s + 1],
+                                            np.array([0, n]), w.scale, dt, 0, i, h)
+                done += time.perf_counter() - t0
+                units += w.H
+                flops += 4.0 * w.D * w.H * (int(w.lens[s]) - n + i + 1)
+                if done >= seconds:
+                    break
+            if done >= seconds:
+                break
+    return {"value": flops / done / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} (new token, head) units of the first requests of the same "
+                      f"batch, float64 numpy, {done:.2f} s"}
+
+
 def main():
     args = parse()
     if args.prefix_cache:
@@ -436,6 +557,9 @@ def main():
         return
     if args.swap:
         swap_bench(args)
+        return
+    if args.workload == "prefix_hit":
+        multi_query_bench(args)
         return
     import torch
     dev = torch.device("cuda:0")

@@ -15,6 +15,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["pkv_decode.hip", "pkv_multi_query.hip", "pkv_cache_ops.hip", "pkv_step.hip"]
 CXX_SOURCES = ["pkv_alloc.cpp"]
+# Per-source hipcc flags.  The multi-query kernel keeps its MFMA accumulators in ordinary
+# VGPRs (gfx950 MFMAs take C/D there too): with the accumulation-register form the compiler
+# copies every accumulator between the two register files on each loop iteration.
+EXTRA_HIPCC_FLAGS = {"pkv_multi_query.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -49,8 +53,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
+        _run([_hipcc(), *HIPCC_FLAGS, *EXTRA_HIPCC_FLAGS.get(src, []), "-I", INCLUDE, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")

@@ -8,23 +8,31 @@
 //
 // With many queries per sequence this is a dense contraction, so both products run on the
 // matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate):
-//   * one workgroup = four waves = 64 consecutive new tokens of one (sequence, head); each
-//     wave owns 16 of them;
-//   * keys go 32 at a time through LDS: K rows as stored, V transposed (row = head dim);
-//   * scores S^T = K Q^T: K rows are the A operand, the wave's q rows (kept in registers for
-//     the whole run) the B operand; lane (r, g) = (lane % 16, lane / 16) receives the scores
-//     of query r against keys 4g .. 4g+3 of each 16-key half of the chunk;
+//   * one workgroup = two waves = 64 consecutive new tokens of one (sequence, head); each
+//     wave owns 32 of them as two 16-query MFMA tiles, so every K/V fragment it reads from
+//     LDS feeds two products;
+//   * keys go 32 at a time through a double-buffered LDS stage, K and V rows both as stored
+//     (16-byte writes), with one barrier per chunk and the global loads two chunks ahead;
+//   * scores S^T = K Q^T: K rows are the A operand (16-byte LDS reads), the wave's q rows
+//     (in registers for the whole run) the B operand; lane (r, g) = (lane % 16, lane / 16)
+//     receives the scores of query r against keys 4g .. 4g+3 of each 16-key half;
 //   * softmax runs per query in log2 units with the running max shared by the four lanes of
-//     a query (two cross-row shuffles per chunk); each lane's probabilities, in the storage
-//     type, are directly the B operand of O^T = V^T P^T once the V^T columns are
-//     stored in the matching key order (slot 8g + j holds key 4g + j for j < 4 and key
-//     16 + 4g + j - 4 for j >= 4);
+//     a query (two cross-row shuffles per chunk); each lane's probabilities are directly the
+//     B operand of O^T = V^T P^T when slot 8g + j of the contraction is key 4g + j (j < 4)
+//     or key 16 + 4g + j - 4 (j >= 4);
+//   * the V^T operand comes from the row-major V stage through gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16): within each 16-lane group, component m of lane i is element
+//     i % 4 of the 4 x 16-bit piece addressed by lane 4m + i / 4, so lane (r, g) addresses
+//     key row 4g + r / 4 (then 16 + 4g + r / 4) at head-dim column 16 t + 4 (r % 4);
 //   * O^T accumulates in 16 x 16 tiles: lane (r, g) holds output elements d = 16 t + 4 g + i
 //     of query r.
+// Row padding of the LDS stages (K: 16 bytes, V: 32 bytes) makes both read patterns hit
+// distinct banks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <vector>
 
 #include "pkv.h"
@@ -34,16 +42,21 @@
 namespace pkv {
 namespace {
 
-constexpr int kMqThreads = 256;     // four waves
-constexpr int kMqTileQueries = 64;  // new tokens per workgroup, 16 per wave
-constexpr int kMqChunk = 32;        // keys staged in LDS per step
-constexpr int kMqItemSeqBits = 20;  // work item = sequence | tile << 20
+constexpr int kMqWaves = 2;
+constexpr int kMqThreads = 64 * kMqWaves;
+constexpr int kMqWaveQueries = 32;                          // two 16-query MFMA tiles
+constexpr int kMqTileQueries = kMqWaves * kMqWaveQueries;   // new tokens per workgroup
+constexpr int kMqChunk = 32;                                // keys staged in LDS per step
+constexpr float kMqSlack = 8.0f;  // log2 units a score may exceed the softmax reference by
+constexpr int kMqItemSeqBits = 20;                          // work item = sequence | tile << 20
 constexpr int kMqItemSeqMask = (1 << kMqItemSeqBits) - 1;
 constexpr int kMqMaxTiles = 1 << (31 - kMqItemSeqBits);
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // One 16x16x32 product on fragments held as four 32-bit words each, and how a probability
 // enters the second product.  fp16 carries 11 significant bits: one rounded copy (relative
@@ -74,23 +87,25 @@ struct Mma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
-    hi = BF16::store(x);  // probabilities are finite, in [0, 1]
-    lo = BF16::store(x - __uint_as_float(hi << 16));
-  }
   static __device__ __forceinline__ void pack(float x, float y, uint32_t& hi, uint32_t& lo) {
-    uint32_t hx, lx, hy, ly;
-    split(x, hx, lx);
-    split(y, hy, ly);
-    hi = hx | (hy << 16);
-    lo = lx | (ly << 16);
+    // round to nearest even (v_cvt_pk_bf16_f32); x - hi(x) is exact in fp32
+    const bf16x2 h = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const bf16x2 l = {static_cast<__bf16>(x - __uint_as_float(hi << 16)),
+                      static_cast<__bf16>(y - __uint_as_float(hi & 0xFFFF0000u))};
+    lo = __builtin_bit_cast(uint32_t, l);
   }
 };
 
-// Position of V^T's 16-byte slot group `grp` in LDS row d: the groups of a row are permuted
-// by bits 3..4 of d so that the transposing writes of one instruction (rows 8 apart) spread
-// over more banks.  Reads stay one whole 1 KiB tile per instruction, conflict free.
-__device__ __forceinline__ int vt_group(int d, int grp) { return grp ^ ((d >> 3) & 3); }
+// Zeros that stand in for K/V pieces a workgroup must not read: keys past what it sees and
+// blocks whose id is outside the pool.  One group of pieces of a wave spans 1 KiB.
+__device__ const u32x4 kMqZeros[64] = {};
+
+// Transposing LDS read of four 16-bit elements (see the lane mapping above).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <class Ty, int D, int BS>
 __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
@@ -101,18 +116,20 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const int32_t* __restrict__ work, int tiles_per_seq, int num_heads, int num_blocks,
     int max_len, float scale_log2) {
   using T = typename Ty::store_t;
-  constexpr int KSTEPS = D / 32;             // k-steps of the score product
-  constexpr int DTILES = D / 16;             // 16-row tiles of O^T
-  constexpr int KROW = D + 8;                // halves per K row in LDS (16 bytes of padding)
-  constexpr int COLS = D / 8;                // 16-byte column groups of a K/V row
-  constexpr int LOADERS = (kMqChunk / 2) * COLS;
-  constexpr size_t ROW_BYTES = D * sizeof(T);
+  constexpr int KSTEPS = D / 32;    // k-steps of the score product
+  constexpr int DTILES = D / 16;    // 16-row tiles of O^T
+  constexpr int KROW = D + 8;       // halves per K row in the stage
+  constexpr int VROW = D + 16;      // halves per V row in the stage
+  constexpr int COLS = D / 8;       // 16-byte pieces per K/V row
+  constexpr int GROUP_ROWS = 64 / COLS;                      // key rows of one wave's pieces
+  constexpr int GROUPS = kMqChunk / GROUP_ROWS / kMqWaves;   // piece groups per wave and chunk
+  constexpr int ROW_BYTES = D * sizeof(T);
   static_assert(sizeof(T) == 2, "16-bit storage only");
-  static_assert(LOADERS <= kMqThreads, "one key pair per loader thread");
-  static_assert(BS % 2 == 0, "a key pair never straddles two blocks");
+  static_assert(BS % GROUP_ROWS == 0, "a wave's piece group lies in one block");
+  static_assert(GROUP_ROWS * ROW_BYTES <= sizeof(kMqZeros), "zero stand-in covers a group");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kMqChunk * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * kMqChunk];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kMqChunk * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kMqChunk * VROW];
 
   // Head-fastest order: neighbouring workgroups read the same blocks' other heads.
   const int h = blockIdx.x % num_heads;
@@ -142,149 +159,194 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     return;
   }
 
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int qi = first + wave * 16 + r;          // this lane's query (may be past n)
-  const int qc = min(qi, n - 1);                 // clamped: rows past n compute a copy
-  const int qpos = L - n + qc;                   // last key the query sees
-  const int wave_first = first + wave * 16;
+  const int wave_first = first + wave * kMqWaveQueries;
   const bool wave_on = wave_first < n;
-  const int wave_keys = L - n + min(wave_first + 16, n);  // keys any query of the wave sees
-  const int tile_keys = L - n + first + nq;               // keys any query of the tile sees
+  const int tile_keys = L - n + first + nq;                       // keys the workgroup sees
+  const int wave_keys = L - n + min(wave_first + kMqWaveQueries, n);  // ... the wave sees
   const int nchunks = (tile_keys + kMqChunk - 1) / kMqChunk;
-
-  // The wave's q rows as B fragments: lane (r, g) holds q[r][32k + 8g .. 32k + 8g + 7].
-  u32x4 qf[KSTEPS];
-  {
-    const T* qrow = q + static_cast<size_t>(q0 + qc) * row_stride + static_cast<size_t>(h) * D;
+  // Per 16-query MFMA tile: whether it holds a new token, this lane's query and the last
+  // key that query sees (rows past n compute a copy of the last one).
+  bool qt_on[2];
+  int qi[2], qpos[2];
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) qf[k] = load16(qrow + 32 * k + 8 * g);
+  for (int qt = 0; qt < 2; ++qt) {
+    const int f = wave_first + 16 * qt;
+    qt_on[qt] = f < n;
+    qi[qt] = f + r;
+    qpos[qt] = L - n + min(qi[qt], n - 1);
   }
 
-  // Staging: loader thread (column group lc, pair lp) moves 16 bytes at column 8 lc of keys
-  // 2 lp and 2 lp + 1 of each chunk; keys the tile does not see are staged as zeros, so NaN
-  // in slots past the context never reaches a product.
-  const bool loader = tid < LOADERS;
-  const int lc = tid % COLS, lp = tid / COLS;
+  // q rows as B fragments: lane (r, g) holds q[r][32k + 8g .. 32k + 8g + 7] of each tile.
+  u32x4 qf[2][KSTEPS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const T* qrow = q + static_cast<size_t>(q0 + min(qi[qt], n - 1)) * row_stride +
+                    static_cast<size_t>(h) * D;
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) qf[qt][k] = load16(qrow + 32 * k + 8 * g);
+  }
+
+  // Staging.  Piece group i of this wave covers key rows row0 .. row0 + GROUP_ROWS - 1 of a
+  // chunk (64 pieces of 16 bytes, lane -> row lane / COLS, column 8 (lane % COLS)); the rows
+  // lie in one block, so its id is a scalar and a lane's byte offset inside the group never
+  // changes.  Rows the workgroup does not see and blocks whose id is outside the pool read
+  // zeros instead (a bad id turns the outputs into NaN).
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
-  const gptr_t kbase = uniform_ptr(k_pool);
-  const gptr_t vbase = uniform_ptr(v_pool);
-  u32x4 k0, k1, v0, v1;
+  const int lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
+  const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros));
+  u32x4 st[2 * GROUPS];
   int bad = 0;
   auto fetch = [&](int c) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    k0 = k1 = v0 = v1 = zero;
-    const int t = c * kMqChunk + 2 * lp;
-    if (!loader || t >= tile_keys) return;
-    const int blk = table[t / BS];
-    if (blk < 0 || blk >= num_blocks) {  // never dereferenced; the outputs become NaN
-      bad = 1;
-      return;
-    }
-    const size_t off =
-        ((static_cast<size_t>(blk) * num_heads + h) * BS + t % BS) * ROW_BYTES + lc * 16;
-    k0 = load16<false>(kbase + off);
-    v0 = load16<false>(vbase + off);
-    if (t + 1 < tile_keys) {
-      k1 = load16<false>(kbase + off + ROW_BYTES);
-      v1 = load16<false>(vbase + off + ROW_BYTES);
-    }
-  };
-  auto stage = [&]() {
-    if (!loader) return;
-    const int t = 2 * lp;
-    *reinterpret_cast<u32x4*>(&ks[t * KROW + 8 * lc]) = k0;
-    *reinterpret_cast<u32x4*>(&ks[(t + 1) * KROW + 8 * lc]) = k1;
-    // key t -> V^T slot 8 grp + 4 half + i (t = 16 half + 4 grp + i); keys t, t+1 share a word
-    const int half = t >> 4, grp = (t >> 2) & 3, i = t & 3;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * lc + e;
-      const uint32_t w0 = v0[e >> 1], w1 = v1[e >> 1];
-      const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u))
-                                    : ((w0 & 0xFFFFu) | (w1 << 16));
-      *reinterpret_cast<uint32_t*>(&vt[d * kMqChunk + 8 * vt_group(d, grp) + 4 * half + i]) =
-          pair;
-    }
-  };
-
-  f32x4 acc[DTILES];
-#pragma unroll
-  for (int t = 0; t < DTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;  // running max (log2 units) of query r, equal in its four lanes
-  float lsum = 0.0f;    // this lane's share of the softmax denominator
-
-  fetch(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();  // every wave is done with the previous chunk
-    stage();
-    __syncthreads();
-    if (c + 1 < nchunks) fetch(c + 1);  // in flight while this chunk is computed
-    if (!wave_on || c * kMqChunk >= wave_keys) continue;
-
-    f32x4 sc[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&ks[(16 * hh + r) * KROW + 32 * k + 8 * g]);
-        sc[hh] = Mma<Ty>::run(a, qf[k], sc[hh]);
+    for (int i = 0; i < GROUPS; ++i) {
+      const int row0 = c * kMqChunk + (i * kMqWaves + wave) * GROUP_ROWS;
+      const int blk = table[min(row0, tile_keys - 1) / BS];
+      const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks);
+      bad |= !ok && row0 < tile_keys;
+      const size_t boff =
+          ((static_cast<size_t>(ok ? blk : 0) * num_heads + h) * BS + row0 % BS) * ROW_BYTES;
+      gptr_t kp = ok ? uniform_ptr(k_pool) + boff : zeros;
+      gptr_t vp = ok ? uniform_ptr(v_pool) + boff : zeros;
+      if (row0 + GROUP_ROWS <= tile_keys) {
+        st[i] = load16<false>(kp + lane_off);
+        st[GROUPS + i] = load16<false>(vp + lane_off);
+      } else {  // the group reaches past the keys the workgroup sees (last chunk only)
+        const bool in = row0 + lane / COLS < tile_keys;
+        st[i] = load16<false>(in ? kp + lane_off : zeros);
+        st[GROUPS + i] = load16<false>(in ? vp + lane_off : zeros);
       }
     }
-    float z[8];
-    float cmax = -INFINITY;
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < GROUPS; ++i) {
+      const int t = (i * kMqWaves + wave) * GROUP_ROWS + lane / COLS;
+      const int col = 8 * (lane % COLS);
+      *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = st[i];
+      *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = st[GROUPS + i];
+    }
+  };
+
+  f32x4 acc[2][DTILES];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t) acc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};  // softmax reference (log2 units), equal in a query's lanes
+  float lsum[2] = {0.0f, 0.0f};         // this lane's share of the softmax denominator
+
+  // One chunk of keys for both query tiles of the wave.  MASK: the chunk holds keys that some
+  // query of the wave does not see (its own later positions, or keys past the workgroup's).
+  auto chunk_step = [&](int buf, int c, auto mask) {
+    constexpr bool MASK = decltype(mask)::value;
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = c * kMqChunk + 16 * hh + 4 * g + i;
-        const float v = key <= qpos ? sc[hh][i] * scale_log2 : -INFINITY;
-        z[4 * hh + i] = v;
-        cmax = fmaxf(cmax, v);
+      for (int k = 0; k < KSTEPS; ++k) {
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(&ks[buf][(16 * hh + r) * KROW + 32 * k + 8 * g]);
+        sc[0][hh] = Mma<Ty>::run(a, qf[0][k], sc[0][hh]);
+        sc[1][hh] = Mma<Ty>::run(a, qf[1][k], sc[1][hh]);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float mn = fmaxf(m, cmax);  // finite: chunk 0 holds key 0, which every query sees
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float p[8], ps = 0.0f;
+    // Online softmax with a lazily moved reference: m moves only when a scaled score exceeds
+    // it by more than kMqSlack, so probabilities stay below 2^kMqSlack and the accumulators
+    // are rescaled only on those rare moves.  scale > 0, so the largest raw score gives the
+    // largest scaled one, and exp2(scale * s - m) is one FMA and one exp.
+    u32x4 pf[2], pfl[2];
+    float alpha[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(z[e] - mn);
-      ps += p[e];
+    for (int qt = 0; qt < 2; ++qt) {
+      float z[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = sc[qt][hh][i];
+          z[4 * hh + i] = MASK && c * kMqChunk + 16 * hh + 4 * g + i > qpos[qt] ? -INFINITY : v;
+        }
+      float cmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float cm = cmax * scale_log2;
+      // m is -inf until the query's first chunk (which holds key 0, seen by every query)
+      const float mn = cm > m[qt] + kMqSlack ? cm : m[qt];
+      alpha[qt] = mn == m[qt] ? 1.0f : __builtin_amdgcn_exp2f(m[qt] - mn);
+      float p[8], ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], scale_log2, -mn));
+        ps += p[e];
+      }
+      lsum[qt] = fmaf(lsum[qt], alpha[qt], ps);
+      m[qt] = mn;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
+      pf[qt] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      pfl[qt] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
-    lsum = fmaf(lsum, alpha, ps);
-    m = mn;
-    uint32_t ph[4], pl[4];
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
-    const u32x4 pf = {ph[0], ph[1], ph[2], ph[3]};
-    const u32x4 pfl = {pl[0], pl[1], pl[2], pl[3]};
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int t = 0; t < DTILES; ++t) acc[qt][t] *= alpha[qt];
+    }
+    // outputs: V^T fragments through the transposing read
+    const uint16_t* vrow = &vs[buf][(4 * g + (r >> 2)) * VROW + 4 * (r & 3)];
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {
-      const int d = 16 * t + r;
-      const u32x4 a =
-          *reinterpret_cast<const u32x4*>(&vt[d * kMqChunk + 8 * vt_group(d, g)]);
-      acc[t] = Mma<Ty>::run(a, pf, acc[t] * alpha);
-      if constexpr (Mma<Ty>::kSplit) acc[t] = Mma<Ty>::run(a, pfl, acc[t]);
+      const uint2 lo = lds_read_tr16(vrow + 16 * t);
+      const uint2 hi = lds_read_tr16(vrow + 16 * VROW + 16 * t);
+      const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        acc[qt][t] = Mma<Ty>::run(a, pf[qt], acc[qt][t]);
+        if constexpr (Mma<Ty>::kSplit) acc[qt][t] = Mma<Ty>::run(a, pfl[qt], acc[qt][t]);
+      }
     }
+  };
+
+  fetch(0);
+  stage(0);
+  if (nchunks > 1) fetch(1);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) {
+      stage(buf ^ 1);  // the other buffer was last read during chunk c - 1
+      if (c + 2 < nchunks) fetch(c + 2);
+    }
+    // a tile past the wave's queries, or one whose queries all come before this chunk, gets
+    // only masked scores and adds nothing
+    if (wave_on && c * kMqChunk < wave_keys) chunk_step(buf, c, std::true_type{});
+    __syncthreads();
   }
 
   const int any_bad = __syncthreads_or(bad);
-  if (!wave_on) return;
-  float lt = lsum + __shfl_xor(lsum, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (qi >= n) return;
-  const float inv = any_bad ? NAN : 1.0f / lt;
-  T* orow = out + static_cast<size_t>(q0 + qi) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
-  for (int t = 0; t < DTILES; ++t) {
-    T o[4];
+  for (int qt = 0; qt < 2; ++qt) {
+    if (!qt_on[qt]) continue;  // uniform in the wave
+    float lt = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (qi[qt] >= n) continue;
+    const float inv = any_bad ? NAN : 1.0f / lt;
+    T* orow = out + static_cast<size_t>(q0 + qi[qt]) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = Ty::store(acc[t][i] * inv);
-    uint2 w;
-    __builtin_memcpy(&w, o, sizeof(w));
-    *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
+    for (int t = 0; t < DTILES; ++t) {
+      T o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = Ty::store(acc[qt][t][i] * inv);
+      uint2 w;
+      __builtin_memcpy(&w, o, sizeof(w));
+      *reinterpret_cast<uint2*>(orow + 16 * t + 4 * g) = w;
+    }
   }
 }
 
@@ -398,7 +460,7 @@ pkv_status_t pkv_paged_attention_multi_query(
   if (st != PKV_OK) return st;
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
   if (num_seqs < 0 || max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
-      !std::isfinite(scale))
+      !std::isfinite(scale) || !(scale > 0.0f))
     return PKV_EINVAL;
   if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)

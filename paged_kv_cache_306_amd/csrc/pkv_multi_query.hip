@@ -166,6 +166,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const bool wave_on = wave_first < n;
   const int tile_keys = L - n + first + nq;                       // keys the workgroup sees
   const int wave_keys = L - n + min(wave_first + kMqWaveQueries, n);  // ... the wave sees
+  const int wave_unmasked = L - n + wave_first + 1;  // keys every query of the wave sees
   const int nchunks = (tile_keys + kMqChunk - 1) / kMqChunk;
   // Per 16-query MFMA tile: whether it holds a new token, this lane's query and the last
   // key that query sees (rows past n compute a copy of the last one).
@@ -238,10 +239,10 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   float m[2] = {-INFINITY, -INFINITY};  // softmax reference (log2 units), equal in a query's lanes
   float lsum[2] = {0.0f, 0.0f};         // this lane's share of the softmax denominator
 
-  // One chunk of keys for both query tiles of the wave.  MASK: the chunk holds keys that some
-  // query of the wave does not see (its own later positions, or keys past the workgroup's).
-  auto chunk_step = [&](int buf, int c, auto mask) {
-    constexpr bool MASK = decltype(mask)::value;
+  // One chunk of keys for both query tiles of the wave.  mask: the chunk holds keys that some
+  // query of the wave does not see (its own later positions, or keys past the workgroup's);
+  // wave-uniform.
+  auto chunk_step = [&](int buf, int c, bool mask) {
     f32x4 sc[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -254,38 +255,55 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
         sc[0][hh] = Mma<Ty>::run(a, qf[0][k], sc[0][hh]);
         sc[1][hh] = Mma<Ty>::run(a, qf[1][k], sc[1][hh]);
       }
-    // Online softmax with a lazily moved reference: m moves only when a scaled score exceeds
-    // it by more than kMqSlack, so probabilities stay below 2^kMqSlack and the accumulators
-    // are rescaled only on those rare moves.  scale > 0, so the largest raw score gives the
-    // largest scaled one, and exp2(scale * s - m) is one FMA and one exp.
-    u32x4 pf[2], pfl[2];
-    float alpha[2];
+    float z[2][8];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float z[8];
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = sc[qt][hh][i];
-          z[4 * hh + i] = MASK && c * kMqChunk + 16 * hh + 4 * g + i > qpos[qt] ? -INFINITY : v;
+        for (int i = 0; i < 4; ++i) z[qt][4 * hh + i] = sc[qt][hh][i];
+    if (mask) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (c * kMqChunk + 16 * (e >> 2) + 4 * g + (e & 3) > qpos[qt]) z[qt][e] = -INFINITY;
+    }
+    // Online softmax with a lazily moved reference: m moves only when a scaled score exceeds
+    // it by more than kMqSlack, so probabilities stay below 2^kMqSlack and the accumulators
+    // are rescaled only on those rare moves.  scale > 0, so the largest raw score gives the
+    // largest scaled one, and exp2(scale * s - m) is one FMA and one exp.  A lane first
+    // checks its own scores; only when some lane of the wave would move is the maximum over
+    // each query's four lanes taken (so the four lanes of a query always agree on m).
+    float lmax[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+      lmax[qt] = fmaxf(fmaxf(fmaxf(z[qt][0], z[qt][1]), fmaxf(z[qt][2], z[qt][3])),
+                       fmaxf(fmaxf(z[qt][4], z[qt][5]), fmaxf(z[qt][6], z[qt][7]))) *
+                 scale_log2;
+    float alpha[2] = {1.0f, 1.0f};
+    if (__builtin_amdgcn_ballot_w64(lmax[0] > m[0] + kMqSlack || lmax[1] > m[1] + kMqSlack)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float cm = fmaxf(lmax[qt], __shfl_xor(lmax[qt], 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        // m is -inf until the query's first chunk (which holds key 0, seen by every query)
+        if (cm > m[qt] + kMqSlack) {
+          alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - cm);
+          m[qt] = cm;
         }
-      float cmax = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
-                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float cm = cmax * scale_log2;
-      // m is -inf until the query's first chunk (which holds key 0, seen by every query)
-      const float mn = cm > m[qt] + kMqSlack ? cm : m[qt];
-      alpha[qt] = mn == m[qt] ? 1.0f : __builtin_amdgcn_exp2f(m[qt] - mn);
+      }
+    }
+    u32x4 pf[2], pfl[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
       float p[8], ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(z[e], scale_log2, -mn));
+        p[e] = __builtin_amdgcn_exp2f(fmaf(z[qt][e], scale_log2, -m[qt]));
         ps += p[e];
       }
       lsum[qt] = fmaf(lsum[qt], alpha[qt], ps);
-      m[qt] = mn;
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
@@ -325,7 +343,8 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     }
     // a tile past the wave's queries, or one whose queries all come before this chunk, gets
     // only masked scores and adds nothing
-    if (wave_on && c * kMqChunk < wave_keys) chunk_step(buf, c, std::true_type{});
+    if (wave_on && c * kMqChunk < wave_keys)
+      chunk_step(buf, c, (c + 1) * kMqChunk > wave_unmasked);
     __syncthreads();
   }
 

@@ -143,6 +143,8 @@ def test_multi_query_argument_errors():
     assert _mq(_desc(), maxq=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), mb=0) == pkv.PKV_EINVAL
     assert _mq(_desc(), scale=float("inf")) == pkv.PKV_EINVAL
+    assert _mq(_desc(), scale=-0.5) == pkv.PKV_EINVAL
+    assert _mq(_desc(), scale=0.0) == pkv.PKV_EINVAL
     assert _mq(_desc(), work=FAKE, nitems=2 * 1 + 1) == pkv.PKV_EINVAL   # 2 seqs x 1 tile
     assert _mq(_desc(), work=FAKE, nitems=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), maxq=64 * 2048 + 1) == pkv.PKV_EUNSUPPORTED     # tiles past 2^11

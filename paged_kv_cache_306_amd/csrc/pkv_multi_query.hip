@@ -199,12 +199,20 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const int lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
   const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros));
   u32x4 st[2 * GROUPS];
+  int bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded a chunk early
   int bad = 0;
+  auto load_ids = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < GROUPS; ++i) {
+      const int row0 = c * kMqChunk + (i * kMqWaves + wave) * GROUP_ROWS;
+      bid[i] = table[min(row0, tile_keys - 1) / BS];
+    }
+  };
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
       const int row0 = c * kMqChunk + (i * kMqWaves + wave) * GROUP_ROWS;
-      const int blk = table[min(row0, tile_keys - 1) / BS];
+      const int blk = bid[i];
       const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks);
       bad |= !ok && row0 < tile_keys;
       const size_t boff =
@@ -243,18 +251,24 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   // query of the wave does not see (its own later positions, or keys past the workgroup's);
   // wave-uniform.
   auto chunk_step = [&](int buf, int c, bool mask) {
+    // all K fragments of the chunk first, then the products k-step by k-step over the four
+    // independent accumulators (two query tiles x two 16-key halves)
+    u32x4 kf[2][KSTEPS];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k)
+        kf[hh][k] =
+            *reinterpret_cast<const u32x4*>(&ks[buf][(16 * hh + r) * KROW + 32 * k + 8 * g]);
     f32x4 sc[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int k = 0; k < KSTEPS; ++k)
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(&ks[buf][(16 * hh + r) * KROW + 32 * k + 8 * g]);
-        sc[0][hh] = Mma<Ty>::run(a, qf[0][k], sc[0][hh]);
-        sc[1][hh] = Mma<Ty>::run(a, qf[1][k], sc[1][hh]);
-      }
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) sc[qt][hh] = Mma<Ty>::run(kf[hh][k], qf[qt][k], sc[qt][hh]);
     float z[2][8];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
@@ -331,15 +345,23 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     }
   };
 
+  load_ids(0);
   fetch(0);
   stage(0);
-  if (nchunks > 1) fetch(1);
+  if (nchunks > 1) {
+    load_ids(1);
+    fetch(1);
+    if (nchunks > 2) load_ids(2);
+  }
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunks) {
       stage(buf ^ 1);  // the other buffer was last read during chunk c - 1
-      if (c + 2 < nchunks) fetch(c + 2);
+      if (c + 2 < nchunks) {
+        fetch(c + 2);
+        if (c + 3 < nchunks) load_ids(c + 3);
+      }
     }
     // a tile past the wave's queries, or one whose queries all come before this chunk, gets
     // only masked scores and adds nothing

@@ -8,9 +8,8 @@
 //
 // With many queries per sequence this is a dense contraction, so both products run on the
 // matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate):
-//   * one workgroup = two waves = 64 consecutive new tokens of one (sequence, head); each
-//     wave owns 32 of them as two 16-query MFMA tiles, so every K/V fragment it reads from
-//     LDS feeds two products;
+//   * one workgroup = 64 consecutive new tokens of one (sequence, head), 16 per wave (one
+//     MFMA query tile; the shape is a compile-time choice, see below);
 //   * keys go 32 at a time through a double-buffered LDS stage, K and V rows both as stored
 //     (16-byte writes), with one barrier per chunk and the global loads two chunks ahead;
 //   * scores S^T = K Q^T: K rows are the A operand (16-byte LDS reads), the wave's q rows
@@ -42,9 +41,20 @@
 namespace pkv {
 namespace {
 
-constexpr int kMqWaves = 2;
+// Workgroup shape: 4 waves x one 16-query tile each (64 new tokens per workgroup) runs at
+// 120 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
+// products) halves the LDS bytes per flop but needs ~200 VGPRs and two waves per SIMD; on the
+// prefix-hit workload it was 4-6% slower, with bit-identical outputs.
+#ifndef PKV_MQ_WAVES
+#define PKV_MQ_WAVES 4
+#endif
+#ifndef PKV_MQ_WAVE_TILES
+#define PKV_MQ_WAVE_TILES 1
+#endif
+constexpr int kMqWaves = PKV_MQ_WAVES;          // waves per workgroup
+constexpr int kMqQt = PKV_MQ_WAVE_TILES;        // 16-query MFMA tiles per wave
 constexpr int kMqThreads = 64 * kMqWaves;
-constexpr int kMqWaveQueries = 32;                          // two 16-query MFMA tiles
+constexpr int kMqWaveQueries = 16 * kMqQt;
 constexpr int kMqTileQueries = kMqWaves * kMqWaveQueries;   // new tokens per workgroup
 constexpr int kMqChunk = 32;                                // keys staged in LDS per step
 constexpr float kMqSlack = 8.0f;  // log2 units a score may exceed the softmax reference by
@@ -170,10 +180,10 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const int nchunks = (tile_keys + kMqChunk - 1) / kMqChunk;
   // Per 16-query MFMA tile: whether it holds a new token, this lane's query and the last
   // key that query sees (rows past n compute a copy of the last one).
-  bool qt_on[2];
-  int qi[2], qpos[2];
+  bool qt_on[kMqQt];
+  int qi[kMqQt], qpos[kMqQt];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kMqQt; ++qt) {
     const int f = wave_first + 16 * qt;
     qt_on[qt] = f < n;
     qi[qt] = f + r;
@@ -181,9 +191,9 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   }
 
   // q rows as B fragments: lane (r, g) holds q[r][32k + 8g .. 32k + 8g + 7] of each tile.
-  u32x4 qf[2][KSTEPS];
+  u32x4 qf[kMqQt][KSTEPS];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kMqQt; ++qt) {
     const T* qrow = q + static_cast<size_t>(q0 + min(qi[qt], n - 1)) * row_stride +
                     static_cast<size_t>(h) * D;
 #pragma unroll
@@ -196,63 +206,74 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   // changes.  Rows the workgroup does not see and blocks whose id is outside the pool read
   // zeros instead (a bad id turns the outputs into NaN).
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
-  const int lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
+  const uint32_t lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
   const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros));
-  u32x4 st[2 * GROUPS];
-  int bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded a chunk early
-  int bad = 0;
-  auto load_ids = [&](int c) {
+  const gptr_t kpool = uniform_ptr(k_pool);
+  const gptr_t vpool = uniform_ptr(v_pool);
+  // Loop-invariant parts of a group's address: chunks are whole multiples of the block size
+  // or of a block, so the group's row inside its block never changes.
+  static_assert(kMqChunk % BS == 0 || BS % kMqChunk == 0, "chunks align with blocks");
+  const uint64_t block_stride = static_cast<uint64_t>(num_heads) * BS * ROW_BYTES;
+  uint64_t grp_off[GROUPS];
+  uint32_t grp_row[GROUPS];
 #pragma unroll
-    for (int i = 0; i < GROUPS; ++i) {
-      const int row0 = c * kMqChunk + (i * kMqWaves + wave) * GROUP_ROWS;
-      bid[i] = table[min(row0, tile_keys - 1) / BS];
-    }
+  for (int i = 0; i < GROUPS; ++i) {
+    grp_row[i] = (i * kMqWaves + wave) * GROUP_ROWS;
+    grp_off[i] = (static_cast<uint64_t>(h) * BS + grp_row[i] % BS) * ROW_BYTES;
+  }
+  u32x4 st[2 * GROUPS];
+  uint32_t bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded early
+  bool bad = false;
+  auto load_ids = [&](int c) {
+    const uint32_t last = static_cast<uint32_t>(tile_keys - 1);
+#pragma unroll
+    for (int i = 0; i < GROUPS; ++i)
+      bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
   };
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
-      const int row0 = c * kMqChunk + (i * kMqWaves + wave) * GROUP_ROWS;
-      const int blk = bid[i];
-      const bool ok = static_cast<unsigned>(blk) < static_cast<unsigned>(num_blocks);
-      bad |= !ok && row0 < tile_keys;
-      const size_t boff =
-          ((static_cast<size_t>(ok ? blk : 0) * num_heads + h) * BS + row0 % BS) * ROW_BYTES;
-      gptr_t kp = ok ? uniform_ptr(k_pool) + boff : zeros;
-      gptr_t vp = ok ? uniform_ptr(v_pool) + boff : zeros;
-      if (row0 + GROUP_ROWS <= tile_keys) {
-        st[i] = load16<false>(kp + lane_off);
-        st[GROUPS + i] = load16<false>(vp + lane_off);
-      } else {  // the group reaches past the keys the workgroup sees (last chunk only)
-        const bool in = row0 + lane / COLS < tile_keys;
-        st[i] = load16<false>(in ? kp + lane_off : zeros);
-        st[GROUPS + i] = load16<false>(in ? vp + lane_off : zeros);
-      }
+      const bool ok = bid[i] < static_cast<uint32_t>(num_blocks);
+      bad |= !ok && c * kMqChunk + static_cast<int>(grp_row[i]) < tile_keys;
+      const uint64_t off = static_cast<uint64_t>(bid[i]) * block_stride + grp_off[i];
+      // rows of the group past the keys the workgroup sees still lie inside this block;
+      // staging replaces them with zeros
+      st[i] = load16<false>((ok ? kpool + off : zeros) + lane_off);
+      st[GROUPS + i] = load16<false>((ok ? vpool + off : zeros) + lane_off);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, int c) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bool tail = (c + 1) * kMqChunk > tile_keys;  // uniform
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
-      const int t = (i * kMqWaves + wave) * GROUP_ROWS + lane / COLS;
+      const int t = static_cast<int>(grp_row[i] + lane / COLS);
       const int col = 8 * (lane % COLS);
-      *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = st[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = st[GROUPS + i];
+      const bool in = !tail || c * kMqChunk + t < tile_keys;
+      *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = in ? st[i] : zero;
+      *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = in ? st[GROUPS + i] : zero;
     }
   };
 
-  f32x4 acc[2][DTILES];
+  f32x4 acc[kMqQt][DTILES];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < kMqQt; ++qt)
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) acc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};  // softmax reference (log2 units), equal in a query's lanes
-  float lsum[2] = {0.0f, 0.0f};         // this lane's share of the softmax denominator
+  float m[kMqQt], lsum[kMqQt];  // softmax reference (log2 units, equal in a query's lanes) and
+                                // this lane's share of the denominator
+#pragma unroll
+  for (int qt = 0; qt < kMqQt; ++qt) {
+    m[qt] = -INFINITY;
+    lsum[qt] = 0.0f;
+  }
 
-  // One chunk of keys for both query tiles of the wave.  mask: the chunk holds keys that some
+  // One chunk of keys for the query tiles of the wave.  mask: the chunk holds keys that some
   // query of the wave does not see (its own later positions, or keys past the workgroup's);
   // wave-uniform.
   auto chunk_step = [&](int buf, int c, bool mask) {
-    // all K fragments of the chunk first, then the products k-step by k-step over the four
-    // independent accumulators (two query tiles x two 16-key halves)
+    // all K fragments of the chunk first, then the products k-step by k-step over the
+    // independent accumulators (query tiles x two 16-key halves)
     u32x4 kf[2][KSTEPS];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -260,25 +281,25 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       for (int k = 0; k < KSTEPS; ++k)
         kf[hh][k] =
             *reinterpret_cast<const u32x4*>(&ks[buf][(16 * hh + r) * KROW + 32 * k + 8 * g]);
-    f32x4 sc[2][2];
+    f32x4 sc[kMqQt][2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < kMqQt; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) sc[qt][hh] = Mma<Ty>::run(kf[hh][k], qf[qt][k], sc[qt][hh]);
-    float z[2][8];
+        for (int qt = 0; qt < kMqQt; ++qt) sc[qt][hh] = Mma<Ty>::run(kf[hh][k], qf[qt][k], sc[qt][hh]);
+    float z[kMqQt][8];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < kMqQt; ++qt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[qt][4 * hh + i] = sc[qt][hh][i];
     if (mask) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < kMqQt; ++qt)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (c * kMqChunk + 16 * (e >> 2) + 4 * g + (e & 3) > qpos[qt]) z[qt][e] = -INFINITY;
@@ -289,16 +310,22 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     // largest scaled one, and exp2(scale * s - m) is one FMA and one exp.  A lane first
     // checks its own scores; only when some lane of the wave would move is the maximum over
     // each query's four lanes taken (so the four lanes of a query always agree on m).
-    float lmax[2];
+    float lmax[kMqQt];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < kMqQt; ++qt)
       lmax[qt] = fmaxf(fmaxf(fmaxf(z[qt][0], z[qt][1]), fmaxf(z[qt][2], z[qt][3])),
                        fmaxf(fmaxf(z[qt][4], z[qt][5]), fmaxf(z[qt][6], z[qt][7]))) *
                  scale_log2;
-    float alpha[2] = {1.0f, 1.0f};
-    if (__builtin_amdgcn_ballot_w64(lmax[0] > m[0] + kMqSlack || lmax[1] > m[1] + kMqSlack)) {
+    float alpha[kMqQt];
+    bool move = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < kMqQt; ++qt) {
+      alpha[qt] = 1.0f;
+      move |= lmax[qt] > m[qt] + kMqSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+      for (int qt = 0; qt < kMqQt; ++qt) {
         float cm = fmaxf(lmax[qt], __shfl_xor(lmax[qt], 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
         // m is -inf until the query's first chunk (which holds key 0, seen by every query)
@@ -307,10 +334,15 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
           m[qt] = cm;
         }
       }
-    }
-    u32x4 pf[2], pfl[2];
+      // the accumulators follow the moved reference (alpha = 1 where it did not move)
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < kMqQt; ++qt)
+#pragma unroll
+        for (int t = 0; t < DTILES; ++t) acc[qt][t] *= alpha[qt];
+    }
+    u32x4 pf[kMqQt], pfl[kMqQt];
+#pragma unroll
+    for (int qt = 0; qt < kMqQt; ++qt) {
       float p[8], ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -324,12 +356,6 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       pf[qt] = u32x4{ph[0], ph[1], ph[2], ph[3]};
       pfl[qt] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
-    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int t = 0; t < DTILES; ++t) acc[qt][t] *= alpha[qt];
-    }
     // outputs: V^T fragments through the transposing read
     const uint16_t* vrow = &vs[buf][(4 * g + (r >> 2)) * VROW + 4 * (r & 3)];
 #pragma unroll
@@ -338,7 +364,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       const uint2 hi = lds_read_tr16(vrow + 16 * VROW + 16 * t);
       const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < kMqQt; ++qt) {
         acc[qt][t] = Mma<Ty>::run(a, pf[qt], acc[qt][t]);
         if constexpr (Mma<Ty>::kSplit) acc[qt][t] = Mma<Ty>::run(a, pfl[qt], acc[qt][t]);
       }
@@ -347,7 +373,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
 
   load_ids(0);
   fetch(0);
-  stage(0);
+  stage(0, 0);
   if (nchunks > 1) {
     load_ids(1);
     fetch(1);
@@ -357,7 +383,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunks) {
-      stage(buf ^ 1);  // the other buffer was last read during chunk c - 1
+      stage(buf ^ 1, c + 1);  // the other buffer was last read during chunk c - 1
       if (c + 2 < nchunks) {
         fetch(c + 2);
         if (c + 3 < nchunks) load_ids(c + 3);
@@ -370,9 +396,9 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     __syncthreads();
   }
 
-  const int any_bad = __syncthreads_or(bad);
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kMqQt; ++qt) {
     if (!qt_on[qt]) continue;  // uniform in the wave
     float lt = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
     lt += __shfl_xor(lt, 32, 64);

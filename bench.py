@@ -37,27 +37,29 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode-attn KV GB/s (frac of HBM peak) and seq·layer/s, LLaMA-13B shape"
 HBM_PEAK_GBS = 8000.0
-# rocprofv3 counter summary of the decode kernel on this workload (see its header for the
-# commands); its traffic figure is used only while the kernel sources are unchanged.
+# rocprofv3 counter summaries (see each one's header for the commands); a traffic figure is
+# used only while the kernel sources it was taken on are unchanged.
+CSRC = os.path.join(ROOT, "paged_kv_cache_306_amd", "csrc")
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "decode_llama13b_layer_fp16_counters.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_306_amd", "csrc", f)
-                  for f in ("pkv_decode.hip", "pkv_device.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_decode.hip", "pkv_device.h")]
+MQ_COUNTER_PROFILE = os.path.join(ROOT, "profiles", "multi_query_prefix_hit_fp16_counters.md")
+MQ_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_multi_query.hip", "pkv_device.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Scaled HBM bytes per decode launch from the committed counter profile, or None when
-    there is none or it was taken on different kernel sources."""
+def measured_traffic(profile=COUNTER_PROFILE, sources=None):
+    """Scaled HBM bytes per launch from a committed counter profile, or None when there is
+    none or it was taken on different kernel sources."""
     try:
-        with open(COUNTER_PROFILE) as f:
+        with open(profile) as f:
             lines = f.read().splitlines()
     except OSError:
         return None
@@ -66,12 +68,14 @@ def measured_traffic():
         if ln.startswith("- ") and ": " in ln:
             k, v = ln[2:].split(": ", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
 GROWTH = 64   # tokens a sequence grows before it is replaced
 
 
@@ -494,7 +498,9 @@ def multi_query_bench(args):
                    "head_dim": D, "block_size": BS, "pool_blocks": w.num_blocks},
         "new_tokens_per_s": round(T * args.steps / wall, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": (measured_traffic(MQ_COUNTER_PROFILE, MQ_KERNEL_SOURCES)
+                                 if dt == "f16" else None),
                      "kernel": f"multi_query_kernel<{dt.upper()},{D},{BS}>",
                      "avg_launch_us": round(launch_s * 1e6, 2),
                      "alg_flops_per_launch": flops},

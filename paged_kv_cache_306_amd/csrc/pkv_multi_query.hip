@@ -24,7 +24,8 @@
 //     i % 4 of the 4 x 16-bit piece addressed by lane 4m + i / 4, so lane (r, g) addresses
 //     key row 4g + r / 4 (then 16 + 4g + r / 4) at head-dim column 16 t + 4 (r % 4);
 //   * O^T accumulates in 16 x 16 tiles: lane (r, g) holds output elements d = 16 t + 4 g + i
-//     of query r.
+//     of query r; one more tile, whose V^T rows are all ones, accumulates the softmax
+//     denominator from the same (rounded) probabilities, in every lane of the query.
 // Row padding of the LDS stages (K: 16 bytes, V: 32 bytes) makes both read patterns hit
 // distinct banks.
 #include <hip/hip_runtime.h>
@@ -79,6 +80,7 @@ struct Mma;
 template <>
 struct Mma<F16> {
   static constexpr bool kSplit = false;
+  static constexpr uint32_t kOnes = 0x3C003C00u;  // two fp16 1.0
   static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -93,6 +95,7 @@ struct Mma<F16> {
 template <>
 struct Mma<BF16> {
   static constexpr bool kSplit = true;
+  static constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
   static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -106,10 +109,6 @@ struct Mma<BF16> {
     lo = __builtin_bit_cast(uint32_t, l);
   }
 };
-
-// Zeros that stand in for K/V pieces a workgroup must not read: keys past what it sees and
-// blocks whose id is outside the pool.  One group of pieces of a wave spans 1 KiB.
-__device__ const u32x4 kMqZeros[64] = {};
 
 // Transposing LDS read of four 16-bit elements (see the lane mapping above).
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
@@ -136,7 +135,6 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   constexpr int ROW_BYTES = D * sizeof(T);
   static_assert(sizeof(T) == 2, "16-bit storage only");
   static_assert(BS % GROUP_ROWS == 0, "a wave's piece group lies in one block");
-  static_assert(GROUP_ROWS * ROW_BYTES <= sizeof(kMqZeros), "zero stand-in covers a group");
 
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kMqChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][kMqChunk * VROW];
@@ -203,27 +201,30 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   // Staging.  Piece group i of this wave covers key rows row0 .. row0 + GROUP_ROWS - 1 of a
   // chunk (64 pieces of 16 bytes, lane -> row lane / COLS, column 8 (lane % COLS)); the rows
   // lie in one block, so its id is a scalar and a lane's byte offset inside the group never
-  // changes.  Rows the workgroup does not see and blocks whose id is outside the pool read
-  // zeros instead (a bad id turns the outputs into NaN).
+  // changes.  Rows the workgroup does not see are zeroed at staging; a block id outside the
+  // pool is clamped into it for the read and turns the outputs into NaN.
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
   const uint32_t lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
-  const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros));
-  const gptr_t kpool = uniform_ptr(k_pool);
-  const gptr_t vpool = uniform_ptr(v_pool);
   // Loop-invariant parts of a group's address: chunks are whole multiples of the block size
   // or of a block, so the group's row inside its block never changes.
   static_assert(kMqChunk % BS == 0 || BS % kMqChunk == 0, "chunks align with blocks");
   const uint64_t block_stride = static_cast<uint64_t>(num_heads) * BS * ROW_BYTES;
-  uint64_t grp_off[GROUPS];
+  gptr_t kgrp[GROUPS], vgrp[GROUPS];
   uint32_t grp_row[GROUPS];
 #pragma unroll
   for (int i = 0; i < GROUPS; ++i) {
     grp_row[i] = (i * kMqWaves + wave) * GROUP_ROWS;
-    grp_off[i] = (static_cast<uint64_t>(h) * BS + grp_row[i] % BS) * ROW_BYTES;
+    const uint64_t off = (static_cast<uint64_t>(h) * BS + grp_row[i] % BS) * ROW_BYTES;
+    kgrp[i] = uniform_ptr(k_pool) + off;
+    vgrp[i] = uniform_ptr(v_pool) + off;
   }
   u32x4 st[2 * GROUPS];
   uint32_t bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded early
-  bool bad = false;
+  // Largest block id fetched.  An id outside the pool is clamped into it (the read stays in
+  // bounds) and turns the outputs into NaN at the end.  Groups of the last chunk that reach
+  // past the keys the workgroup sees read the block of its last key (clamped table index).
+  uint32_t max_bid = 0;
+  const uint32_t last_block = static_cast<uint32_t>(num_blocks - 1);
   auto load_ids = [&](int c) {
     const uint32_t last = static_cast<uint32_t>(tile_keys - 1);
 #pragma unroll
@@ -231,27 +232,35 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
   };
   auto fetch = [&](int c) {
+    (void)c;
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
-      const bool ok = bid[i] < static_cast<uint32_t>(num_blocks);
-      bad |= !ok && c * kMqChunk + static_cast<int>(grp_row[i]) < tile_keys;
-      const uint64_t off = static_cast<uint64_t>(bid[i]) * block_stride + grp_off[i];
-      // rows of the group past the keys the workgroup sees still lie inside this block;
-      // staging replaces them with zeros
-      st[i] = load16<false>((ok ? kpool + off : zeros) + lane_off);
-      st[GROUPS + i] = load16<false>((ok ? vpool + off : zeros) + lane_off);
+      max_bid = max(max_bid, bid[i]);
+      const uint64_t off = static_cast<uint64_t>(min(bid[i], last_block)) * block_stride;
+      // rows of the group past the keys the workgroup sees lie inside this block; staging
+      // replaces them with zeros
+      st[i] = load16<false>(kgrp[i] + off + lane_off);
+      st[GROUPS + i] = load16<false>(vgrp[i] + off + lane_off);
     }
   };
   auto stage = [&](int buf, int c) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const bool tail = (c + 1) * kMqChunk > tile_keys;  // uniform
+    const int col = 8 * (lane % COLS);
+    if ((c + 1) * kMqChunk <= tile_keys) {  // every row of the chunk is seen (uniform)
 #pragma unroll
-    for (int i = 0; i < GROUPS; ++i) {
-      const int t = static_cast<int>(grp_row[i] + lane / COLS);
-      const int col = 8 * (lane % COLS);
-      const bool in = !tail || c * kMqChunk + t < tile_keys;
-      *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = in ? st[i] : zero;
-      *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = in ? st[GROUPS + i] : zero;
+      for (int i = 0; i < GROUPS; ++i) {
+        const int t = static_cast<int>(grp_row[i] + lane / COLS);
+        *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = st[i];
+        *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = st[GROUPS + i];
+      }
+    } else {  // the last chunk: rows past the keys the workgroup sees become zeros
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < GROUPS; ++i) {
+        const int t = static_cast<int>(grp_row[i] + lane / COLS);
+        const bool in = c * kMqChunk + t < tile_keys;
+        *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = in ? st[i] : zero;
+        *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = in ? st[GROUPS + i] : zero;
+      }
     }
   };
 
@@ -260,13 +269,17 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   for (int qt = 0; qt < kMqQt; ++qt)
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) acc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[kMqQt], lsum[kMqQt];  // softmax reference (log2 units, equal in a query's lanes) and
-                                // this lane's share of the denominator
+  // Softmax reference (log2 units, equal in a query's four lanes) and the denominator: a
+  // 16 x 16 output tile whose V^T rows are all ones accumulates the sum of exactly the
+  // probabilities that enter the output products, in every lane of the query.
+  float m[kMqQt];
+  f32x4 den[kMqQt];
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
     m[qt] = -INFINITY;
-    lsum[qt] = 0.0f;
+    den[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const u32x4 ones = {Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes};
 
   // One chunk of keys for the query tiles of the wave.  mask: the chunk holds keys that some
   // query of the wave does not see (its own later positions, or keys past the workgroup's);
@@ -336,20 +349,18 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       }
       // the accumulators follow the moved reference (alpha = 1 where it did not move)
 #pragma unroll
-      for (int qt = 0; qt < kMqQt; ++qt)
+      for (int qt = 0; qt < kMqQt; ++qt) {
 #pragma unroll
         for (int t = 0; t < DTILES; ++t) acc[qt][t] *= alpha[qt];
+        den[qt] *= alpha[qt];
+      }
     }
     u32x4 pf[kMqQt], pfl[kMqQt];
 #pragma unroll
     for (int qt = 0; qt < kMqQt; ++qt) {
-      float p[8], ps = 0.0f;
+      float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(z[qt][e], scale_log2, -m[qt]));
-        ps += p[e];
-      }
-      lsum[qt] = fmaf(lsum[qt], alpha[qt], ps);
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[qt][e], scale_log2, -m[qt]));
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
@@ -368,6 +379,11 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
         acc[qt][t] = Mma<Ty>::run(a, pf[qt], acc[qt][t]);
         if constexpr (Mma<Ty>::kSplit) acc[qt][t] = Mma<Ty>::run(a, pfl[qt], acc[qt][t]);
       }
+    }
+#pragma unroll
+    for (int qt = 0; qt < kMqQt; ++qt) {
+      den[qt] = Mma<Ty>::run(ones, pf[qt], den[qt]);
+      if constexpr (Mma<Ty>::kSplit) den[qt] = Mma<Ty>::run(ones, pfl[qt], den[qt]);
     }
   };
 
@@ -396,14 +412,12 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     __syncthreads();
   }
 
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  // every wave reads what the others staged: a bad id seen by any wave spoils them all
+  const int any_bad = __syncthreads_or(max_bid > last_block ? 1 : 0);
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
-    if (!qt_on[qt]) continue;  // uniform in the wave
-    float lt = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (qi[qt] >= n) continue;
-    const float inv = any_bad ? NAN : 1.0f / lt;
+    if (!qt_on[qt] || qi[qt] >= n) continue;
+    const float inv = any_bad ? NAN : 1.0f / den[qt][0];
     T* orow = out + static_cast<size_t>(q0 + qi[qt]) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {

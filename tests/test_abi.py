@@ -232,3 +232,13 @@ def test_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         pkv.paged_attention_decode(q.clone(), q, kp, kp, torch.zeros(1, 1, dtype=torch.int32),
                                    torch.ones(1, dtype=torch.int32), 0.1, 1)
+    bt, cl = torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32)
+    qs = torch.tensor([0, 1], dtype=torch.int32)
+    with pytest.raises(ValueError):      # host tensors
+        pkv.paged_attention_multi_query(q.clone(), q, kp, kp, bt, cl, qs, 0.1, 1, 1)
+    with pytest.raises(ValueError):      # query_start needs num_seqs + 1 entries
+        pkv.paged_attention_multi_query(q.clone(), q, kp, kp, bt, cl, qs[:1], 0.1, 1, 1)
+    with pytest.raises(ValueError):      # out and q shapes differ
+        pkv.paged_attention_multi_query(q[:, :1].clone(), q, kp, kp, bt, cl, qs, 0.1, 1, 1)
+    with pytest.raises(ValueError):
+        pkv.multi_query_schedule([0, 1], [1, 2], 4)   # query_start of the wrong length

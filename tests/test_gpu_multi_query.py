@@ -190,3 +190,78 @@ def test_multi_query_prefix_hit_full_size_sampled(dtype):
                                                     np.array([0, n]), w.scale, dtype, 0, i, h)
                             for i in range(n)])
             check_close(got[qs[s]:qs[s + 1], h], ref, dtype, f"prefix hit s{s} h{h}")
+
+
+def _mq_rows_vs_oracle(q, kp, vp, tables, ctx, qs, scale, dtype, dev, heads, items=None):
+    """Run the kernel on device pools, then compare every row of the given heads with the
+    oracle evaluated on each sequence's blocks read back from the device."""
+    import torch
+    bt = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+    cl = torch.from_numpy(np.ascontiguousarray(ctx, np.int32)).to(dev)
+    qsd = torch.from_numpy(np.ascontiguousarray(qs, np.int32)).to(dev)
+    qd = to_dev(q, dtype, dev)
+    out = torch.full_like(qd, float("nan"))
+    wi = None if items is None else torch.from_numpy(items).to(dev)
+    pkv.paged_attention_multi_query(out, qd, kp, vp, bt, cl, qsd, scale, int(np.diff(qs).max()),
+                                    int(np.max(ctx)), work_items=wi)
+    torch.cuda.synchronize()
+    got = oracle.decode(W.from_torch(out, dtype), dtype)
+    BS = kp.shape[2]
+    for s in range(len(ctx)):
+        n = int(qs[s + 1] - qs[s])
+        nbk = W.nblocks_for(int(ctx[s]), BS)
+        idx = torch.from_numpy(np.asarray(tables[s, :nbk], np.int64)).to(dev)
+        kc = W.from_torch(kp.index_select(0, idx), dtype)
+        vc = W.from_torch(vp.index_select(0, idx), dtype)
+        tab = np.arange(nbk, dtype=np.int32)[None, :]
+        for h in heads:
+            ref = np.stack([oracle.multi_query_unit(q[qs[s]:qs[s + 1]], kc, vc, tab,
+                                                    np.asarray(ctx[s:s + 1]), np.array([0, n]),
+                                                    scale, dtype, 0, i, h) for i in range(n)])
+            check_close(got[qs[s]:qs[s + 1], h], ref, dtype, f"seq {s} head {h}")
+
+
+def test_multi_query_pool_above_4gib():
+    """Blocks whose byte offsets exceed 2^32 (a 4.6 GB pool per K and V): the per-group block
+    offsets are 64-bit."""
+    import torch
+    dev = device()
+    dt, H, D, BS, NB = "f16", 40, 128, 16, 28000        # 28000 * 163840 B = 4.59 GB per pool
+    g = W.rng(4343)
+    ctx = np.array([300, 1100, 64], np.int32)
+    new = np.array([70, 129, 64], np.int32)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    pick = g.permutation(np.arange(NB - 400, NB, dtype=np.int32))   # offsets >= 4.52e9
+    tables = np.full((3, 80), -1, np.int32)
+    k = 0
+    for s, L in enumerate(ctx):
+        nb = W.nblocks_for(int(L), BS)
+        tables[s, :nb] = pick[k:k + nb]
+        k += nb
+    kp = W.device_normal((NB, H, BS, D), dt, 11, dev)
+    vp = W.device_normal((NB, H, BS, D), dt, 12, dev)
+    q = W.normal_values(g, (int(qs[-1]), H, D), dt)
+    _mq_rows_vs_oracle(q, kp, vp, tables, ctx, qs, float(np.float32(1 / np.sqrt(D))), dt, dev,
+                       heads=(0, 39))
+    del kp, vp
+    torch.cuda.empty_cache()
+
+
+def test_multi_query_draft_tokens_after_long_context():
+    """Speculative-decoding shape: 4 draft tokens per sequence after 16-32K cached tokens,
+    bf16 (about a thousand 32-key chunks per workgroup, one wave holding queries)."""
+    dev = device()
+    dt, H, D, BS = "bf16", 8, 128, 16
+    g = W.rng(4444)
+    ctx = W.uniform_lens(g, 3, 16384, 32768)
+    new = np.array([4, 4, 1], np.int32)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    tables, nb = W.permuted_block_tables(g, ctx, BS, pool_factor=1.1)
+    kp = W.device_normal((nb, H, BS, D), dt, 21, dev)
+    vp = W.device_normal((nb, H, BS, D), dt, 22, dev)
+    W.poison_unused_device(kp, tables, ctx, BS)
+    W.poison_unused_device(vp, tables, ctx, BS)
+    q = W.normal_values(g, (int(qs[-1]), H, D), dt)
+    items = pkv.multi_query_schedule(qs, ctx, int(ctx.max()))
+    _mq_rows_vs_oracle(q, kp, vp, tables, ctx, qs, float(np.float32(1 / np.sqrt(D))), dt, dev,
+                       heads=range(H), items=items)

@@ -503,8 +503,10 @@ class LayerIO(ctypes.Structure):
 
 class DecodeStepper:
     """Native decode-step driver (pkv_stepper_* in include/pkv.h): per call, one slot per
-    sequence from the block manager, one packed H2D copy of tables / lengths / slots / pairs,
-    copy_blocks for copy-on-write pairs, then per layer reshape_and_cache and decode."""
+    sequence from the block manager, one prologue kernel that pulls the packed tables /
+    lengths / slots / pairs / work list from pinned host memory (and appends layer 0's new K/V
+    when nothing is copied), copy_blocks for copy-on-write pairs, then per layer
+    reshape_and_cache and decode."""
 
     def __init__(self, alloc: BlockAllocator, k_pools, v_pools, q, k_new, v_new, out,
                  scale: float, max_seqs: int, max_blocks_per_seq: int, max_context_len: int):

@@ -134,7 +134,8 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
  * partition by partition, so the members read their shared blocks at the same time.
  * pkv_paged_attention_decode_scheduled takes those items in device memory (work_items,
  * num_items).  The items must be built from the same lengths as context_lens: a partition
- * left out leaves its output undefined (the kernels still stay inside every buffer).
+ * left out leaves its output undefined (the kernels still stay inside every buffer); an item
+ * naming a sequence or partition outside the call is ignored.
  * flags: 0, or PKV_DECODE_SHARED_KV when sequences of the batch share blocks -- K/V are then
  * read with ordinary (cache-allocating) loads so a block shared by a group is fetched from
  * HBM once, instead of the nontemporal loads used for K/V read by one sequence only.
@@ -169,12 +170,13 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  *                                  t = 0 .. P, K_t, V_t read through block_tables[s]
  * A sequence with n_s = 1 is single-query decode; n_s = 0 contributes no rows.
  *
- *   out, q        device, [T][num_heads][head_dim], dtype, contiguous, 16-byte aligned;
- *                 T = query_start[num_seqs]; out is written, q is read
+ *   out, q        device, [num_tokens][num_heads][head_dim], dtype, contiguous, 16-byte
+ *                 aligned; out is written, q is read
  *   k_pool,v_pool device, pool layout above, 16-byte aligned; read only
  *   block_tables  device, int32 [num_seqs][max_blocks_per_seq]
  *   context_lens  device, int32 [num_seqs]
- *   query_start   device, int32 [num_seqs + 1], nondecreasing from 0
+ *   query_start   device, int32 [num_seqs + 1], nondecreasing from 0 to num_tokens; a
+ *                 sequence whose rows fall outside [0, num_tokens) is skipped (rows untouched)
  *   max_query_len host: at least every n_s (rows of a longer sequence past it stay unwritten)
  *   scale         host; the softmax temperature, finite and > 0
  *   work_items    NULL (one workgroup per (sequence, 64-token tile, head) of max_query_len),
@@ -193,7 +195,7 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  * adjacent (the one reading the most keys first) so they share its K/V in L2.  Returns the
  * number of items, or -1 for bad arguments, capacity too small, a decreasing query_start,
  * num_seqs > 2^20 or more than 2^11 tiles per sequence.  Outputs are bit-identical for any
- * item order.
+ * item order.  A device item naming a sequence or tile outside the call is ignored.
  */
 int32_t pkv_multi_query_tile(void);
 int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
@@ -203,8 +205,8 @@ pkv_status_t pkv_paged_attention_multi_query(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
-    int32_t max_query_len, int32_t max_context_len, float scale, const int32_t* work_items,
-    int32_t num_items, pkv_stream_t stream);
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* work_items, int32_t num_items, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Append new tokens' keys and values to the cache.

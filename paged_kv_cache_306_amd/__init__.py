@@ -62,7 +62,7 @@ _SIGNATURES = {
     "pkv_multi_query_tile": (_i32, []),
     "pkv_multi_query_schedule": (_i32, [_p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_multi_query": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p, _i32,
-                                               _i32, _i32, _f32, _p, _i32, _p]),
+                                               _i32, _i32, _i32, _f32, _p, _i32, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
     "pkv_copy_blocks": (_i32, [_pdesc, _p, _p, _i32, _p, _i32, _p]),
     "pkv_alloc_create": (_p, [_i32, _i32, _p]),
@@ -273,7 +273,7 @@ def paged_attention_multi_query(out, q, k_pool, v_pool, block_tables, context_le
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32),
-        _dev(query_start, "query_start", torch.int32), S, int(max_query_len),
+        _dev(query_start, "query_start", torch.int32), S, int(q.shape[0]), int(max_query_len),
         int(max_context_len), float(scale), work,
         int(work_items.numel()) if work_items is not None else 0, _stream_ptr(stream))
     _check(st, "pkv_paged_attention_multi_query")

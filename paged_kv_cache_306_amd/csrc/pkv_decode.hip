@@ -140,8 +140,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     typename Ty::store_t* __restrict__ out, const typename Ty::store_t* __restrict__ q,
     const typename Ty::store_t* __restrict__ k_pool, const typename Ty::store_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
-    int num_heads, int num_blocks, int max_len, float scale_log2, int part_tokens, int max_parts,
-    const int32_t* __restrict__ work, float* __restrict__ ws_ml, float* __restrict__ ws_o) {
+    int num_seqs, int num_heads, int num_blocks, int max_len, float scale_log2, int part_tokens,
+    int max_parts, const int32_t* __restrict__ work, float* __restrict__ ws_ml,
+    float* __restrict__ ws_o) {
   using C = DecodeCfg<Ty, D, BS>;
   using T = typename Ty::store_t;
   __shared__ int sm_blk[C::kMaxBlocks];
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     const int item = work[j];
     s = item & kItemSeqMask;
     p = item >> kItemPartShift;
+    if (s >= num_seqs || p >= max_parts) return;  // not an item of this call: touch nothing
   } else {
     s = j / max_parts;
     p = j % max_parts;
@@ -387,9 +389,9 @@ static void launch_decode(const DecodeArgs& a) {
     hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
                        a.stream, static_cast<T*>(a.out), static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
-                       a.block_tables, a.max_blocks, a.context_lens, a.num_heads, a.num_blocks,
-                       a.max_len, a.scale_log2, a.part_tokens, a.max_parts, a.work, a.ws_ml,
-                       a.ws_o);
+                       a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.num_heads,
+                       a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts, a.work,
+                       a.ws_ml, a.ws_o);
   if (a.part_tokens > 0) {
     const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
     hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)), dim3(D),

@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
-    const int32_t* __restrict__ work, int tiles_per_seq, int num_heads, int num_blocks,
-    int max_len, float scale_log2) {
+    const int32_t* __restrict__ work, int num_seqs, int num_tokens, int tiles_per_seq,
+    int num_heads, int num_blocks, int max_len, float scale_log2) {
   using T = typename Ty::store_t;
   constexpr int KSTEPS = D / 32;    // k-steps of the score product
   constexpr int DTILES = D / 16;    // 16-row tiles of O^T
@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const int item = work[j];
     s = item & kMqItemSeqMask;
     tile = item >> kMqItemSeqBits;
+    if (s >= num_seqs || tile >= tiles_per_seq) return;  // not an item of this call
   } else {
     s = j / tiles_per_seq;
     tile = j % tiles_per_seq;
@@ -155,6 +156,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const int n = query_start[s + 1] - q0;
   const int first = tile * kMqTileQueries;
   if (first >= n) return;  // tile past this sequence's new tokens (uniform)
+  if (q0 < 0 || q0 > num_tokens - n) return;  // rows outside q / out: touch nothing
   const int nq = min(kMqTileQueries, n - first);
   const int L = min(context_lens[s], max_len);
   const size_t row_stride = static_cast<size_t>(num_heads) * D;
@@ -443,6 +445,8 @@ struct MqArgs {
   const int32_t* query_start;
   const int32_t* work;
   int64_t wgs;
+  int num_seqs;
+  int num_tokens;
   int tiles_per_seq;
   int num_heads;
   int num_blocks;
@@ -459,8 +463,8 @@ static void launch_mq(const MqArgs& a) {
                      dim3(kMqThreads), 0, a.stream, static_cast<T*>(a.out),
                      static_cast<const T*>(a.q), static_cast<const char*>(a.k_pool),
                      static_cast<const char*>(a.v_pool), a.block_tables, a.max_blocks,
-                     a.context_lens, a.query_start, a.work, a.tiles_per_seq, a.num_heads,
-                     a.num_blocks, a.max_len, a.scale_log2);
+                     a.context_lens, a.query_start, a.work, a.num_seqs, a.num_tokens,
+                     a.tiles_per_seq, a.num_heads, a.num_blocks, a.max_len, a.scale_log2);
 }
 
 template <class Ty, int D>
@@ -535,15 +539,15 @@ pkv_status_t pkv_paged_attention_multi_query(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
-    int32_t max_query_len, int32_t max_context_len, float scale, const int32_t* work_items,
-    int32_t num_items, pkv_stream_t stream) {
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* work_items, int32_t num_items, pkv_stream_t stream) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
-  if (num_seqs < 0 || max_query_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
-      !std::isfinite(scale) || !(scale > 0.0f))
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
+      max_blocks_per_seq <= 0 || !std::isfinite(scale) || !(scale > 0.0f))
     return PKV_EINVAL;
-  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return PKV_EINVAL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
@@ -569,6 +573,8 @@ pkv_status_t pkv_paged_attention_multi_query(
   a.context_lens = context_lens;
   a.query_start = query_start;
   a.work = work_items;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
   a.tiles_per_seq = static_cast<int>(tiles);
   a.num_heads = desc->num_heads;
   a.num_blocks = desc->num_blocks;

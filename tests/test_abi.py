@@ -122,12 +122,12 @@ def test_decode_schedule_covers_every_partition_longest_first():
 
 
 def _mq(desc, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, cl=FAKE, qs=FAKE, S=2, maxq=64,
-             maxlen=64, scale=0.1, work=None, nitems=0)
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, cl=FAKE, qs=FAKE, S=2, T=100,
+             maxq=64, maxlen=64, scale=0.1, work=None, nitems=0)
     a.update(kw)
     return pkv.lib().pkv_paged_attention_multi_query(
         ctypes.byref(desc) if desc is not None else None, a["out"], a["q"], a["k"], a["v"],
-        a["bt"], a["mb"], a["cl"], a["qs"], a["S"], a["maxq"], a["maxlen"], a["scale"],
+        a["bt"], a["mb"], a["cl"], a["qs"], a["S"], a["T"], a["maxq"], a["maxlen"], a["scale"],
         a["work"], a["nitems"], None)
 
 
@@ -148,7 +148,9 @@ def test_multi_query_argument_errors():
     assert _mq(_desc(), work=FAKE, nitems=2 * 1 + 1) == pkv.PKV_EINVAL   # 2 seqs x 1 tile
     assert _mq(_desc(), work=FAKE, nitems=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), maxq=64 * 2048 + 1) == pkv.PKV_EUNSUPPORTED     # tiles past 2^11
+    assert _mq(_desc(), T=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), S=0) == pkv.PKV_OK                               # nothing to do
+    assert _mq(_desc(), T=0) == pkv.PKV_OK
     assert _mq(_desc(), maxq=0) == pkv.PKV_OK
 
 

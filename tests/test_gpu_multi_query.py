@@ -265,3 +265,35 @@ def test_multi_query_draft_tokens_after_long_context():
     items = pkv.multi_query_schedule(qs, ctx, int(ctx.max()))
     _mq_rows_vs_oracle(q, kp, vp, tables, ctx, qs, float(np.float32(1 / np.sqrt(D))), dt, dev,
                        heads=range(H), items=items)
+
+
+def test_multi_query_ignores_rows_and_items_outside_the_call():
+    """A sequence whose query_start range runs past the q rows is skipped (its rows stay
+    untouched) and a device work item naming a sequence past num_seqs is ignored; the other
+    sequences are unaffected."""
+    import torch
+    dev = device()
+    pairs = [(100, 10), (40, 5), (300, 5)]
+    q, kp, vp, tables, ctx, qs = make_mq_case(3105, 2, 128, 16, pairs, "f16")
+    T = int(qs[-1])                                  # 20 rows
+    bad_qs = qs.copy()
+    bad_qs[3] = 1000                                 # sequence 2 claims rows 15 .. 999
+    scale = float(np.float32(1 / np.sqrt(128)))
+    items = np.array([0, 7, 5 | (3 << 20)], np.int32)   # 7 and (5, tile 3) name no sequence
+    got = {}
+    for name, wi in (("grid", None), ("items", items)):
+        qd = to_dev(q, "f16", dev)
+        out = torch.full_like(qd, float("nan"))
+        pkv.paged_attention_multi_query(
+            out, qd, to_dev(kp, "f16", dev), to_dev(vp, "f16", dev),
+            torch.from_numpy(tables).to(dev), torch.from_numpy(ctx).to(dev),
+            torch.from_numpy(bad_qs).to(dev), scale, 10, int(ctx.max()),
+            work_items=None if wi is None else torch.from_numpy(wi).to(dev))
+        torch.cuda.synchronize()
+        got[name] = oracle.decode(W.from_torch(out, "f16"), "f16")
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, "f16")
+    for name, g_ in got.items():
+        assert np.isnan(g_[int(qs[2]):T]).all(), "rows of the skipped sequence were written"
+        done = int(qs[2]) if name == "grid" else int(qs[1])   # the list holds only sequence 0
+        check_close(g_[:done], ref[:done], "f16", f"unaffected sequences ({name})")
+        assert np.isnan(g_[done:int(qs[2])]).all()

@@ -108,6 +108,30 @@ def test_scheduled_decode_bit_identical(dtype, D, BS):
     check_close(oracle.decode(plain, dtype), ref, dtype, f"{dtype} D{D} BS{BS}")
 
 
+def test_scheduled_decode_ignores_items_outside_the_call():
+    """Device work items naming a sequence past num_seqs or a partition past the call's
+    partition count are ignored (no read or write for them); the real items give the same
+    bits as the plain grid, in split mode too."""
+    import torch
+    dev = device()
+    lens = [100, 5000, 30]
+    S, H, D, BS, dt = 3, 4, 128, 16, "f16"
+    q, kp, vp, tables, lens = make_case(95, S, H, D, BS, lens, dt)
+    plain = run_decode(q, kp, vp, tables, lens, 0.09, dt, dev)
+    desc = pkv.CacheDesc(kp.shape[0], H, BS, D, 1)
+    assert pkv.decode_partition_tokens(desc, S, int(lens.max())) > 0   # split mode
+    items = pkv.decode_schedule(desc, lens, int(lens.max()))
+    bad = np.array([7, 1 | (5 << 20)], np.int32)     # sequence 7; partition 5 of sequence 1
+    work = np.concatenate([bad[:1], items, bad[1:]]).astype(np.int32)
+    qt = to_dev(q, dt, dev)
+    out = torch.empty_like(qt)
+    pkv.paged_attention_decode(out, qt, to_dev(kp, dt, dev), to_dev(vp, dt, dev),
+                               torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                               0.09, int(lens.max()), work_items=torch.from_numpy(work).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(W.from_torch(out, dt).view(np.uint8), plain.view(np.uint8))
+
+
 def test_placement_invariance_and_determinism():
     """The same logical KV under two physical placements gives bit-identical outputs, and a
     second run gives the same bits."""

@@ -110,6 +110,19 @@ struct Mma<BF16> {
   }
 };
 
+// Stage layout: K and V rows of D halves, unpadded; the 16-byte piece p of row t sits at piece
+// p ^ swz(t), which keeps a row's pieces in the row and spreads the reads over the banks:
+// K reads take rows r = 0..15 at one logical piece (a distinct piece per row), the V reads
+// take 4 rows x 4 columns per 16-lane group (8 distinct pieces x 2 halves).
+template <int D>
+__device__ __forceinline__ int k_swz(int t) {
+  return D == 128 ? (t & 15) : ((t ^ (t >> 3)) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int t) {
+  return D == 128 ? ((2 * (t & 3)) | (((t >> 2) & 1) << 3)) : (2 * (t & 3));
+}
+
 // Transposing LDS read of four 16-bit elements (see the lane mapping above).
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -127,8 +140,6 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   using T = typename Ty::store_t;
   constexpr int KSTEPS = D / 32;    // k-steps of the score product
   constexpr int DTILES = D / 16;    // 16-row tiles of O^T
-  constexpr int KROW = D + 8;       // halves per K row in the stage
-  constexpr int VROW = D + 16;      // halves per V row in the stage
   constexpr int COLS = D / 8;       // 16-byte pieces per K/V row
   constexpr int GROUP_ROWS = 64 / COLS;                      // key rows of one wave's pieces
   constexpr int GROUPS = kMqChunk / GROUP_ROWS / kMqWaves;   // piece groups per wave and chunk
@@ -136,8 +147,8 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   static_assert(sizeof(T) == 2, "16-bit storage only");
   static_assert(BS % GROUP_ROWS == 0, "a wave's piece group lies in one block");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kMqChunk * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kMqChunk * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kMqChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kMqChunk * D];
 
   // Head-fastest order: neighbouring workgroups read the same blocks' other heads.
   const int h = blockIdx.x % num_heads;
@@ -246,13 +257,13 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     }
   };
   auto stage = [&](int buf, int c) {
-    const int col = 8 * (lane % COLS);
+    const int lc = static_cast<int>(lane % COLS);
     if ((c + 1) * kMqChunk <= tile_keys) {  // every row of the chunk is seen (uniform)
 #pragma unroll
       for (int i = 0; i < GROUPS; ++i) {
         const int t = static_cast<int>(grp_row[i] + lane / COLS);
-        *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = st[i];
-        *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = st[GROUPS + i];
+        *reinterpret_cast<u32x4*>(&ks[buf][t * D + 8 * (lc ^ k_swz<D>(t))]) = st[i];
+        *reinterpret_cast<u32x4*>(&vs[buf][t * D + 8 * (lc ^ v_swz<D>(t))]) = st[GROUPS + i];
       }
     } else {  // the last chunk: rows past the keys the workgroup sees become zeros
       const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -260,8 +271,9 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       for (int i = 0; i < GROUPS; ++i) {
         const int t = static_cast<int>(grp_row[i] + lane / COLS);
         const bool in = c * kMqChunk + t < tile_keys;
-        *reinterpret_cast<u32x4*>(&ks[buf][t * KROW + col]) = in ? st[i] : zero;
-        *reinterpret_cast<u32x4*>(&vs[buf][t * VROW + col]) = in ? st[GROUPS + i] : zero;
+        *reinterpret_cast<u32x4*>(&ks[buf][t * D + 8 * (lc ^ k_swz<D>(t))]) = in ? st[i] : zero;
+        *reinterpret_cast<u32x4*>(&vs[buf][t * D + 8 * (lc ^ v_swz<D>(t))]) =
+            in ? st[GROUPS + i] : zero;
       }
     }
   };
@@ -294,8 +306,8 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k)
-        kf[hh][k] =
-            *reinterpret_cast<const u32x4*>(&ks[buf][(16 * hh + r) * KROW + 32 * k + 8 * g]);
+        kf[hh][k] = *reinterpret_cast<const u32x4*>(
+            &ks[buf][(16 * hh + r) * D + 8 * ((4 * k + g) ^ k_swz<D>(16 * hh + r))]);
     f32x4 sc[kMqQt][2];
 #pragma unroll
     for (int qt = 0; qt < kMqQt; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -370,11 +382,16 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       pfl[qt] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
     // outputs: V^T fragments through the transposing read
-    const uint16_t* vrow = &vs[buf][(4 * g + (r >> 2)) * VROW + 4 * (r & 3)];
+    // lane (r, g) reads 4 elements of key row 4g + r / 4 (and 16 more) at head-dim column
+    // 16 t + 4 (r % 4): 16-byte piece 2t + (r / 2) % 2, half r % 2 of it
+    const int vr = 4 * g + (r >> 2);
+    const int vpc = ((r >> 1) & 1) ^ v_swz<D>(vr);       // v_swz(vr + 16) == v_swz(vr)
+    const uint16_t* vrow = &vs[buf][vr * D + 4 * (r & 1)];
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {
-      const uint2 lo = lds_read_tr16(vrow + 16 * t);
-      const uint2 hi = lds_read_tr16(vrow + 16 * VROW + 16 * t);
+      const int off = 8 * ((2 * t) ^ vpc);
+      const uint2 lo = lds_read_tr16(vrow + off);
+      const uint2 hi = lds_read_tr16(vrow + 16 * D + off);
       const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
       for (int qt = 0; qt < kMqQt; ++qt) {
@@ -414,8 +431,13 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     __syncthreads();
   }
 
-  // every wave reads what the others staged: a bad id seen by any wave spoils them all
-  const int any_bad = __syncthreads_or(max_bid > last_block ? 1 : 0);
+  // Every wave reads what the others staged: a bad id seen by any wave spoils them all.  The
+  // K stage is idle after the loop's last barrier; it carries one flag per wave.
+  if (lane == 0) ks[0][wave] = max_bid > last_block ? 1 : 0;
+  __syncthreads();
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < kMqWaves; ++w) any_bad |= ks[0][w] != 0;
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
     if (!qt_on[qt] || qi[qt] >= n) continue;

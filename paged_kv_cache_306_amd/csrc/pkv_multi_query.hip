@@ -123,6 +123,21 @@ __device__ __forceinline__ int v_swz(int t) {
   return D == 128 ? ((2 * (t & 3)) | (((t >> 2) & 1) << 3)) : (2 * (t & 3));
 }
 
+// Zeros that stand in for the K/V rows of the last chunk that the workgroup does not see.
+// One wave's load covers 1 KiB.
+__device__ const u32x4 kMqZeros[64] = {};
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at lds + 16 l
+// (gfx950 global_load_lds_dwordx4; lds must be the same in every lane).
+__device__ __forceinline__ void load16_to_lds(gptr_t src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
+// Wait until this wave's loads (the direct-to-LDS ones included) have landed:
+// s_waitcnt vmcnt(0), leaving the other counters free.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Transposing LDS read of four 16-bit elements (see the lane mapping above).
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -212,26 +227,31 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   }
 
   // Staging.  Piece group i of this wave covers key rows row0 .. row0 + GROUP_ROWS - 1 of a
-  // chunk (64 pieces of 16 bytes, lane -> row lane / COLS, column 8 (lane % COLS)); the rows
-  // lie in one block, so its id is a scalar and a lane's byte offset inside the group never
-  // changes.  Rows the workgroup does not see are zeroed at staging; a block id outside the
-  // pool is clamped into it for the read and turns the outputs into NaN.
+  // chunk, 1 KiB that one direct-to-LDS load of the wave fills: lane l lands at stage row
+  // l / COLS, stage piece l % COLS, which under the stage swizzle holds logical piece
+  // (l % COLS) ^ swz(row), so that is the piece lane l loads.  The rows lie in one block: its
+  // id is a scalar and a lane's byte offset inside the group never changes.  In the last
+  // chunk, rows the workgroup does not see read zeros; a block id outside the pool is
+  // clamped into it for the read and turns the outputs into NaN.
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
-  const uint32_t lane_off = (lane / COLS) * ROW_BYTES + (lane % COLS) * 16;
   // Loop-invariant parts of a group's address: chunks are whole multiples of the block size
   // or of a block, so the group's row inside its block never changes.
   static_assert(kMqChunk % BS == 0 || BS % kMqChunk == 0, "chunks align with blocks");
   const uint64_t block_stride = static_cast<uint64_t>(num_heads) * BS * ROW_BYTES;
+  const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros)) + 16 * lane;
   gptr_t kgrp[GROUPS], vgrp[GROUPS];
-  uint32_t grp_row[GROUPS];
+  uint32_t grp_row[GROUPS], koff[GROUPS], voff[GROUPS];
 #pragma unroll
   for (int i = 0; i < GROUPS; ++i) {
     grp_row[i] = (i * kMqWaves + wave) * GROUP_ROWS;
     const uint64_t off = (static_cast<uint64_t>(h) * BS + grp_row[i] % BS) * ROW_BYTES;
     kgrp[i] = uniform_ptr(k_pool) + off;
     vgrp[i] = uniform_ptr(v_pool) + off;
+    const int t = static_cast<int>(grp_row[i] + lane / COLS);
+    const int lc = static_cast<int>(lane % COLS);
+    koff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ k_swz<D>(t));
+    voff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ v_swz<D>(t));
   }
-  u32x4 st[2 * GROUPS];
   uint32_t bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded early
   // Largest block id fetched.  An id outside the pool is clamped into it (the read stays in
   // bounds) and turns the outputs into NaN at the end.  Groups of the last chunk that reach
@@ -244,37 +264,21 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     for (int i = 0; i < GROUPS; ++i)
       bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
   };
-  auto fetch = [&](int c) {
-    (void)c;
+  // chunk c -> stage buffer buf, asynchronously (complete after wait_loads)
+  auto fetch = [&](int c, int buf) {
+    const bool tail = (c + 1) * kMqChunk > tile_keys;  // uniform
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
       max_bid = max(max_bid, bid[i]);
       const uint64_t off = static_cast<uint64_t>(min(bid[i], last_block)) * block_stride;
-      // rows of the group past the keys the workgroup sees lie inside this block; staging
-      // replaces them with zeros
-      st[i] = load16<false>(kgrp[i] + off + lane_off);
-      st[GROUPS + i] = load16<false>(vgrp[i] + off + lane_off);
-    }
-  };
-  auto stage = [&](int buf, int c) {
-    const int lc = static_cast<int>(lane % COLS);
-    if ((c + 1) * kMqChunk <= tile_keys) {  // every row of the chunk is seen (uniform)
-#pragma unroll
-      for (int i = 0; i < GROUPS; ++i) {
-        const int t = static_cast<int>(grp_row[i] + lane / COLS);
-        *reinterpret_cast<u32x4*>(&ks[buf][t * D + 8 * (lc ^ k_swz<D>(t))]) = st[i];
-        *reinterpret_cast<u32x4*>(&vs[buf][t * D + 8 * (lc ^ v_swz<D>(t))]) = st[GROUPS + i];
+      gptr_t kp = kgrp[i] + off + koff[i];
+      gptr_t vp = vgrp[i] + off + voff[i];
+      if (tail && c * kMqChunk + static_cast<int>(grp_row[i] + lane / COLS) >= tile_keys) {
+        kp = zeros;
+        vp = zeros;
       }
-    } else {  // the last chunk: rows past the keys the workgroup sees become zeros
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < GROUPS; ++i) {
-        const int t = static_cast<int>(grp_row[i] + lane / COLS);
-        const bool in = c * kMqChunk + t < tile_keys;
-        *reinterpret_cast<u32x4*>(&ks[buf][t * D + 8 * (lc ^ k_swz<D>(t))]) = in ? st[i] : zero;
-        *reinterpret_cast<u32x4*>(&vs[buf][t * D + 8 * (lc ^ v_swz<D>(t))]) =
-            in ? st[GROUPS + i] : zero;
-      }
+      load16_to_lds(kp, &ks[buf][grp_row[i] * D]);
+      load16_to_lds(vp, &vs[buf][grp_row[i] * D]);
     }
   };
 
@@ -407,27 +411,21 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   };
 
   load_ids(0);
-  fetch(0);
-  stage(0, 0);
-  if (nchunks > 1) {
-    load_ids(1);
-    fetch(1);
-    if (nchunks > 2) load_ids(2);
-  }
+  fetch(0, 0);
+  if (nchunks > 1) load_ids(1);
+  wait_loads();
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunks) {
-      stage(buf ^ 1, c + 1);  // the other buffer was last read during chunk c - 1
-      if (c + 2 < nchunks) {
-        fetch(c + 2);
-        if (c + 3 < nchunks) load_ids(c + 3);
-      }
+      fetch(c + 1, buf ^ 1);  // the other buffer was last read during chunk c - 1
+      if (c + 2 < nchunks) load_ids(c + 2);
     }
     // a tile past the wave's queries, or one whose queries all come before this chunk, gets
     // only masked scores and adds nothing
     if (wave_on && c * kMqChunk < wave_keys)
       chunk_step(buf, c, (c + 1) * kMqChunk > wave_unmasked);
+    wait_loads();  // chunk c + 1 has landed in this wave's part of the other buffer
     __syncthreads();
   }
 

@@ -47,11 +47,17 @@ MQ_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_multi_query.hip", "pkv
 
 
 def kernel_source_hash(sources=None) -> str:
+    """SHA-256 of the kernel sources' code: comments and whitespace are dropped first, so a
+    change to the comments alone leaves a counter profile valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sources or KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

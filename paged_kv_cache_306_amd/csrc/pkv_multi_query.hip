@@ -10,13 +10,16 @@
 // matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate):
 //   * one workgroup = 64 consecutive new tokens of one (sequence, head), 16 per wave (one
 //     MFMA query tile; the shape is a compile-time choice, see below);
-//   * keys go 32 at a time through a double-buffered LDS stage, K and V rows both as stored
-//     (16-byte writes), with one barrier per chunk and the global loads two chunks ahead;
+//   * keys go 32 at a time through a double-buffered LDS stage, K and V rows loaded straight
+//     from HBM into LDS (global_load_lds_dwordx4), chunk c + 1 landing while chunk c is
+//     computed, one barrier per chunk; the stage rows are XOR-swizzled so that every read
+//     pattern below hits distinct banks;
 //   * scores S^T = K Q^T: K rows are the A operand (16-byte LDS reads), the wave's q rows
 //     (in registers for the whole run) the B operand; lane (r, g) = (lane % 16, lane / 16)
 //     receives the scores of query r against keys 4g .. 4g+3 of each 16-key half;
-//   * softmax runs per query in log2 units with the running max shared by the four lanes of
-//     a query (two cross-row shuffles per chunk); each lane's probabilities are directly the
+//   * softmax runs per query in log2 units against a reference shared by the four lanes of a
+//     query and moved only when a score exceeds it by a margin (the cross-lane max is taken
+//     only then); each lane's probabilities are directly the
 //     B operand of O^T = V^T P^T when slot 8g + j of the contraction is key 4g + j (j < 4)
 //     or key 16 + 4g + j - 4 (j >= 4);
 //   * the V^T operand comes from the row-major V stage through gfx950's transposing LDS read
@@ -26,8 +29,6 @@
 //   * O^T accumulates in 16 x 16 tiles: lane (r, g) holds output elements d = 16 t + 4 g + i
 //     of query r; one more tile, whose V^T rows are all ones, accumulates the softmax
 //     denominator from the same (rounded) probabilities, in every lane of the query.
-// Row padding of the LDS stages (K: 16 bytes, V: 32 bytes) makes both read patterns hit
-// distinct banks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,7 +44,7 @@ namespace pkv {
 namespace {
 
 // Workgroup shape: 4 waves x one 16-query tile each (64 new tokens per workgroup) runs at
-// 120 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
+// 112 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
 // products) halves the LDS bytes per flop but needs ~200 VGPRs and two waves per SIMD; on the
 // prefix-hit workload it was 4-6% slower, with bit-identical outputs.
 #ifndef PKV_MQ_WAVES

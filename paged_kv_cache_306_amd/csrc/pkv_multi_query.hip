@@ -158,13 +158,22 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   constexpr int DTILES = D / 16;    // 16-row tiles of O^T
   constexpr int COLS = D / 8;       // 16-byte pieces per K/V row
   constexpr int GROUP_ROWS = 64 / COLS;                      // key rows of one wave's pieces
-  constexpr int GROUPS = kMqChunk / GROUP_ROWS / kMqWaves;   // piece groups per wave and chunk
+  constexpr int CHUNK_GROUPS = kMqChunk / GROUP_ROWS;         // piece groups per chunk
+  constexpr int GROUPS = (CHUNK_GROUPS + kMqWaves - 1) / kMqWaves;  // ... per wave (at most)
+  constexpr bool ALL_GROUPS = CHUNK_GROUPS % kMqWaves == 0;   // every wave loads GROUPS
   constexpr int ROW_BYTES = D * sizeof(T);
   static_assert(sizeof(T) == 2, "16-bit storage only");
   static_assert(BS % GROUP_ROWS == 0, "a wave's piece group lies in one block");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][kMqChunk * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kMqChunk * D];
+  // The two stage buffers are separate LDS arrays, and the chunk loop below is unrolled by
+  // two so that each chunk's buffers are known at compile time.  Then the compiler can tell
+  // that the reads of chunk c never touch the buffer that chunk c + 1's direct-to-LDS loads
+  // fill, and it issues them without waiting for those loads; with one array indexed by
+  // c & 1 it waits for every outstanding load first, which serialises loading and computing.
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[kMqChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[kMqChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[kMqChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[kMqChunk * D];
 
   // Head-fastest order: neighbouring workgroups read the same blocks' other heads.
   const int h = blockIdx.x % num_heads;
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     koff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ k_swz<D>(t));
     voff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ v_swz<D>(t));
   }
-  uint32_t bid[GROUPS];  // block ids of the groups of the next chunk to fetch, loaded early
+  uint32_t bid[GROUPS] = {};  // block ids of the groups of the next chunk to fetch, loaded early
   // Largest block id fetched.  An id outside the pool is clamped into it (the read stays in
   // bounds) and turns the outputs into NaN at the end.  Groups of the last chunk that reach
   // past the keys the workgroup sees read the block of its last key (clamped table index).
@@ -263,13 +272,15 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const uint32_t last = static_cast<uint32_t>(tile_keys - 1);
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i)
-      bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
+      if (ALL_GROUPS || grp_row[i] < kMqChunk)
+        bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
   };
-  // chunk c -> stage buffer buf, asynchronously (complete after wait_loads)
-  auto fetch = [&](int c, int buf) {
+  // chunk c -> stage buffers (kst, vst), asynchronously (complete after wait_loads)
+  auto fetch = [&](int c, uint16_t* kst, uint16_t* vst) {
     const bool tail = (c + 1) * kMqChunk > tile_keys;  // uniform
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
+      if (!ALL_GROUPS && grp_row[i] >= kMqChunk) continue;  // more waves than groups
       max_bid = max(max_bid, bid[i]);
       const uint64_t off = static_cast<uint64_t>(min(bid[i], last_block)) * block_stride;
       gptr_t kp = kgrp[i] + off + koff[i];
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
         kp = zeros;
         vp = zeros;
       }
-      load16_to_lds(kp, &ks[buf][grp_row[i] * D]);
-      load16_to_lds(vp, &vs[buf][grp_row[i] * D]);
+      load16_to_lds(kp, &kst[grp_row[i] * D]);
+      load16_to_lds(vp, &vst[grp_row[i] * D]);
     }
   };
 
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   // One chunk of keys for the query tiles of the wave.  mask: the chunk holds keys that some
   // query of the wave does not see (its own later positions, or keys past the workgroup's);
   // wave-uniform.
-  auto chunk_step = [&](int buf, int c, bool mask) {
+  auto chunk_step = [&](const uint16_t* kst, const uint16_t* vst, int c, bool mask) {
     // all K fragments of the chunk first, then the products k-step by k-step over the
     // independent accumulators (query tiles x two 16-key halves)
     u32x4 kf[2][KSTEPS];
@@ -312,7 +323,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k)
         kf[hh][k] = *reinterpret_cast<const u32x4*>(
-            &ks[buf][(16 * hh + r) * D + 8 * ((4 * k + g) ^ k_swz<D>(16 * hh + r))]);
+            &kst[(16 * hh + r) * D + 8 * ((4 * k + g) ^ k_swz<D>(16 * hh + r))]);
     f32x4 sc[kMqQt][2];
 #pragma unroll
     for (int qt = 0; qt < kMqQt; ++qt) sc[qt][0] = sc[qt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     // 16 t + 4 (r % 4): 16-byte piece 2t + (r / 2) % 2, half r % 2 of it
     const int vr = 4 * g + (r >> 2);
     const int vpc = ((r >> 1) & 1) ^ v_swz<D>(vr);       // v_swz(vr + 16) == v_swz(vr)
-    const uint16_t* vrow = &vs[buf][vr * D + 4 * (r & 1)];
+    const uint16_t* vrow = &vst[vr * D + 4 * (r & 1)];
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {
       const int off = 8 * ((2 * t) ^ vpc);
@@ -412,31 +423,36 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   };
 
   load_ids(0);
-  fetch(0, 0);
+  fetch(0, ks0, vs0);
   if (nchunks > 1) load_ids(1);
   wait_loads();
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
+  // One chunk: stage chunk c + 1 into (knext, vnext) while chunk c is read from (kcur, vcur).
+  auto step = [&](int c, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knext,
+                  uint16_t* vnext) {
     if (c + 1 < nchunks) {
-      fetch(c + 1, buf ^ 1);  // the other buffer was last read during chunk c - 1
+      fetch(c + 1, knext, vnext);  // the other buffer was last read during chunk c - 1
       if (c + 2 < nchunks) load_ids(c + 2);
     }
     // a tile past the wave's queries, or one whose queries all come before this chunk, gets
     // only masked scores and adds nothing
     if (wave_on && c * kMqChunk < wave_keys)
-      chunk_step(buf, c, (c + 1) * kMqChunk > wave_unmasked);
+      chunk_step(kcur, vcur, c, (c + 1) * kMqChunk > wave_unmasked);
     wait_loads();  // chunk c + 1 has landed in this wave's part of the other buffer
     __syncthreads();
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, ks0, vs0, ks1, vs1);
+    if (c + 1 < nchunks) step(c + 1, ks1, vs1, ks0, vs0);
   }
 
   // Every wave reads what the others staged: a bad id seen by any wave spoils them all.  The
   // K stage is idle after the loop's last barrier; it carries one flag per wave.
-  if (lane == 0) ks[0][wave] = max_bid > last_block ? 1 : 0;
+  if (lane == 0) ks0[wave] = max_bid > last_block ? 1 : 0;
   __syncthreads();
   bool any_bad = false;
 #pragma unroll
-  for (int w = 0; w < kMqWaves; ++w) any_bad |= ks[0][w] != 0;
+  for (int w = 0; w < kMqWaves; ++w) any_bad |= ks0[w] != 0;
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
     if (!qt_on[qt] || qi[qt] >= n) continue;

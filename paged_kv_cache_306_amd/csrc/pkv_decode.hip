@@ -38,7 +38,7 @@
 namespace pkv {
 
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 8
+#define PKV_DECODE_WAVES 4
 #endif
 #ifndef PKV_PART_TOKENS
 #define PKV_PART_TOKENS 2048

@@ -105,6 +105,10 @@ def parse():
                          "workloads: one JSON line per configuration")
     ap.add_argument("--dtype", choices=("f16", "bf16"), default="f16",
                     help="storage type of the prefix_hit workload")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="decode workloads: read a 1 GiB buffer before every timed step (outside "
+                         "the decode launch's events) so the 256 MB MALL holds none of the "
+                         "previous step's K/V; the step time then includes that read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=2560,
                     help="most (sequence, head) units the oracle baseline computes")
@@ -594,10 +598,14 @@ def main():
             z.record()
             arr[2 * l], arr[2 * l + 1] = a.cuda_event, z.cuda_event
         handles.append(arr)
+    flush = (torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+             if args.flush_mall else None)
     torch.cuda.synchronize()
     host = 0.0
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.view(torch.int64).sum()   # reads 1 GiB: evicts the MALL, leaves no dirty lines
         h0 = time.perf_counter()
         b.step(handles[i])
         host += time.perf_counter() - h0
@@ -624,7 +632,8 @@ def main():
         "config": {"workload": f"{args.workload}_{b.dtype}", "description": b.sp["desc"],
                    "seqs": b.S, "heads": b.H, "head_dim": b.D, "block_size": b.BS,
                    "layers": L, "pool_blocks": b.NB, "placement": args.placement,
-                   "growth_tokens_before_replacement": b.growth},
+                   "growth_tokens_before_replacement": b.growth,
+                   "flush_mall_bytes_per_step": (1 << 30) if args.flush_mall else 0},
         "seq_layer_per_s": round(b.S * L * args.steps / wall, 1),
         "host_ms_per_step": round(host / args.steps * 1e3, 4),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

@@ -114,6 +114,9 @@ def parse():
                     help="most (sequence, head) units the oracle baseline computes")
     ap.add_argument("--cpu-bytes", type=float, default=1.6e9,
                     help="most K+V bytes the oracle baseline reads (about 10 s of CPU work)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the achievable HBM read rate (libpkv_probe.so): a "
+                         "contiguous stream and whole 2/4/8 KiB tiles in random order")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     return ap.parse_args()
@@ -130,6 +133,63 @@ def calibrate_copy(mib: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+
+
+def ceiling_bench(args):
+    """Achievable HBM read rate on this GPU for the decode kernel's access patterns: one
+    contiguous stream, and whole tiles visited in a seeded random order (a paged gather reads
+    whole (block, head) tiles: 2, 4 and 8 KiB at fp16, head_dim 128, block size 8, 16, 32),
+    plus the same 4 KiB tiles in address order.  4 GiB buffer, HIP events, median of 20."""
+    import ctypes
+    import torch
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_306_amd",
+                        "libpkv_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+    probe = ctypes.CDLL(path).pkv_probe_read
+    probe.restype = ctypes.c_int32
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                      ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    g = np.random.default_rng(args.seed)
+    wgs = 4096
+    cases = [("stream", 0, 1), ("stream", 0, 0)]
+    cases += [("tiles_random", tb, 1) for tb in (2048, 4096, 8192)]
+    cases += [("tiles_random", 4096, 0), ("tiles_in_order", 4096, 1)]
+    rows = []
+    for pattern, tb, nt in cases:
+        order = None
+        n_tiles = nbytes // tb if tb else 0
+        if tb:
+            idx = np.arange(n_tiles) if pattern == "tiles_in_order" else g.permutation(n_tiles)
+            order = torch.from_numpy(idx.astype(np.int32)).to(dev)
+
+        def launch():
+            st = probe(buf.data_ptr(), nbytes, tb, order.data_ptr() if order is not None else None,
+                       n_tiles, nt, sink.data_ptr(), wgs, stream)
+            if st != 0:
+                raise RuntimeError(f"pkv_probe_read returned {st}")
+        for _ in range(3):
+            launch()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        for a, z in evs:
+            a.record()
+            launch()
+            z.record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(z) for a, z in evs])) / 1e3
+        rows.append({"pattern": pattern, "tile_bytes": tb, "nontemporal": bool(nt),
+                     "us": round(t * 1e6, 1), "GB/s": round(nbytes / t / 1e9, 1),
+                     "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
+        print(json.dumps(rows[-1]), flush=True)
+    print(json.dumps({"ceiling_bytes_per_launch": nbytes, "workgroups": wgs,
+                      "peak_GB/s": HBM_PEAK_GBS, "cases": len(rows)}), flush=True)
 
 
 WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "full_step_40", "prefix_hit")
@@ -562,11 +622,14 @@ def main():
         prefix_cache_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the paged "
+              "attention path here has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.ceiling:
+        ceiling_bench(args)
         return
     if args.sweep:
         sweep(args)

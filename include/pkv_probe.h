@@ -1,0 +1,43 @@
+/* Read-bandwidth probes (libpkv_probe.so) -- a measurement aid, not part of the paged-attention
+ * path.  bench.py --ceiling uses them to measure what HBM delivers on this chip for the two
+ * access patterns that bound the decode kernel: one contiguous stream, and whole fixed-size
+ * tiles visited in a given (random) order, which is how decode gathers K/V through a block
+ * table ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm":
+ * blocks sit anywhere in the pool and are reached through the table).  The figures they give
+ * are the achievable ceilings that decode's bandwidth is compared with, beside the spec peak.
+ */
+#ifndef PKV_PROBE_H
+#define PKV_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Enqueue one read of device memory on `stream` (a hipStream_t; NULL = default stream).
+ *
+ *   buf, bytes      device buffer of `bytes` bytes (16-byte aligned, bytes a multiple of 16);
+ *                   read only.
+ *   tile_bytes      0: read the whole buffer, each workgroup one contiguous span of it;
+ *                   2048, 4096 or 8192: read num_tiles whole tiles of that size, tile i of the
+ *                   visit being the tile at byte offset order[i] * tile_bytes.
+ *   order           device int32 [num_tiles], each entry in [0, bytes / tile_bytes); unused
+ *                   when tile_bytes = 0.  Entries are not checked on the device.
+ *   num_tiles       tiles to visit (0 < num_tiles, num_tiles * tile_bytes <= bytes).
+ *   nontemporal     nonzero: nontemporal loads (the decode kernel's), else ordinary loads.
+ *   sink            device uint32 [1]; written only when a data-dependent hash takes one
+ *                   particular value, which keeps the loads from being removed.
+ *   workgroups      grid size (1 .. 65536), 256 threads each.
+ *
+ * Returns 0 on success, 1 for invalid arguments (nothing enqueued), 2 when the launch fails.
+ */
+int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes, const int32_t* order,
+                       int64_t num_tiles, int32_t nontemporal, uint32_t* sink,
+                       int32_t workgroups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_PROBE_H */

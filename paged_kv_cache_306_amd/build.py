@@ -1,5 +1,6 @@
 """Build libpkv.so in-tree: the HIP kernels for gfx950 (hipcc) plus the host block manager
-(g++, plain C++).  ``python -m paged_kv_cache_306_amd.build`` or ``build()``."""
+(g++, plain C++); and libpkv_probe.so, the read-bandwidth probes bench.py --ceiling uses.
+``python -m paged_kv_cache_306_amd.build`` or ``build()``."""
 from __future__ import annotations
 
 import os
@@ -11,10 +12,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["pkv_decode.hip", "pkv_multi_query.hip", "pkv_cache_ops.hip", "pkv_step.hip"]
 CXX_SOURCES = ["pkv_alloc.cpp"]
+PROBE_SOURCES = ["pkv_probe.hip"]
 # Per-source hipcc flags.  The multi-query kernel keeps its MFMA accumulators in ordinary
 # VGPRs (gfx950 MFMAs take C/D there too): with the accumulation-register form the compiler
 # copies every accumulator between the two register files on each loop iteration.
@@ -47,8 +50,15 @@ def _run(cmd, verbose):
         sys.stderr.write(r.stderr)
 
 
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libpkv.so next to this file; returns its path."""
+    """Compile every source, link libpkv.so and libpkv_probe.so next to this file; returns the
+    path of libpkv.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
     for src in HIP_SOURCES:
@@ -61,9 +71,14 @@ def build(verbose: bool = False) -> str:
         _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
               os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    _link(objs, LIB, verbose)
+    probe_objs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        _run([_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
+        probe_objs.append(obj)
+    _link(probe_objs, PROBE_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,135 @@
+// Read-bandwidth probes for gfx950 (declared in pkv_probe.h): a contiguous stream and a
+// visit of whole fixed-size tiles in a given order, the access pattern of a paged K/V gather.
+// Measurement aids only; nothing on the paged-attention path calls them.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pkv_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kStreamUnroll = 8;        // 16-byte loads in flight per lane, contiguous read
+constexpr int kTileLoadsInFlight = 16;  // 16-byte loads in flight per lane, tile visit
+constexpr uint32_t kNever = 0x9E3779B9u;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+__device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// Contiguous read: workgroup b streams its own span of the buffer (the spans tile it in
+// order), 256 threads x kStreamUnroll consecutive 16-byte vectors (32 KiB) per iteration.
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4* __restrict__ p,
+                                                               int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  constexpr int64_t kStep = static_cast<int64_t>(kThreads) * kStreamUnroll;
+  const int64_t steps = (n16 + kStep - 1) / kStep;
+  const int64_t per_wg = (steps + gridDim.x - 1) / gridDim.x;
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * per_wg * kStep;
+  const int64_t end = begin + per_wg * kStep < n16 ? begin + per_wg * kStep : n16;
+  uint32_t acc = 0;
+  for (int64_t i = begin + threadIdx.x; i < end; i += kStep) {
+    u32x4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * kThreads;
+      v[u] = j < end ? load16<NT>(p + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= fold(v[u]);
+  }
+  if (acc == kNever) sink[0] = acc;
+}
+
+// Whole tiles of VPL x 1 KiB (one wave-wide 16-byte load covers 1 KiB): wave w of the grid
+// visits order[w], order[w + waves], ...; TILES of them are in flight at once, so every lane
+// keeps kTileLoadsInFlight loads outstanding whatever the tile size.
+template <bool NT, int VPL>
+__global__ __launch_bounds__(kThreads) void read_tiles_kernel(const u32x4* __restrict__ p,
+                                                              const int32_t* __restrict__ order,
+                                                              int64_t num_tiles,
+                                                              uint32_t* __restrict__ sink) {
+  constexpr int TILES = kTileLoadsInFlight / VPL;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  const int64_t waves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  uint32_t acc = 0;
+  for (int64_t t0 = wave; t0 < num_tiles; t0 += TILES * waves) {
+    u32x4 v[TILES][VPL];
+#pragma unroll
+    for (int k = 0; k < TILES; ++k) {
+      const int64_t t = t0 + k * waves;
+      const bool on = t < num_tiles;
+      const int64_t base = static_cast<int64_t>(on ? order[t] : 0) * (64 * VPL) + lane;
+#pragma unroll
+      for (int u = 0; u < VPL; ++u)
+        v[k][u] = on ? load16<NT>(p + base + 64 * u) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < TILES; ++k)
+#pragma unroll
+      for (int u = 0; u < VPL; ++u) acc ^= fold(v[k][u]);
+  }
+  if (acc == kNever) sink[0] = acc;
+}
+
+template <bool NT>
+hipError_t launch_tiles(const u32x4* p, const int32_t* order, int64_t num_tiles, int tile_bytes,
+                        uint32_t* sink, int wgs, hipStream_t s) {
+  switch (tile_bytes) {
+    case 2048:
+      hipLaunchKernelGGL((read_tiles_kernel<NT, 2>), dim3(wgs), dim3(kThreads), 0, s, p, order,
+                         num_tiles, sink);
+      break;
+    case 4096:
+      hipLaunchKernelGGL((read_tiles_kernel<NT, 4>), dim3(wgs), dim3(kThreads), 0, s, p, order,
+                         num_tiles, sink);
+      break;
+    default:
+      hipLaunchKernelGGL((read_tiles_kernel<NT, 8>), dim3(wgs), dim3(kThreads), 0, s, p, order,
+                         num_tiles, sink);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes,
+                                  const int32_t* order, int64_t num_tiles, int32_t nontemporal,
+                                  uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % 16 ||
+      reinterpret_cast<uintptr_t>(buf) % 16 || workgroups < 1 || workgroups > 65536)
+    return 1;
+  if (tile_bytes != 0 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
+    return 1;
+  if (tile_bytes != 0 && (!order || num_tiles <= 0 || num_tiles > bytes / tile_bytes))
+    return 1;
+  const u32x4* p = static_cast<const u32x4*>(buf);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e;
+  if (tile_bytes == 0) {
+    if (nontemporal)
+      hipLaunchKernelGGL(read_stream_kernel<true>, dim3(workgroups), dim3(kThreads), 0, s, p,
+                         bytes / 16, sink);
+    else
+      hipLaunchKernelGGL(read_stream_kernel<false>, dim3(workgroups), dim3(kThreads), 0, s, p,
+                         bytes / 16, sink);
+    e = hipGetLastError();
+  } else {
+    e = nontemporal ? launch_tiles<true>(p, order, num_tiles, tile_bytes, sink, workgroups, s)
+                    : launch_tiles<false>(p, order, num_tiles, tile_bytes, sink, workgroups, s);
+  }
+  return e == hipSuccess ? 0 : 2;
+}

@@ -11,8 +11,8 @@ import paged_kv_cache_306_amd as pkv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+def declared_symbols(header="pkv.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
 
@@ -244,3 +244,31 @@ def test_binding_requires_device_tensors():
         pkv.paged_attention_multi_query(q[:, :1].clone(), q, kp, kp, bt, cl, qs, 0.1, 1, 1)
     with pytest.raises(ValueError):
         pkv.multi_query_schedule([0, 1], [1, 2], 4)   # query_start of the wrong length
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libpkv_probe.so (bench.py --ceiling) exports what include/pkv_probe.h declares and
+    returns 1 for invalid arguments before touching the GPU."""
+    path = os.path.join(ROOT, "paged_kv_cache_306_amd", "libpkv_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libpkv_probe.so is not built")
+    lib = ctypes.CDLL(path)
+    names = declared_symbols("pkv_probe.h")
+    assert names == ["pkv_probe_read"]
+    for n in names:
+        assert hasattr(lib, n), n
+    f = lib.pkv_probe_read
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p]
+    p, sink, order = 1 << 20, 1 << 21, 1 << 22        # never dereferenced: rejected first
+    ok = dict(buf=p, bytes=1 << 20, tile=4096, order=order, tiles=256, nt=1, sink=sink, wgs=64)
+    bad = [dict(buf=None), dict(sink=None), dict(bytes=0), dict(bytes=100), dict(buf=p + 8),
+           dict(wgs=0), dict(wgs=65537), dict(tile=1024), dict(tile=3000), dict(order=None),
+           dict(tiles=0), dict(tiles=257)]
+    for change in bad:
+        a = {**ok, **change}
+        st = f(a["buf"], a["bytes"], a["tile"], a["order"], a["tiles"], a["nt"], a["sink"],
+               a["wgs"], None)
+        assert st == 1, change

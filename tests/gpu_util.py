@@ -26,6 +26,23 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(ax)) - 7)
 
 
+# mantissa bits and smallest normal exponent of each output type
+_FORMAT = {"f32": (23, -126), "f16": (10, -14), "bf16": (7, -126)}
+
+
+def ulp(x, dtype):
+    """Spacing of the output type's numbers at |x| (x float64); subnormal spacing below the
+    smallest normal."""
+    bits, emin = _FORMAT[dtype]
+    ax = np.maximum(np.abs(x), 2.0 ** emin)
+    return np.exp2(np.floor(np.log2(ax)) - bits)
+
+
+# (what, dtype, elements, max abs error, max error in output ulps) of every check_close in the
+# session; tests/conftest.py prints them at the end of the run.
+REPORT = []
+
+
 def check_close(got64, ref64, dtype, what=""):
     """|got - ref| <= the stated bound: 1e-5 (f32) or 2e-3 (f16 / bf16).  Where a bfloat16
     output's own spacing exceeds 2e-3 (|ref| >= 0.5) the bound is one bfloat16 ulp, since
@@ -38,6 +55,8 @@ def check_close(got64, ref64, dtype, what=""):
     if dtype == "bf16":
         bound = np.maximum(bound, bf16_ulp(ref64))
     worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    REPORT.append((what, dtype, int(err.size), float(err.max()),
+                   float((err / ulp(ref64, dtype)).max())))
     assert (err <= bound).all(), (
         f"{what}: max err {err.max():.3g} at {worst} (got {got64[worst]}, ref {ref64[worst]})")
     return float(err.max())

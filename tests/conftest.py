@@ -13,19 +13,20 @@ def pytest_configure(config):
 
 
 def pytest_terminal_summary(terminalreporter):
-    """Parity errors of the GPU tests, absolute and in ulps of the output type."""
-    mod = sys.modules.get("gpu_util") or sys.modules.get("tests.gpu_util")
+    """Parity errors of the GPU tests vs the float64 oracle, per test and output type:
+    elements compared, max absolute error, max error in ulps of the output type."""
+    mod = sys.modules.get("gpu_util")
     rows = getattr(mod, "REPORT", None) if mod else None
     if not rows:
         return
+    agg = {}
+    for test, dtype, n, err, ulps in rows:
+        a = agg.setdefault((test, dtype), [0, 0.0, 0.0])
+        a[0] += n
+        a[1], a[2] = max(a[1], err), max(a[2], ulps)
     tr = terminalreporter
     tr.section("parity errors vs the float64 oracle")
-    tr.write_line(f"{'check':60s} {'dtype':5s} {'elements':>10s} {'max abs':>10s} {'max ulp':>8s}")
-    for what, dtype, n, err, ulps in rows:
-        tr.write_line(f"{(what or '-')[:60]:60s} {dtype:5s} {n:10d} {err:10.3g} {ulps:8.2f}")
-    worst = {}
-    for what, dtype, n, err, ulps in rows:
-        w = worst.setdefault(dtype, [0.0, 0.0])
-        w[0], w[1] = max(w[0], err), max(w[1], ulps)
-    for dtype, (err, ulps) in sorted(worst.items()):
-        tr.write_line(f"worst {dtype}: max abs {err:.3g}, {ulps:.2f} ulp of the output type")
+    tr.write_line(f"{'test':64s} {'dtype':5s} {'elements':>10s} {'max abs':>9s} {'max ulp':>8s}")
+    for (test, dtype), (n, err, ulps) in agg.items():
+        name = test.split("::", 1)[-1]
+        tr.write_line(f"{name[:64]:64s} {dtype:5s} {n:10d} {err:9.3g} {ulps:8.1f}")

@@ -31,6 +31,8 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <cmath>
 #include <vector>
@@ -375,6 +377,8 @@ struct DecodeArgs {
   float* ws_ml;
   float* ws_o;
   hipStream_t stream;
+  hipEvent_t ev_start;  // optional: takes the start of the launch (hipExtLaunchKernel)
+  hipEvent_t ev_stop;   // optional: takes its end (the reduce kernel's, in split mode)
 };
 
 template <class Ty, int D, int BS>
@@ -385,19 +389,47 @@ static void launch_decode(const DecodeArgs& a) {
   const int64_t wgs = items * a.num_heads;
   auto kernel = a.shared_kv ? decode_partition_kernel<Ty, D, BS, false>
                             : decode_partition_kernel<Ty, D, BS, true>;
-  if (wgs > 0)
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
-                       a.stream, static_cast<T*>(a.out), static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
-                       a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.num_heads,
-                       a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts, a.work,
-                       a.ws_ml, a.ws_o);
-  if (a.part_tokens > 0) {
-    const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
-    hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)), dim3(D),
-                       0, a.stream, static_cast<T*>(a.out), a.context_lens, a.num_heads, a.max_len,
-                       a.part_tokens, a.max_parts, a.ws_ml, a.ws_o);
+  const bool reduce = a.part_tokens > 0;
+  // Timing events ride on the launches themselves (the dispatch records its own start and end
+  // time), so no event packet sits between kernels; with nothing launched they are recorded
+  // on the stream instead.
+  hipEvent_t start = a.ev_start, stop = a.ev_stop;
+  if (wgs > 0) {
+    hipEvent_t stop_here = reduce ? nullptr : stop;
+    if (start || stop_here)
+      hipExtLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
+                            a.stream, start, stop_here, 0u, static_cast<T*>(a.out),
+                            static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
+                            static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks,
+                            a.context_lens, a.num_seqs, a.num_heads, a.num_blocks, a.max_len,
+                            a.scale_log2, a.part_tokens, a.max_parts, a.work, a.ws_ml, a.ws_o);
+    else
+      hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
+                         a.stream, static_cast<T*>(a.out), static_cast<const T*>(a.q),
+                         static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
+                         a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.num_heads,
+                         a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts,
+                         a.work, a.ws_ml, a.ws_o);
+    start = nullptr;
+    if (!reduce) stop = nullptr;
+  } else if (start) {
+    (void)hipEventRecord(start, a.stream);
+    start = nullptr;
   }
+  if (reduce) {
+    const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+    if (stop)
+      hipExtLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)),
+                            dim3(D), 0, a.stream, nullptr, stop, 0u, static_cast<T*>(a.out),
+                            a.context_lens, a.num_heads, a.max_len, a.part_tokens, a.max_parts,
+                            a.ws_ml, a.ws_o);
+    else
+      hipLaunchKernelGGL((decode_reduce_kernel<Ty, D>), dim3(static_cast<unsigned>(units)),
+                         dim3(D), 0, a.stream, static_cast<T*>(a.out), a.context_lens,
+                         a.num_heads, a.max_len, a.part_tokens, a.max_parts, a.ws_ml, a.ws_o);
+    stop = nullptr;
+  }
+  if (stop) (void)hipEventRecord(stop, a.stream);
 }
 
 template <class Ty, int D>
@@ -425,7 +457,8 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
                                 const int32_t* context_lens, int32_t num_seqs,
                                 int32_t max_context_len, float scale, const int32_t* work,
                                 int32_t num_items, uint32_t flags, void* workspace,
-                                size_t workspace_bytes, pkv_stream_t stream) {
+                                size_t workspace_bytes, pkv_stream_t stream,
+                                void* ev_start = nullptr, void* ev_stop = nullptr) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale) ||
@@ -473,6 +506,8 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
   a.num_items = num_items;
   a.shared_kv = (flags & PKV_DECODE_SHARED_KV) != 0;
   a.stream = static_cast<hipStream_t>(stream);
+  a.ev_start = static_cast<hipEvent_t>(ev_start);
+  a.ev_stop = static_cast<hipEvent_t>(ev_stop);
 
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
   switch (desc->dtype) {
@@ -483,6 +518,20 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
   }
   if (st != PKV_OK) return st;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t max_context_len, float scale,
+                                    const int32_t* work_items, int32_t num_items, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, pkv_stream_t stream,
+                                    void* ev_start, void* ev_stop) {
+  if (!work_items) return PKV_EINVAL;
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, work_items, num_items, flags, workspace,
+                     workspace_bytes, stream, ev_start, ev_stop);
 }
 
 }  // namespace pkv

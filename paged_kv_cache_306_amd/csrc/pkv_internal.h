@@ -32,4 +32,15 @@ inline pkv_status_t check_desc(const pkv_cache_desc_t* d) {
   return PKV_OK;
 }
 
+// pkv_paged_attention_decode_scheduled with optional timing: ev_start / ev_stop (hipEvent_t,
+// created with timing, or null) take the start and end time of the attention launch itself.
+pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                    const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t max_context_len, float scale,
+                                    const int32_t* work_items, int32_t num_items, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, pkv_stream_t stream,
+                                    void* ev_start, void* ev_stop);
+
 }  // namespace pkv

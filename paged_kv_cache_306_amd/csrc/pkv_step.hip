@@ -83,7 +83,7 @@ size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_ite
 
 // Two stages are used alternately.  Stage k owns a pinned host area and a device area of
 // d_index.  The prologue of step i reads the host area of its stage; the host refills that
-// area at step i+2 only after the event recorded behind that prologue has fired.  The device
+// area at step i+2 only after the event recorded behind step i's last launch has fired.  The device
 // area is rewritten at step i+2 by a kernel on the same stream, so step i's readers are done.
 struct pkv_stepper {
   pkv_alloc_t* alloc = nullptr;
@@ -96,7 +96,7 @@ struct pkv_stepper {
     int32_t* host = nullptr;        // pinned: tables | lens | slots | pairs | items
     const char* host_dev = nullptr; // the same memory as the device sees it
     char* dev = nullptr;            // device area of the same size inside d_index
-    hipEvent_t read = nullptr;      // recorded behind the prologue that read `host`
+    hipEvent_t read = nullptr;      // recorded behind the step whose prologue read `host`
     bool pending = false;
   } stage[2];
   int cur = 0;
@@ -238,9 +238,15 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       fuse_append ? static_cast<pkv::u32x4*>(io->v_pools[0]) : nullptr, total_vecs, row_vecs,
       st->desc.num_heads, st->desc.block_size,
       static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size);
-  if (hipGetLastError() != hipSuccess || hipEventRecord(sg.read, hs) != hipSuccess)
-    return PKV_EHIP;
-  sg.pending = true;
+  if (hipGetLastError() != hipSuccess) return PKV_EHIP;
+  // The marker that frees this staging area goes behind the step's last launch rather than
+  // right behind the prologue: an event between two kernels leaves the GPU idle for a few
+  // microseconds, and the host waits on it only two steps later.
+  auto mark_read = [&](pkv_status_t r) {
+    if (hipEventRecord(sg.read, hs) != hipSuccess && r == PKV_OK) r = PKV_EHIP;
+    sg.pending = true;
+    return r;
+  };
 
   const int32_t* d_tables = reinterpret_cast<const int32_t*>(sg.dev);
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;
@@ -250,27 +256,23 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
 
   if (*num_cow > 0 && L > 0) {
     s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
-    if (s != PKV_OK) return s;
+    if (s != PKV_OK) return mark_read(s);
   }
   for (int32_t l = 0; l < L; ++l) {
     if (!(l == 0 && fuse_append)) {
       s = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l], io->k_pools[l],
                                 io->v_pools[l], d_slots, n, stream);
-      if (s != PKV_OK) return s;
+      if (s != PKV_OK) return mark_read(s);
     }
-    if (attn_events &&
-        hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l]), hs) != hipSuccess)
-      return PKV_EHIP;
-    s = pkv_paged_attention_decode_scheduled(&st->desc, io->out[l], io->q[l], io->k_pools[l],
-                                             io->v_pools[l], d_tables, MB, d_lens, n, *max_len,
-                                             io->scale, d_items, num_items, decode_flags,
-                                             workspace, workspace_bytes, stream);
-    if (s != PKV_OK) return s;
-    if (attn_events &&
-        hipEventRecord(static_cast<hipEvent_t>(attn_events[2 * l + 1]), hs) != hipSuccess)
-      return PKV_EHIP;
+    // timing, when asked for, comes from the attention launch itself
+    s = pkv::decode_scheduled_timed(&st->desc, io->out[l], io->q[l], io->k_pools[l],
+                                    io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
+                                    d_items, num_items, decode_flags, workspace, workspace_bytes,
+                                    stream, attn_events ? attn_events[2 * l] : nullptr,
+                                    attn_events ? attn_events[2 * l + 1] : nullptr);
+    if (s != PKV_OK) return mark_read(s);
   }
-  return PKV_OK;
+  return mark_read(PKV_OK);
 }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {

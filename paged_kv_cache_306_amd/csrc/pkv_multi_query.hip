@@ -44,9 +44,10 @@ namespace pkv {
 namespace {
 
 // Workgroup shape: 4 waves x one 16-query tile each (64 new tokens per workgroup) runs at
-// 112 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
-// products) halves the LDS bytes per flop but needs ~200 VGPRs and two waves per SIMD; on the
-// prefix-hit workload it was 4-6% slower, with bit-identical outputs.
+// 122 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
+// products) halves the LDS bytes per flop but needs 184 VGPRs and two waves per SIMD; on the
+// prefix-hit workload it tied at fp16 and was 6% slower at bf16, and 8 waves of one tile were
+// no faster, all with bit-identical outputs.
 #ifndef PKV_MQ_WAVES
 #define PKV_MQ_WAVES 4
 #endif

@@ -230,7 +230,8 @@ pkv_status_t pkv_reshape_and_cache(const pkv_cache_desc_t* desc, const void* k, 
 /* ---------------------------------------------------------------------------------------
  * Copy whole blocks, in every layer, for copy-on-write of shared prefix blocks.
  * ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" ->
- * "KV-Cache Sharing (Copy-on-Write)": blocks stay shared until a write, like fork().)
+ * "KV-Cache Sharing (Copy-on-Write)": blocks stay shared until a write, as the memory pages
+ * of a forked process do.)
  *
  * For every layer l < num_layers and pair p < num_pairs with (src, dst) = (pairs[2p],
  * pairs[2p+1]):  k_pools[l][dst] = k_pools[l][src] and v_pools[l][dst] = v_pools[l][src]

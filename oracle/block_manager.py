@@ -3,20 +3,20 @@
 Model of the host-side KV block allocator, written from the pages:
   * "PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm",
     steps 1-4: a request's first block is allocated when it starts; tokens fill the block;
-    when the block is full the next one is allocated wherever there is space; a page table
+    when the block is full the next one is taken from any free place in the pool; a page table
     records logical block -> physical block.
   * same page, "Memory Efficiency": blocks are allocated on demand, so the only waste is the
     unused tail of each sequence's last block (100 tokens -> 7 blocks of 16 -> 112 slots,
     12 unused).
   * same page, "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)": sequences that share
-    a prefix share its blocks; only divergent tokens get new blocks; like fork(), pages stay
-    shared until someone writes to them.
+    a prefix share its blocks; only divergent tokens get new blocks; as with the pages of a
+    forked Unix process, a block stays shared until one of its holders writes to it.
   * "Efficient Memory Management for Large Language Model Serving with PagedAttention",
     observer card, "Key ideas": prefix blocks are shared across sequences of one prompt
     (parallel sampling, beam search) via copy-on-write.
 
 Readings where the pages are silent:
-  * "wherever there's space" is a free list whose initial order is an input (tests pass a
+  * "any free place" is a free list whose initial order is an input (tests pass a
     seeded random permutation); a freed block goes back on top of the list and is handed out
     next (last in, first out); a freed sequence returns its blocks so that its logical block
     0 is on top;

@@ -6,8 +6,9 @@ the slot the block manager gave it.  A slot number is physical_block * block_siz
 a negative slot means "no write" (reading).
 
 copy_blocks: copy-on-write of a shared block ("PagedAttention: Efficient LLM Serving with
-vLLM", "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)": shared pages until a write,
-like fork()) -- the destination block receives the source block's bytes, in every layer.
+vLLM", "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)": blocks stay shared until a
+holder writes, as the pages of a forked process do) -- the destination block receives the
+source block's bytes, in every layer.
 
 Both work on integer views of the storage so that every bit, NaN payloads included, is copied
 unchanged; the result is compared bit for bit.

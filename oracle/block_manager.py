@@ -9,7 +9,7 @@ Model of the host-side KV block allocator, written from the pages:
     unused tail of each sequence's last block (100 tokens -> 7 blocks of 16 -> 112 slots,
     12 unused).
   * same page, "Advanced Features" -> "KV-Cache Sharing (Copy-on-Write)": sequences that share
-    a prefix share its blocks; only divergent tokens get new blocks; as with the pages of a
+    a prefix share its blocks; tokens past the point where they differ go to new blocks; as with the pages of a
     forked Unix process, a block stays shared until one of its holders writes to it.
   * "Efficient Memory Management for Large Language Model Serving with PagedAttention",
     observer card, "Key ideas": prefix blocks are shared across sequences of one prompt

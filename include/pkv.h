@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = 1,        /* a null pointer, a negative or inconsistent size, an unknown id */
-  PKV_EUNSUPPORTED = 2,  /* a shape or dtype this build has no kernel for */
+  PKV_EUNSUPPORTED = 2,  /* a shape or dtype the library has no kernel for */
   PKV_ENOMEM = 3,        /* block pool exhausted (allocator) or workspace too small */
   PKV_EHIP = 4           /* the HIP runtime reported an error at launch */
 } pkv_status_t;

@@ -18,7 +18,7 @@ inline int dtype_bytes(int32_t dtype) {
   return 0;
 }
 
-// Shape checks common to every device call: positive sizes, and a shape this build has
+// Shape checks common to every device call: positive sizes, and a shape the library has
 // kernels for (head_dim 64 or 128, block_size 8, 16 or 32, dtype f32 / f16 / bf16).
 // Slot numbers (block * block_size + offset) must fit in int32.
 inline pkv_status_t check_desc(const pkv_cache_desc_t* d) {

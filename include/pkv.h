@@ -179,7 +179,7 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  *                 sequence whose rows fall outside [0, num_tokens) is skipped (rows untouched)
  *   max_query_len host: at least every n_s (rows of a longer sequence past it stay unwritten)
  *   scale         host; the softmax temperature, finite and > 0
- *   work_items    NULL (one workgroup per (sequence, 64-token tile, head) of max_query_len),
+ *   work_items    NULL (one workgroup per (sequence, tile of pkv_multi_query_tile() tokens, head) of max_query_len),
  *                 or device items from pkv_multi_query_schedule (num_items of them)
  * Storage types f16 and bf16 only (the products run on 16-bit matrix-core instructions):
  * PKV_EUNSUPPORTED for f32.  Scores and outputs accumulate in fp32; the probabilities enter

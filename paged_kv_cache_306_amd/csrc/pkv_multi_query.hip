@@ -8,12 +8,12 @@
 //
 // With many queries per sequence this is a dense contraction, so both products run on the
 // matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate):
-//   * one workgroup = 64 consecutive new tokens of one (sequence, head), 16 per wave (one
+//   * one workgroup = 128 consecutive new tokens of one (sequence, head), 16 per wave (one
 //     MFMA query tile; the shape is a compile-time choice, see below);
-//   * keys go 32 at a time through a double-buffered LDS stage, K and V rows loaded straight
-//     from HBM into LDS (global_load_lds_dwordx4), chunk c + 1 landing while chunk c is
-//     computed, one barrier per chunk; the stage rows are XOR-swizzled so that every read
-//     pattern below hits distinct banks;
+//   * keys go 64 at a time through a double-buffered LDS stage, K and V rows loaded straight
+//     from HBM into LDS (global_load_lds_dwordx4), stage c + 1 landing while stage c is
+//     computed as two 32-key steps, one barrier per stage; the stage rows are XOR-swizzled
+//     so that every read pattern below hits distinct banks;
 //   * scores S^T = K Q^T: K rows are the A operand (16-byte LDS reads), the wave's q rows
 //     (in registers for the whole run) the B operand; lane (r, g) = (lane % 16, lane / 16)
 //     receives the scores of query r against keys 4g .. 4g+3 of each 16-key half;
@@ -43,13 +43,15 @@
 namespace pkv {
 namespace {
 
-// Workgroup shape: 4 waves x one 16-query tile each (64 new tokens per workgroup) runs at
-// 122 VGPRs, four waves per SIMD.  Two tiles per wave (each K/V fragment feeding two
-// products) halves the LDS bytes per flop but needs 184 VGPRs and two waves per SIMD; on the
-// prefix-hit workload it tied at fp16 and was 6% slower at bf16, and 8 waves of one tile were
-// no faster, all with bit-identical outputs.
+// Workgroup shape: 8 waves x one 16-query tile each (128 new tokens per workgroup) with a
+// 64-key stage (64 KiB of LDS) runs at 118 VGPRs: two workgroups and four waves per SIMD
+// share each CU.  Against 4 waves with a 32-key stage (64 tokens, 32 KiB) it halves the K/V
+// reads per query and the barriers per key; on the prefix-hit workload, side by side, 4%
+// faster at fp16 and 1.5% at bf16 (each change alone was not faster).  Two tiles per wave
+// (each K/V fragment feeding two products) halves the LDS bytes per flop but needs 184 VGPRs
+// and two waves per SIMD; it tied or lost.  All shapes give bit-identical outputs.
 #ifndef PKV_MQ_WAVES
-#define PKV_MQ_WAVES 4
+#define PKV_MQ_WAVES 8
 #endif
 #ifndef PKV_MQ_WAVE_TILES
 #define PKV_MQ_WAVE_TILES 1
@@ -59,7 +61,12 @@ constexpr int kMqQt = PKV_MQ_WAVE_TILES;        // 16-query MFMA tiles per wave
 constexpr int kMqThreads = 64 * kMqWaves;
 constexpr int kMqWaveQueries = 16 * kMqQt;
 constexpr int kMqTileQueries = kMqWaves * kMqWaveQueries;   // new tokens per workgroup
-constexpr int kMqChunk = 32;                                // keys staged in LDS per step
+constexpr int kMqChunk = 32;                                // keys per compute step
+#ifndef PKV_MQ_SUB
+#define PKV_MQ_SUB 2
+#endif
+constexpr int kMqSub = PKV_MQ_SUB;                          // compute steps per LDS stage
+constexpr int kMqStage = kMqChunk * kMqSub;                 // keys staged per barrier
 constexpr float kMqSlack = 8.0f;  // log2 units a score may exceed the softmax reference by
 constexpr int kMqItemSeqBits = 20;                          // work item = sequence | tile << 20
 constexpr int kMqItemSeqMask = (1 << kMqItemSeqBits) - 1;
@@ -159,22 +166,22 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   constexpr int DTILES = D / 16;    // 16-row tiles of O^T
   constexpr int COLS = D / 8;       // 16-byte pieces per K/V row
   constexpr int GROUP_ROWS = 64 / COLS;                      // key rows of one wave's pieces
-  constexpr int CHUNK_GROUPS = kMqChunk / GROUP_ROWS;         // piece groups per chunk
+  constexpr int CHUNK_GROUPS = kMqStage / GROUP_ROWS;         // piece groups per stage
   constexpr int GROUPS = (CHUNK_GROUPS + kMqWaves - 1) / kMqWaves;  // ... per wave (at most)
   constexpr bool ALL_GROUPS = CHUNK_GROUPS % kMqWaves == 0;   // every wave loads GROUPS
   constexpr int ROW_BYTES = D * sizeof(T);
   static_assert(sizeof(T) == 2, "16-bit storage only");
   static_assert(BS % GROUP_ROWS == 0, "a wave's piece group lies in one block");
 
-  // The two stage buffers are separate LDS arrays, and the chunk loop below is unrolled by
-  // two so that each chunk's buffers are known at compile time.  Then the compiler can tell
-  // that the reads of chunk c never touch the buffer that chunk c + 1's direct-to-LDS loads
+  // The two stage buffers are separate LDS arrays, and the stage loop below is unrolled by
+  // two so that each stage's buffers are known at compile time.  Then the compiler can tell
+  // that the reads of stage c never touch the buffer that stage c + 1's direct-to-LDS loads
   // fill, and it issues them without waiting for those loads; with one array indexed by
   // c & 1 it waits for every outstanding load first, which serialises loading and computing.
-  __shared__ __attribute__((aligned(16))) uint16_t ks0[kMqChunk * D];
-  __shared__ __attribute__((aligned(16))) uint16_t ks1[kMqChunk * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs0[kMqChunk * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vs1[kMqChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[kMqStage * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[kMqStage * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[kMqStage * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs1[kMqStage * D];
 
   // Head-fastest order: neighbouring workgroups read the same blocks' other heads.
   const int h = blockIdx.x % num_heads;
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const int tile_keys = L - n + first + nq;                       // keys the workgroup sees
   const int wave_keys = L - n + min(wave_first + kMqWaveQueries, n);  // ... the wave sees
   const int wave_unmasked = L - n + wave_first + 1;  // keys every query of the wave sees
-  const int nchunks = (tile_keys + kMqChunk - 1) / kMqChunk;
+  const int nstages = (tile_keys + kMqStage - 1) / kMqStage;   // stages
   // Per 16-query MFMA tile: whether it holds a new token, this lane's query and the last
   // key that query sees (rows past n compute a copy of the last one).
   bool qt_on[kMqQt];
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
   // Loop-invariant parts of a group's address: chunks are whole multiples of the block size
   // or of a block, so the group's row inside its block never changes.
-  static_assert(kMqChunk % BS == 0 || BS % kMqChunk == 0, "chunks align with blocks");
+  static_assert(kMqStage % BS == 0 || BS % kMqStage == 0, "stages align with blocks");
   const uint64_t block_stride = static_cast<uint64_t>(num_heads) * BS * ROW_BYTES;
   const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros)) + 16 * lane;
   gptr_t kgrp[GROUPS], vgrp[GROUPS];
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const uint64_t off = (static_cast<uint64_t>(h) * BS + grp_row[i] % BS) * ROW_BYTES;
     kgrp[i] = uniform_ptr(k_pool) + off;
     vgrp[i] = uniform_ptr(v_pool) + off;
-    const int t = static_cast<int>(grp_row[i] + lane / COLS);
+    const int t = static_cast<int>(grp_row[i] + lane / COLS) % kMqChunk;
     const int lc = static_cast<int>(lane % COLS);
     koff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ k_swz<D>(t));
     voff[i] = (lane / COLS) * ROW_BYTES + 16 * (lc ^ v_swz<D>(t));
@@ -273,20 +280,20 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     const uint32_t last = static_cast<uint32_t>(tile_keys - 1);
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i)
-      if (ALL_GROUPS || grp_row[i] < kMqChunk)
-        bid[i] = table[min(static_cast<uint32_t>(c * kMqChunk) + grp_row[i], last) / BS];
+      if (ALL_GROUPS || grp_row[i] < kMqStage)
+        bid[i] = table[min(static_cast<uint32_t>(c * kMqStage) + grp_row[i], last) / BS];
   };
-  // chunk c -> stage buffers (kst, vst), asynchronously (complete after wait_loads)
+  // stage c -> stage buffers (kst, vst), asynchronously (complete after wait_loads)
   auto fetch = [&](int c, uint16_t* kst, uint16_t* vst) {
-    const bool tail = (c + 1) * kMqChunk > tile_keys;  // uniform
+    const bool tail = (c + 1) * kMqStage > tile_keys;  // uniform
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
-      if (!ALL_GROUPS && grp_row[i] >= kMqChunk) continue;  // more waves than groups
+      if (!ALL_GROUPS && grp_row[i] >= kMqStage) continue;  // more waves than groups
       max_bid = max(max_bid, bid[i]);
       const uint64_t off = static_cast<uint64_t>(min(bid[i], last_block)) * block_stride;
       gptr_t kp = kgrp[i] + off + koff[i];
       gptr_t vp = vgrp[i] + off + voff[i];
-      if (tail && c * kMqChunk + static_cast<int>(grp_row[i] + lane / COLS) >= tile_keys) {
+      if (tail && c * kMqStage + static_cast<int>(grp_row[i] + lane / COLS) >= tile_keys) {
         kp = zeros;
         vp = zeros;
       }
@@ -425,26 +432,31 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
 
   load_ids(0);
   fetch(0, ks0, vs0);
-  if (nchunks > 1) load_ids(1);
+  if (nstages > 1) load_ids(1);
   wait_loads();
   __syncthreads();
-  // One chunk: stage chunk c + 1 into (knext, vnext) while chunk c is read from (kcur, vcur).
+  // One stage: load stage c + 1 into (knext, vnext) while stage c is read from (kcur, vcur).
   auto step = [&](int c, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knext,
                   uint16_t* vnext) {
-    if (c + 1 < nchunks) {
-      fetch(c + 1, knext, vnext);  // the other buffer was last read during chunk c - 1
-      if (c + 2 < nchunks) load_ids(c + 2);
+    if (c + 1 < nstages) {
+      fetch(c + 1, knext, vnext);  // the other buffer was last read during stage c - 1
+      if (c + 2 < nstages) load_ids(c + 2);
     }
-    // a tile past the wave's queries, or one whose queries all come before this chunk, gets
+    // a tile past the wave's queries, or one whose queries all come before this step, gets
     // only masked scores and adds nothing
-    if (wave_on && c * kMqChunk < wave_keys)
-      chunk_step(kcur, vcur, c, (c + 1) * kMqChunk > wave_unmasked);
-    wait_loads();  // chunk c + 1 has landed in this wave's part of the other buffer
+#pragma unroll
+    for (int u = 0; u < kMqSub; ++u) {
+      const int cc = c * kMqSub + u;   // 32-key compute step
+      if (wave_on && cc * kMqChunk < wave_keys)
+        chunk_step(kcur + u * kMqChunk * D, vcur + u * kMqChunk * D, cc,
+                   (cc + 1) * kMqChunk > wave_unmasked);
+    }
+    wait_loads();  // stage c + 1 has landed in this wave's part of the other buffer
     __syncthreads();
   };
-  for (int c = 0; c < nchunks; c += 2) {
+  for (int c = 0; c < nstages; c += 2) {
     step(c, ks0, vs0, ks1, vs1);
-    if (c + 1 < nchunks) step(c + 1, ks1, vs1, ks0, vs0);
+    if (c + 1 < nstages) step(c + 1, ks1, vs1, ks0, vs0);
   }
 
   // Every wave reads what the others staged: a bad id seen by any wave spoils them all.  The

@@ -147,7 +147,7 @@ def test_multi_query_argument_errors():
     assert _mq(_desc(), scale=0.0) == pkv.PKV_EINVAL
     assert _mq(_desc(), work=FAKE, nitems=2 * 1 + 1) == pkv.PKV_EINVAL   # 2 seqs x 1 tile
     assert _mq(_desc(), work=FAKE, nitems=-1) == pkv.PKV_EINVAL
-    assert _mq(_desc(), maxq=64 * 2048 + 1) == pkv.PKV_EUNSUPPORTED     # tiles past 2^11
+    assert _mq(_desc(), maxq=pkv.multi_query_tile() * 2048 + 1) == pkv.PKV_EUNSUPPORTED  # > 2^11 tiles
     assert _mq(_desc(), T=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), S=0) == pkv.PKV_OK                               # nothing to do
     assert _mq(_desc(), T=0) == pkv.PKV_OK
@@ -157,27 +157,31 @@ def test_multi_query_argument_errors():
 def test_multi_query_schedule_covers_every_tile_by_sequence():
     import numpy as np
     tile = pkv.multi_query_tile()
-    assert tile == 64
-    n = np.array([3, 0, 200, 64, 65, 1], np.int64)
-    ctx = np.array([1000, 50, 200, 5000, 65, 1], np.int32)
+    assert tile in (64, 128)
+    n = np.array([3, 0, 2 * tile + 72, tile, tile + 1, 1], np.int64)
+    ctx = np.array([1000, 50, 2 * tile + 72, 5000, tile + 1, 1], np.int32)
     qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
     items = pkv.multi_query_schedule(qs, ctx, 6000)
     seqs, tiles = (items & ((1 << 20) - 1)).tolist(), (items >> 20).tolist()
-    want = [(s, t) for s in range(len(n)) for t in range(-(-int(n[s]) // tile))]
+    ntiles = [-(-int(x) // tile) for x in n]
+    want = [(s, t) for s in range(len(n)) for t in range(ntiles[s])]
     assert sorted(zip(seqs, tiles)) == sorted(want)
-    # sequences by the keys their last token sees (5000, 1000, 200, 65, 1); tiles adjacent,
-    # the tile whose last token sees the most keys first
-    assert seqs == [3, 0, 2, 2, 2, 2, 4, 4, 5]
-    assert tiles[2:6] == [3, 2, 1, 0] and tiles[6:8] == [1, 0]
-    # max_context_len clamps the key counts: sequence 3 drops to 200 keys, after sequence 2
-    items2 = pkv.multi_query_schedule(qs, ctx, 200)
-    assert (items2 & ((1 << 20) - 1)).tolist()[:2] == [0, 2]
+    # sequences by the keys their last token sees (5000, 1000, 2 tile + 72, tile + 1, 1);
+    # a sequence's tiles adjacent, the tile whose last token sees the most keys first
+    order = [3, 0, 2, 4, 5]
+    assert list(zip(seqs, tiles)) == [(s, t) for s in order for t in reversed(range(ntiles[s]))]
+    # max_context_len clamps the key counts: sequences 0 and 3 drop to sequence 2's count,
+    # and equal counts go by sequence index
+    items2 = pkv.multi_query_schedule(qs, ctx, 2 * tile + 72)
+    assert (items2 & ((1 << 20) - 1)).tolist() == [s for s in (0, 2, 3, 4, 5) for _ in range(ntiles[s])]
     lib = pkv.lib()
     buf = np.zeros(16, np.int32)
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     bad_qs = np.array([0, 5, 3], np.int32)                        # decreasing
     assert lib.pkv_multi_query_schedule(ptr(bad_qs), ptr(ctx), 2, 100, ptr(buf), 16) == -1
-    assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 6, 6000, ptr(buf), 8) == -1   # 9 items
+    k = len(want)
+    assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 6, 6000, ptr(buf), k - 1) == -1
+    assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 6, 6000, ptr(buf), k) == k
     assert lib.pkv_multi_query_schedule(None, ptr(ctx), 6, 6000, ptr(buf), 16) == -1
     assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 0, 6000, ptr(buf), 0) == 0
 

@@ -24,9 +24,10 @@ from gpu_util import check_close, device, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# (context length, new tokens) per sequence
+# (context length, new tokens) per sequence: runs of exactly one, one plus one and several
+# workgroup tiles for a 64- and for a 128-token tile, and the other shapes above
 RAGGED = [(1, 1), (2, 1), (17, 17), (100, 37), (300, 64), (301, 65), (530, 130), (40, 0),
-          (1000, 3), (64, 64), (129, 1), (257, 200)]
+          (1000, 3), (64, 64), (129, 1), (257, 200), (130, 128), (140, 129), (300, 260)]
 
 
 def make_mq_case(seed, H, D, BS, pairs, dtype, pool_factor=1.3):

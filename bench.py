@@ -192,7 +192,8 @@ def ceiling_bench(args):
                       "peak_GB/s": HBM_PEAK_GBS, "cases": len(rows)}), flush=True)
 
 
-WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "full_step_40", "prefix_hit")
+WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "fork_step", "full_step_40",
+             "prefix_hit")
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16 matrix peak
 
 
@@ -220,6 +221,20 @@ def workload_spec(name: str, seed: int, block_size: int, placement: str):
         spec = dict(S=w.S, H=w.H, D=w.D, BS=w.BS, dtype=w.dtype, scale=w.scale, layers=1,
                     lens=w.lens.astype(np.int64), NB=NB, growth=64, groups=32, prefix=512,
                     desc="32 groups x 8 seqs sharing a 512-token prefix, tails U[0,256], fp16")
+    elif name == "fork_step":
+        # every step re-forks each group: member 0 takes the group's prompt of 512 + r_g tokens
+        # (r_g uniform in [1, 15], so the last prompt block is shared and partly filled), the
+        # other 7 fork from it, and the step's append copies that block for 7 of the 8
+        g = W.rng(seed * 31 + 3)
+        r = W.uniform_lens(g, 32, 1, 15)
+        prompts = (512 + r).astype(np.int64)
+        lens = np.repeat(prompts, 8)
+        NB = 2 * 32 * (W.nblocks_for(512 + 15, 16) + 8)
+        spec = dict(S=256, H=40, D=128, BS=16, dtype="f16",
+                    scale=float(np.float32(1 / math.sqrt(128))), layers=1, lens=lens, NB=NB,
+                    growth=1, groups=32, refork=True, prompts=prompts,
+                    desc="32 groups x 8 seqs forked from a prompt of 512 + U[1,15] tokens every "
+                         "step: 224 copy-on-write block copies, then the append and decode, fp16")
     elif name == "full_step_40":
         lens, nb, _ = W.full_step(seed=5)
         spec = dict(S=len(lens), H=40, D=128, BS=16, dtype="f16",
@@ -257,7 +272,10 @@ class DecodeBatch:
         self.seq_ids = np.arange(self.S, dtype=np.int64)
         self.next_id = self.S
         self.roots = []
-        if sp["groups"]:
+        if sp.get("refork"):
+            for gi in range(sp["groups"]):
+                self._fork_group(gi)
+        elif sp["groups"]:
             per = self.S // sp["groups"]
             for gi in range(sp["groups"]):
                 root = 1_000_000 + gi
@@ -285,9 +303,21 @@ class DecodeBatch:
         self.stepper = pkv.DecodeStepper(self.alloc, tensors["kp"], tensors["vp"], tensors["q"],
                                          tensors["kn"], tensors["vn"], tensors["out"],
                                          self.scale, self.S, self.MB, self.max_ctx)
+        self.cow_pairs = []      # copy-on-write block copies per step
         self.kv_bytes = []       # logical K+V bytes read by attention, per step (all layers)
         self.alg_bytes = []      # algorithmic bytes of one attention launch, per step
         self.last = None
+
+    def _fork_group(self, gi):
+        """Group gi afresh: member 0 holds the group's prompt, the other members fork it."""
+        per = self.S // self.sp["groups"]
+        first = gi * per
+        for s in range(first, first + per):
+            self.seq_ids[s] = self.next_id
+            self.next_id += 1
+        self.alloc.add_seq(int(self.seq_ids[first]), int(self.sp["prompts"][gi]))
+        for s in range(first + 1, first + per):
+            self.alloc.fork(int(self.seq_ids[first]), int(self.seq_ids[s]))
 
     def _fork_member(self, s, sid):
         """Member s of its group: a fork of the group's prefix root plus its own tail."""
@@ -298,7 +328,16 @@ class DecodeBatch:
             self.alloc.append_slots(np.full(tail, sid, np.int64))
 
     def recycle(self):
-        """Replace sequences that grew `growth` tokens by fresh ones of their start length."""
+        """Replace sequences that grew `growth` tokens by fresh ones of their start length
+        (the fork step replaces every group after each step)."""
+        if self.sp.get("refork"):
+            if (self.cur_len > self.init_lens).any():
+                for sid in self.seq_ids:
+                    self.alloc.free_seq(int(sid))
+                for gi in range(self.sp["groups"]):
+                    self._fork_group(gi)
+                self.cur_len = self.init_lens.copy()
+            return
         done = np.nonzero(self.cur_len - self.init_lens >= self.growth)[0]
         for s in done:
             self.alloc.free_seq(int(self.seq_ids[s]))
@@ -313,6 +352,7 @@ class DecodeBatch:
     def step(self, events=None):
         self.recycle()
         max_len, ncow = self.stepper.step(self.seq_ids, events)
+        self.cow_pairs.append(ncow)
         self.cur_len += 1
         self.last = (max_len, ncow)
         tot = int(self.cur_len.sum())
@@ -713,6 +753,7 @@ def main():
                    "growth_tokens_before_replacement": b.growth,
                    "flush_mall_bytes_per_step": (1 << 30) if args.flush_mall else 0},
         "seq_layer_per_s": round(b.S * L * args.steps / wall, 1),
+        "cow_pairs_per_step": round(float(np.mean(b.cow_pairs[-args.steps:])), 2),
         "host_ms_per_step": round(host / args.steps * 1e3, 4),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

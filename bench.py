@@ -497,6 +497,26 @@ def swap_bench(args, layers: int = 8, tokens: int = 16384):
             t = float(np.median(times))
             res[f"swap_{name}_ms"] = round(t * 1e3, 3)
             res[f"swap_{name}_GBs"] = round(nbytes / t / 1e9, 2)
+        # the same swap-out done block by block (one async copy per K or V block of layer 0):
+        # the per-transfer cost that one batched launch avoids
+        lb = 2 * n * H * bs * D * 2
+        srcs, dsts = out_pairs[:, 0].tolist(), out_pairs[:, 1].tolist()
+
+        def per_block():
+            for sb, db in zip(srcs, dsts):
+                hk[0][db].copy_(dk[0][sb], non_blocking=True)
+                hv[0][db].copy_(dv[0][sb], non_blocking=True)
+        per_block()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        per_block()
+        z.record()
+        torch.cuda.synchronize()
+        res["per_block_copies_out"] = 2 * n
+        res["per_block_copy_out_GBs"] = round(lb / (a.elapsed_time(z) / 1e3) / 1e9, 2)
+        res["per_block_copy_out_wall_GBs"] = round(lb / (time.perf_counter() - t0) / 1e9, 2)
         # one contiguous copy of the same size each way (the PCIe reference)
         flat_d = torch.empty(nbytes // 2, dtype=torch.float16, device=dev)
         flat_h = torch.empty(nbytes // 2, dtype=torch.float16).pin_memory()

@@ -93,6 +93,30 @@ def test_multi_query_schedule_is_bit_identical_to_the_grid():
     assert np.array_equal(plain.view(np.uint16), shuf.view(np.uint16))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multi_query_long_whole_prompts(dtype):
+    """Whole prompts (n = L) of 1500 and 700 tokens: 12 and 6 workgroup tiles per head, the
+    causal diagonal crossing every tile; sampled rows (the first and last 130 of each
+    sequence and every 17th) against the oracle, the rest must be finite."""
+    dev = device()
+    pairs = [(1500, 1500), (700, 700), (3, 3)]
+    H, D, BS = 2, 128, 16
+    q, kp, vp, tables, ctx, qs = make_mq_case(3107 + (dtype == "bf16"), H, D, BS, pairs, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    got = oracle.decode(run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev), dtype)
+    assert np.isfinite(got).all()
+    units, rows = [], []
+    for s_, (L, n) in enumerate(pairs):
+        pick = sorted(set(range(min(130, n))) | set(range(max(0, n - 130), n)) |
+                      set(range(0, n, 17)))
+        for i in pick:
+            rows.append(int(qs[s_]) + i)
+            units += [(s_, i, h) for h in range(H)]
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, dtype,
+                                             units=units)
+    check_close(got[rows], ref[rows], dtype, f"long whole prompts {dtype}")
+
+
 def test_multi_query_single_tokens_are_decode():
     """One new token per sequence: the same outputs as the oracle's decode."""
     dev = device()

@@ -39,6 +39,10 @@
 
 namespace pkv {
 
+// Compile-time tuning knobs; the defaults measured best on MI355X: waves per workgroup (4:
+// three workgroups per CU at 167 VGPRs), tokens per partition of a long sequence, the longest
+// sequence attended in one pass, K bytes per wave per chunk, and the two-deep load pipeline
+// (0 gives the plain loop, kept for comparison).
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4
 #endif

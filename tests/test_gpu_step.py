@@ -216,3 +216,61 @@ def test_full_40_layer_decode_step():
                 check_close(oracle.decode(got[s, h], dt), ref, dt, f"layer {l} seq {s} head {h}")
     del kpt, vpt
     torch.cuda.empty_cache()
+
+
+def test_step_timing_events_are_taken_by_the_launch():
+    """With timing events the step driver lets the attention launch record them (its own start
+    and end, the merge kernel's end in split mode): every layer's pair holds a positive
+    duration, and the outputs are bit-identical to a step without events."""
+    import ctypes
+    import torch
+    dev = device()
+    H, D, BS, dt, layers = 4, 128, 16, "f16", 2
+    NB = 500
+    g = W.rng(321)
+    order = g.permutation(NB)
+    prompts = [(0, 5000), (1, 37), (2, 0)]             # 5001 tokens: split into partitions
+    seqs = np.array([0, 1, 2], np.int64)
+    S = len(seqs)
+    kps = [W.normal_values(g, (NB, H, BS, D), dt) for _ in range(layers)]
+    vps = [W.normal_values(g, (NB, H, BS, D), dt) for _ in range(layers)]
+    qs = [W.normal_values(g, (S, H, D), dt) for _ in range(layers)]
+    kn = [W.normal_values(g, (S, H, D), dt) for _ in range(layers)]
+    vn = [W.normal_values(g, (S, H, D), dt) for _ in range(layers)]
+    MB = 320
+    outs = {}
+    for timed in (False, True):
+        a, m = _setup((NB, order), prompts, [], BS)
+        T = lambda arrs: [to_dev(x, dt, dev) for x in arrs]
+        kpt, vpt, qt, knt, vnt = T(kps), T(vps), T(qs), T(kn), T(vn)
+        out = [torch.empty_like(x) for x in qt]
+        st = pkv.DecodeStepper(a, kpt, vpt, qt, knt, vnt, out, 0.09, S, MB, 5120)
+        evs = arr = None
+        if timed:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(layers)]
+            arr = (ctypes.c_void_p * (2 * layers))()
+            for l, (e0, e1) in enumerate(evs):
+                e0.record()                               # creates the HIP events
+                e1.record()
+                arr[2 * l], arr[2 * l + 1] = e0.cuda_event, e1.cuda_event
+            torch.cuda.synchronize()
+        max_len, ncow = st.step(seqs, arr)
+        torch.cuda.synchronize()
+        assert max_len == 5001 and ncow == 0
+        assert pkv.decode_partition_tokens(st.desc, S, max_len) > 0       # split mode
+        outs[timed] = [W.from_torch(o, dt).view(np.uint16).copy() for o in out]
+        if timed:
+            for l, (e0, e1) in enumerate(evs):
+                assert e0.elapsed_time(e1) > 0, f"layer {l}"
+            mslots, _, _ = m.append_slots(seqs.tolist())
+            ek, ev = oracle.reshape_and_cache(kn[1], vn[1], kps[1], vps[1], np.array(mslots))
+            tables = np.full((S, MB), -1, np.int32)
+            for i, s in enumerate(seqs):
+                row = m.block_table(int(s))
+                tables[i, :len(row)] = row
+            lens = np.array([m.seq_len(int(s)) for s in seqs], np.int32)
+            ref = oracle.paged_attention_decode(qs[1], ek, ev, tables, lens, 0.09, dt)
+            check_close(oracle.decode(W.from_torch(out[1], dt), dt), ref, dt, "timed step")
+    for l in range(layers):
+        assert np.array_equal(outs[False][l], outs[True][l])

@@ -384,7 +384,8 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * device address of the packed index data of the last step.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t (created with timing): event
  * 2l takes the start and event 2l+1 the end of layer l's attention launch, recorded by the
- * launch itself (hipExtLaunchKernel) so that no event packet sits between kernels.
+ * launch itself (hipExtLaunchKernel) so that no event packet sits between kernels; a step with
+ * n = 0 records them back to back on `stream`.
  * ---------------------------------------------------------------------------------------*/
 typedef struct pkv_stepper pkv_stepper_t;
 

@@ -163,7 +163,15 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   *max_len = 0;
   *num_cow = 0;
   *num_done = 0;
-  if (n == 0) return PKV_OK;
+  if (n == 0) {
+    // nothing to attend: timing events, if any, are recorded back to back (zero duration)
+    if (attn_events)
+      for (int64_t e = 0; e < 2 * static_cast<int64_t>(io->num_layers); ++e)
+        if (attn_events[e] && hipEventRecord(static_cast<hipEvent_t>(attn_events[e]),
+                                              static_cast<hipStream_t>(stream)) != hipSuccess)
+          return PKV_EHIP;
+    return PKV_OK;
+  }
   const int32_t L = io->num_layers;
   if (L > 0 && (!io->k_pools || !io->v_pools || !io->q || !io->k_new || !io->v_new || !io->out))
     return PKV_EINVAL;

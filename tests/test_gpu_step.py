@@ -272,5 +272,10 @@ def test_step_timing_events_are_taken_by_the_launch():
             lens = np.array([m.seq_len(int(s)) for s in seqs], np.int32)
             ref = oracle.paged_attention_decode(qs[1], ek, ev, tables, lens, 0.09, dt)
             check_close(oracle.decode(W.from_torch(out[1], dt), dt), ref, dt, "timed step")
+            # a step with no sequences still leaves the events recorded (zero duration)
+            assert st.step(np.zeros(0, np.int64), arr) == (0, 0)
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                assert e0.elapsed_time(e1) >= 0
     for l in range(layers):
         assert np.array_equal(outs[False][l], outs[True][l])

@@ -550,8 +550,9 @@ class DecodeStepper:
 
     def step(self, seqs, events=None, stream=None):
         """One decode step for the sequences in ``seqs`` (C-contiguous int64 numpy).
-        ``events``: optional ctypes array of 2 * num_layers hipEvent_t handles.
-        Returns (max_len, num_cow)."""
+        ``events``: optional ctypes array of 2 * num_layers hipEvent_t handles (created with
+        timing); the attention launch of layer l records its start into event 2l and its end
+        into event 2l+1.  Returns (max_len, num_cow)."""
         n = int(seqs.shape[0])
         st = _lib().pkv_stepper_step(self._h, seqs.ctypes.data_as(ctypes.c_void_p), n,
                                      ctypes.byref(self.io), self.workspace.data_ptr(),

@@ -179,16 +179,18 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  *                 sequence whose rows fall outside [0, num_tokens) is skipped (rows untouched)
  *   max_query_len host: at least every n_s (rows of a longer sequence past it stay unwritten)
  *   scale         host; the softmax temperature, finite and > 0
- *   work_items    NULL (one workgroup per (sequence, tile of pkv_multi_query_tile() tokens, head) of max_query_len),
- *                 or device items from pkv_multi_query_schedule (num_items of them)
+ *   work_items    NULL (one workgroup per sequence, head and tile of pkv_multi_query_tile()
+ *                 new tokens up to max_query_len), or device items from
+ *                 pkv_multi_query_schedule (num_items of them)
  * Storage types f16 and bf16 only (the products run on 16-bit matrix-core instructions):
  * PKV_EUNSUPPORTED for f32.  Scores and outputs accumulate in fp32; the probabilities enter
- * the second product as fp16 (f16), or as a bf16 pair hi + lo (bf16).  A block id outside [0, num_blocks) among a
- * tile's keys is never dereferenced: that tile's outputs are NaN; so are the rows of a
- * sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned pointers, negative
+ * the second product as fp16 (f16), or as a bf16 pair hi + lo (bf16).  A block id outside
+ * [0, num_blocks) among a tile's keys is never dereferenced: that tile's outputs are NaN; so
+ * are the rows of a sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned pointers, negative
  * sizes, a scale that is not finite and positive, bad num_items), PKV_EUNSUPPORTED, PKV_EHIP
  * or PKV_OK.
  *
+ * pkv_multi_query_tile(): new tokens per workgroup tile (128: 8 waves of 16).
  * pkv_multi_query_schedule (host only): one item per (sequence s, tile of
  * pkv_multi_query_tile() new tokens) from host copies of query_start and context_lens,
  * encoded s | tile << 20; sequences that read the most keys first, a sequence's tiles

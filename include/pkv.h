@@ -186,9 +186,9 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  * PKV_EUNSUPPORTED for f32.  Scores and outputs accumulate in fp32; the probabilities enter
  * the second product as fp16 (f16), or as a bf16 pair hi + lo (bf16).  A block id outside
  * [0, num_blocks) among a tile's keys is never dereferenced: that tile's outputs are NaN; so
- * are the rows of a sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned pointers, negative
- * sizes, a scale that is not finite and positive, bad num_items), PKV_EUNSUPPORTED, PKV_EHIP
- * or PKV_OK.
+ * are the rows of a sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned
+ * pointers, negative sizes, a scale that is not finite and positive, bad num_items),
+ * PKV_EUNSUPPORTED, PKV_EHIP or PKV_OK.
  *
  * pkv_multi_query_tile(): new tokens per workgroup tile (128: 8 waves of 16).
  * pkv_multi_query_schedule (host only): one item per (sequence s, tile of

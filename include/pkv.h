@@ -381,8 +381,9 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *
  * The stepper allocates only pinned host memory and HIP events of its own; the caller owns the
  * device buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned: two areas used by
- * alternate steps) and the workspace.  The host refills a staging area only after the step
- * whose prologue read it (two steps earlier) has run.  pkv_stepper_last_index returns the
+ * alternate steps) and the workspace.  The host refills a staging area only after the
+ * prologue that read it (two steps earlier) has finished; that launch records its own
+ * completion marker, so no event packet sits between kernels.  pkv_stepper_last_index returns the
  * device address of the packed index data of the last step.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t (created with timing): event
  * 2l takes the start and event 2l+1 the end of layer l's attention launch, recorded by the

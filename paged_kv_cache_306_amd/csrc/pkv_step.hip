@@ -8,6 +8,7 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -236,9 +237,14 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   (void)hipGetLastError();
   const int32_t* slots_host_dev =
       reinterpret_cast<const int32_t*>(sg.host_dev) + static_cast<size_t>(n) * MB + n;
-  hipLaunchKernelGGL(
+  // The marker that frees this staging area is the prologue launch's own completion (the
+  // launch records sg.read when the kernel ends): the prologue is the only reader of the
+  // area, and an event recorded on the stream between two kernels would leave the GPU idle
+  // for a few microseconds.  The host waits on it only two steps later.
+  hipExtLaunchKernelGGL(
       step_prologue_kernel, dim3(static_cast<unsigned>(copy_wgs + append_wgs)),
-      dim3(kPrologueThreads), 0, hs, reinterpret_cast<const pkv::u32x4*>(sg.host_dev),
+      dim3(kPrologueThreads), 0, hs, nullptr, sg.read, 0u,
+      reinterpret_cast<const pkv::u32x4*>(sg.host_dev),
       reinterpret_cast<pkv::u32x4*>(sg.dev), idx_vecs, copy_wgs, slots_host_dev,
       fuse_append ? static_cast<const pkv::u32x4*>(io->k_new[0]) : nullptr,
       fuse_append ? static_cast<const pkv::u32x4*>(io->v_new[0]) : nullptr,
@@ -247,14 +253,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       st->desc.num_heads, st->desc.block_size,
       static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size);
   if (hipGetLastError() != hipSuccess) return PKV_EHIP;
-  // The marker that frees this staging area goes behind the step's last launch rather than
-  // right behind the prologue: an event between two kernels leaves the GPU idle for a few
-  // microseconds, and the host waits on it only two steps later.
-  auto mark_read = [&](pkv_status_t r) {
-    if (hipEventRecord(sg.read, hs) != hipSuccess && r == PKV_OK) r = PKV_EHIP;
-    sg.pending = true;
-    return r;
-  };
+  sg.pending = true;
 
   const int32_t* d_tables = reinterpret_cast<const int32_t*>(sg.dev);
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;
@@ -264,13 +263,13 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
 
   if (*num_cow > 0 && L > 0) {
     s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
-    if (s != PKV_OK) return mark_read(s);
+    if (s != PKV_OK) return s;
   }
   for (int32_t l = 0; l < L; ++l) {
     if (!(l == 0 && fuse_append)) {
       s = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l], io->k_pools[l],
                                 io->v_pools[l], d_slots, n, stream);
-      if (s != PKV_OK) return mark_read(s);
+      if (s != PKV_OK) return s;
     }
     // timing, when asked for, comes from the attention launch itself
     s = pkv::decode_scheduled_timed(&st->desc, io->out[l], io->q[l], io->k_pools[l],
@@ -278,9 +277,9 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
                                     d_items, num_items, decode_flags, workspace, workspace_bytes,
                                     stream, attn_events ? attn_events[2 * l] : nullptr,
                                     attn_events ? attn_events[2 * l + 1] : nullptr);
-    if (s != PKV_OK) return mark_read(s);
+    if (s != PKV_OK) return s;
   }
-  return mark_read(PKV_OK);
+  return PKV_OK;
 }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {

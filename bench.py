@@ -407,6 +407,20 @@ class DecodeBatch:
         self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * self.e + 4 * nblk + 4 * self.S)
 
 
+def host_cpu() -> dict:
+    """The host CPU the oracle baseline ran on: model name and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(batch, units_wanted, bytes_wanted):
     """Time the float64 oracle on (sequence, head) units of the same workload."""
     import torch
@@ -457,7 +471,8 @@ def cpu_baseline(batch, units_wanted, bytes_wanted):
             "seq_layer_per_s": len(units) / batch.H / dt,
             "all_cores": {"value": kv / dt_all / 1e9, "threads": threads,
                           "seq_layer_per_s": len(units) / batch.H / dt_all,
-                          "seconds": round(dt_all, 2)}}
+                          "seconds": round(dt_all, 2)},
+            "host_cpu": host_cpu()}
 
 
 def sweep(args):
@@ -733,7 +748,8 @@ def multi_query_cpu_baseline(w, q, kp, vp, dt, seconds: float = 8.0):
                 break
     return {"value": flops / done / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"{units} (new token, head) units of the first requests of the same "
-                      f"batch, float64 numpy, {done:.2f} s"}
+                      f"batch, float64 numpy, {done:.2f} s",
+            "host_cpu": host_cpu()}
 
 
 def main():

@@ -84,8 +84,9 @@ size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_ite
 
 // Two stages are used alternately.  Stage k owns a pinned host area and a device area of
 // d_index.  The prologue of step i reads the host area of its stage; the host refills that
-// area at step i+2 only after the event recorded behind step i's last launch has fired.  The device
-// area is rewritten at step i+2 by a kernel on the same stream, so step i's readers are done.
+// area at step i+2 only after the completion event of step i's prologue launch has fired.  The
+// device area is rewritten at step i+2 by a kernel on the same stream, so step i's readers are
+// done.
 struct pkv_stepper {
   pkv_alloc_t* alloc = nullptr;
   pkv_cache_desc_t desc{};
@@ -97,7 +98,7 @@ struct pkv_stepper {
     int32_t* host = nullptr;        // pinned: tables | lens | slots | pairs | items
     const char* host_dev = nullptr; // the same memory as the device sees it
     char* dev = nullptr;            // device area of the same size inside d_index
-    hipEvent_t read = nullptr;      // recorded behind the step whose prologue read `host`
+    hipEvent_t read = nullptr;      // completion of the prologue launch that read `host`
     bool pending = false;
   } stage[2];
   int cur = 0;

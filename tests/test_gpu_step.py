@@ -86,6 +86,71 @@ def test_small_two_layer_step_with_copy_on_write():
         check_close(oracle.decode(W.from_torch(outs[l], dt), dt), ref, dt, f"layer {l}")
 
 
+def test_consecutive_steps_without_host_sync():
+    """Eight steps issued back to back behind a long GPU job, with new q / K / V every step and
+    sequences that cross into fresh blocks.  The host runs ahead of the GPU, so it refills each
+    of the two staging areas only on the completion of the prologue that read it; every step's
+    output and the final pools match the oracle replaying the same block-manager decisions."""
+    import torch
+    dev = device()
+    H, D, BS, dt, steps, scale = 4, 128, 16, "f16", 8, 0.1
+    NB, MB = 200, 16
+    g = W.rng(321)
+    order = g.permutation(NB)
+    start = [14, 15, 16, 30, 47, 105, 9]
+    a, m = _setup((NB, order), list(enumerate(start)), [], BS)
+    seqs = np.arange(len(start), dtype=np.int64)
+    S = len(seqs)
+    kp = W.normal_values(g, (NB, H, BS, D), dt)
+    vp = W.normal_values(g, (NB, H, BS, D), dt)
+    qs = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+    kn = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+    vn = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+    kpt, vpt = to_dev(kp, dt, dev), to_dev(vp, dt, dev)
+    qd = [to_dev(x, dt, dev) for x in qs]
+    knd = [to_dev(x, dt, dev) for x in kn]
+    vnd = [to_dev(x, dt, dev) for x in vn]
+    q_t, kn_t, vn_t, out_t = (torch.empty_like(qd[0]) for _ in range(4))
+    outs = [torch.empty_like(qd[0]) for _ in range(steps)]
+    st = pkv.DecodeStepper(a, [kpt], [vpt], [q_t], [kn_t], [vn_t], [out_t], scale, S, MB, 256)
+    x = torch.randn(4096, 4096, device=dev)
+    torch.cuda.synchronize()
+
+    for _ in range(40):               # ~tens of ms of GPU work ahead of the steps
+        y = x @ x
+    busy_done = torch.cuda.Event()
+    busy_done.record()
+    ahead = []
+    for i in range(steps):            # everything on the current stream, no host sync
+        q_t.copy_(qd[i])
+        kn_t.copy_(knd[i])
+        vn_t.copy_(vnd[i])
+        st.step(seqs)
+        outs[i].copy_(out_t)
+        ahead.append(not busy_done.query())
+    torch.cuda.synchronize()
+    del y
+    assert ahead[1], "the host did not run ahead of the GPU"
+
+    ek, ev = kp, vp
+    crossed = 0
+    for i in range(steps):
+        mslots, mpairs, _ = m.append_slots(seqs.tolist())
+        assert not mpairs
+        crossed += sum(1 for sl in mslots if sl % BS == 0)
+        ek, ev = oracle.reshape_and_cache(kn[i], vn[i], ek, ev, np.array(mslots))
+        lens = np.array([m.seq_len(int(s)) for s in seqs], np.int32)
+        tables = np.full((S, MB), -1, np.int32)
+        for j, s in enumerate(seqs):
+            row = m.block_table(int(s))
+            tables[j, :len(row)] = row
+        ref = oracle.paged_attention_decode(qs[i], ek, ev, tables, lens, scale, dt)
+        check_close(oracle.decode(W.from_torch(outs[i], dt), dt), ref, dt, f"step {i}")
+    assert crossed >= S                # every sequence started a fresh block at least once
+    assert np.array_equal(W.from_torch(kpt, dt).view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(W.from_torch(vpt, dt).view(np.uint16), ev.view(np.uint16))
+
+
 def test_fork_step_shared_prefix_copy_on_write():
     """32 groups x 8 sequences forked from a 512 + r (r in [1, 15]) token prompt: one decode
     step copies each group's shared partial block 7 times (the 8th writer owns it) -- 224

@@ -135,12 +135,58 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
+def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
+    """Plain nontemporal read of exactly the K/V tiles one decode layer of `workload` reads."""
+    import torch
+    import paged_kv_cache_306_amd as pkv
+    sp = workload_spec(workload, seed, 16, "permuted")
+    H, NB = sp["H"], sp["NB"]
+    tile = sp["BS"] * sp["D"] * 2
+    alloc = pkv.BlockAllocator(NB, sp["BS"], free_order=sp["order"])
+    lens = sp["lens"] + 1
+    for s, L in enumerate(lens.tolist()):
+        alloc.add_seq(s, int(L))
+    heads = np.arange(H, dtype=np.int64)
+    parts = []
+    for s in np.argsort(-lens, kind="stable").tolist():
+        blk = np.asarray(alloc.block_table(s), np.int64)
+        k_tiles = (blk[:, None] * H + heads[None, :]).reshape(-1)
+        parts.append(np.stack([k_tiles, NB * H + k_tiles], axis=1).reshape(-1))
+    idx = np.concatenate(parts)
+    nbytes = 2 * NB * H * tile
+    assert tile == 4096 and idx.max() < 2 * NB * H
+    dev = torch.device("cuda:0")
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    order = torch.from_numpy(idx.astype(np.int32)).to(dev)
+    read = len(idx) * tile
+
+    def launch():
+        st = probe(buf.data_ptr(), nbytes, tile, order.data_ptr(), len(idx), 1, sink.data_ptr(),
+                   wgs, stream)
+        if st != 0:
+            raise RuntimeError(f"pkv_probe_read returned {st}")
+    for _ in range(3):
+        launch()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for a, z in evs:
+        a.record()
+        launch()
+        z.record()
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(z) for a, z in evs])) / 1e3
+    return {"pattern": f"decode_tiles_{workload}", "tile_bytes": tile, "nontemporal": True,
+            "bytes": int(read), "us": round(t * 1e6, 1), "GB/s": round(read / t / 1e9, 1),
+            "frac_of_peak": round(read / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def ceiling_bench(args):
     """Achievable HBM read rate on this GPU for the decode kernel's access patterns: one
     contiguous stream, and whole tiles visited in a seeded random order (a paged gather reads
     whole (block, head) tiles: 2, 4 and 8 KiB at fp16, head_dim 128, block size 8, 16, 32),
-    plus the same 4 KiB tiles in address order, and exactly the tiles one decode launch of the
-    LLaMA-13B-shaped layer reads.  4 GiB buffer, HIP events, median of 20."""
+    plus the same 4 KiB tiles in address order (4 GiB buffer), and exactly the tiles one decode
+    launch of the LLaMA-13B-shaped layer and of the 40-layer step reads.  HIP events, median
+    of 20."""
     import ctypes
     import torch
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_306_amd",
@@ -190,49 +236,15 @@ def ceiling_bench(args):
                      "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
         print(json.dumps(rows[-1]), flush=True)
 
-    # The decode launch's own bytes: every K and V (block, head) tile that one decode step of
-    # the LLaMA-13B-shaped layer reads (start lengths + the appended token), at their seeded
-    # physical places, in one launch of that size -- sequences longest first, then logical
-    # block, then head, K before V.  The two pools sit back to back in the same buffer.
-    import paged_kv_cache_306_amd as pkv
-    sp = workload_spec("llama13b_layer", args.seed, 16, "permuted")
-    H, NB = sp["H"], sp["NB"]
-    tile = sp["BS"] * sp["D"] * 2
-    alloc = pkv.BlockAllocator(NB, sp["BS"], free_order=sp["order"])
-    lens = sp["lens"] + 1
-    for s, L in enumerate(lens.tolist()):
-        alloc.add_seq(s, int(L))
-    heads = np.arange(H, dtype=np.int64)
-    parts = []
-    for s in np.argsort(-lens, kind="stable").tolist():
-        blk = np.asarray(alloc.block_table(s), np.int64)
-        k_tiles = (blk[:, None] * H + heads[None, :]).reshape(-1)
-        parts.append(np.stack([k_tiles, NB * H + k_tiles], axis=1).reshape(-1))
-    idx = np.concatenate(parts)
-    assert tile == 4096 and 2 * NB * H * tile <= nbytes and idx.max() < 2 * NB * H
-    order = torch.from_numpy(idx.astype(np.int32)).to(dev)
-    n_tiles = len(idx)
-    read = n_tiles * tile
-
-    def launch_decode_tiles():
-        st = probe(buf.data_ptr(), nbytes, tile, order.data_ptr(), n_tiles, 1, sink.data_ptr(),
-                   wgs, stream)
-        if st != 0:
-            raise RuntimeError(f"pkv_probe_read returned {st}")
-    for _ in range(3):
-        launch_decode_tiles()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(20)]
-    for a, z in evs:
-        a.record()
-        launch_decode_tiles()
-        z.record()
-    torch.cuda.synchronize()
-    t = float(np.median([a.elapsed_time(z) for a, z in evs])) / 1e3
-    rows.append({"pattern": "decode_tiles", "tile_bytes": tile, "nontemporal": True,
-                 "bytes": int(read), "us": round(t * 1e6, 1), "GB/s": round(read / t / 1e9, 1),
-                 "frac_of_peak": round(read / t / 1e9 / HBM_PEAK_GBS, 4)})
-    print(json.dumps(rows[-1]), flush=True)
+    # The decode launch's own bytes: every K and V (block, head) tile that one decode layer of
+    # the LLaMA-13B-shaped layer and of the 40-layer step reads (start lengths + the appended
+    # token), at their seeded physical places, in one launch of that size -- sequences longest
+    # first, then logical block, then head, K before V.  Each workload's two pools sit back to
+    # back in a buffer of their own.
+    del buf
+    for wl in ("llama13b_layer", "full_step_40"):
+        rows.append(decode_tiles_ceiling(probe, wl, args.seed, wgs, sink, stream))
+        print(json.dumps(rows[-1]), flush=True)
     print(json.dumps({"ceiling_bytes_per_launch": nbytes, "workgroups": wgs,
                       "peak_GB/s": HBM_PEAK_GBS, "cases": len(rows)}), flush=True)
 

@@ -669,7 +669,9 @@ def multi_query_bench(args):
     cl = torch.from_numpy(w.lens).to(dev)
     qsd = torch.from_numpy(qs).to(dev)
     sl = torch.from_numpy(slots).to(dev)
-    items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len)).to(dev)
+    # requests that share a system prompt (the same first physical block) run side by side
+    items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len,
+                                                      group_keys=w.tables[:, 0])).to(dev)
     maxq = int(new.max())
     # algorithmic work: token i of sequence s sees P + 1 = L_s - n_s + i + 1 keys; per key and
     # head 2 D flops for the score and 2 D for the output

@@ -198,11 +198,21 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  * number of items, or -1 for bad arguments, capacity too small, a decreasing query_start,
  * num_seqs > 2^20 or more than 2^11 tiles per sequence.  Outputs are bit-identical for any
  * item order.  A device item naming a sequence or tile outside the call is ignored.
+ * pkv_multi_query_schedule_grouped (host only): the same items, with group_keys (host,
+ * [num_seqs], or NULL for the order above): sequences with equal keys -- for instance the
+ * first physical block of their tables, so sequences that share prefix blocks after a
+ * prefix-cache hit ("Advanced Features" -> "Prefix Caching") -- are scheduled side by side,
+ * so their shared K/V is read from L2 while they run; groups that read the most keys first,
+ * inside a group the order above.  Same return values.
  */
 int32_t pkv_multi_query_tile(void);
 int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
                                  int32_t num_seqs, int32_t max_context_len, int32_t* items,
                                  int32_t capacity);
+int32_t pkv_multi_query_schedule_grouped(const int32_t* query_start,
+                                         const int32_t* context_lens, const int32_t* group_keys,
+                                         int32_t num_seqs, int32_t max_context_len,
+                                         int32_t* items, int32_t capacity);
 pkv_status_t pkv_paged_attention_multi_query(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -61,6 +61,7 @@ _SIGNATURES = {
                                           _p, _sz, _p]),
     "pkv_multi_query_tile": (_i32, []),
     "pkv_multi_query_schedule": (_i32, [_p, _p, _i32, _i32, _p, _i32]),
+    "pkv_multi_query_schedule_grouped": (_i32, [_p, _p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_multi_query": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p, _i32,
                                                _i32, _i32, _i32, _f32, _p, _i32, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
@@ -228,25 +229,32 @@ def multi_query_tile() -> int:
     return int(_lib().pkv_multi_query_tile())
 
 
-def multi_query_schedule(query_start, context_lens, max_context_len: int):
+def multi_query_schedule(query_start, context_lens, max_context_len: int, group_keys=None):
     """Host-built work items (int32 numpy) for multi-query attention from host copies of
-    query_start [S+1] and context_lens [S]: one per (sequence, tile) with new tokens."""
+    query_start [S+1] and context_lens [S]: one per (sequence, tile) with new tokens.
+    ``group_keys`` (int [S], e.g. the first physical block of each table): sequences with
+    equal keys are scheduled side by side, so the prefix blocks they share are read from L2."""
     import numpy as np
     qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
     cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     S = int(cl.shape[0])
     if qs.shape != (S + 1,):
         raise ValueError("query_start needs num_seqs + 1 entries")
+    keys = None
+    if group_keys is not None:
+        keys = np.ascontiguousarray(np.asarray(group_keys, dtype=np.int32))
+        if keys.shape != (S,):
+            raise ValueError("group_keys needs num_seqs entries")
     tile = multi_query_tile()
     n = np.diff(qs.astype(np.int64))
     cap = max(1, int(np.sum(np.maximum(-(-n // tile), 0))))
     items = np.empty(cap, np.int32)
-    k = _lib().pkv_multi_query_schedule(qs.ctypes.data_as(ctypes.c_void_p),
-                                        cl.ctypes.data_as(ctypes.c_void_p), S,
-                                        int(max_context_len),
-                                        items.ctypes.data_as(ctypes.c_void_p), cap)
+    k = _lib().pkv_multi_query_schedule_grouped(
+        qs.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p),
+        keys.ctypes.data_as(ctypes.c_void_p) if keys is not None else None, S,
+        int(max_context_len), items.ctypes.data_as(ctypes.c_void_p), cap)
     if k < 0:
-        raise PkvError(PKV_EINVAL, "pkv_multi_query_schedule")
+        raise PkvError(PKV_EINVAL, "pkv_multi_query_schedule_grouped")
     return items[:k].copy()
 
 

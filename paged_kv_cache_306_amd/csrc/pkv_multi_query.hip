@@ -547,18 +547,36 @@ extern "C" {
 
 int32_t pkv_multi_query_tile(void) { return kMqTileQueries; }
 
-int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
-                                 int32_t num_seqs, int32_t max_context_len, int32_t* items,
-                                 int32_t capacity) {
+int32_t pkv_multi_query_schedule_grouped(const int32_t* query_start,
+                                         const int32_t* context_lens, const int32_t* group_keys,
+                                         int32_t num_seqs, int32_t max_context_len,
+                                         int32_t* items, int32_t capacity) {
   if (num_seqs < 0 || max_context_len < 0 || capacity < 0 || num_seqs > kMqItemSeqMask + 1 ||
       (num_seqs > 0 && (!query_start || !context_lens || !items)))
     return -1;
   struct Item {
-    int64_t seq_keys;   // keys read by the sequence's largest tile
-    int64_t keys;       // keys read by this tile
+    int64_t group_keys;  // keys read by the largest tile of the sequence's group
+    int32_t leader;      // first sequence of the group
+    int64_t seq_keys;    // keys read by the sequence's largest tile
+    int64_t keys;        // keys read by this tile
     int32_t s, tile;
   };
+  // group leader = first sequence with the same key (sequences sharing prefix blocks); with
+  // no keys every sequence is a group of its own
+  std::vector<int32_t> leader(static_cast<size_t>(num_seqs));
+  if (group_keys) {
+    std::vector<std::pair<int32_t, int32_t>> kv;
+    kv.reserve(static_cast<size_t>(num_seqs));
+    for (int32_t s = 0; s < num_seqs; ++s) kv.push_back({group_keys[s], s});
+    std::sort(kv.begin(), kv.end());
+    for (size_t i = 0; i < kv.size(); ++i)
+      leader[kv[i].second] = (i > 0 && kv[i].first == kv[i - 1].first)
+                                 ? leader[kv[i - 1].second] : kv[i].second;
+  } else {
+    for (int32_t s = 0; s < num_seqs; ++s) leader[s] = s;
+  }
   std::vector<Item> list;
+  std::vector<int64_t> best(static_cast<size_t>(num_seqs), 0);
   for (int s = 0; s < num_seqs; ++s) {
     const int64_t n = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
     if (n < 0) return -1;
@@ -567,15 +585,20 @@ int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* cont
     if (tiles > kMqMaxTiles) return -1;
     const int64_t L = std::min<int64_t>(context_lens[s], max_context_len);
     const int64_t base = std::max<int64_t>(L - n, 0);
+    best[leader[s]] = std::max(best[leader[s]], base + n);
     for (int64_t t = 0; t < tiles; ++t) {
       const int64_t keys = base + std::min<int64_t>(n, (t + 1) * kMqTileQueries);
-      list.push_back({base + n, keys, s, static_cast<int32_t>(t)});
+      list.push_back({0, leader[s], base + n, keys, s, static_cast<int32_t>(t)});
     }
   }
   if (static_cast<int64_t>(list.size()) > capacity) return -1;
-  // Longest sequences first; a sequence's tiles stay adjacent (largest first) so that its
-  // K/V, read by every tile, is shared in L2 while they run.
+  for (Item& it : list) it.group_keys = best[it.leader];
+  // Groups that read the most keys first, a group's sequences adjacent (so the prefix blocks
+  // they share stay in L2 while they run), inside a group the longest sequences first, and a
+  // sequence's tiles adjacent (largest first) so that they share its own K/V in L2 too.
   std::stable_sort(list.begin(), list.end(), [](const Item& x, const Item& y) {
+    if (x.group_keys != y.group_keys) return x.group_keys > y.group_keys;
+    if (x.leader != y.leader) return x.leader < y.leader;
     if (x.seq_keys != y.seq_keys) return x.seq_keys > y.seq_keys;
     if (x.s != y.s) return x.s < y.s;
     return x.keys > y.keys;
@@ -583,6 +606,13 @@ int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* cont
   for (size_t i = 0; i < list.size(); ++i)
     items[i] = list[i].s | (list[i].tile << kMqItemSeqBits);
   return static_cast<int32_t>(list.size());
+}
+
+int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t* items,
+                                 int32_t capacity) {
+  return pkv_multi_query_schedule_grouped(query_start, context_lens, nullptr, num_seqs,
+                                          max_context_len, items, capacity);
 }
 
 pkv_status_t pkv_paged_attention_multi_query(

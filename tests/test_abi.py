@@ -186,6 +186,38 @@ def test_multi_query_schedule_covers_every_tile_by_sequence():
     assert lib.pkv_multi_query_schedule(ptr(qs), ptr(ctx), 0, 6000, ptr(buf), 0) == 0
 
 
+def test_multi_query_schedule_grouped_keeps_groups_together():
+    import numpy as np
+    tile = pkv.multi_query_tile()
+    n = np.array([3, 0, 2 * tile + 72, tile, tile + 1, 1, 40], np.int64)
+    ctx = np.array([1000, 50, 2 * tile + 72, 5000, tile + 1, 1, 1100], np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    ntiles = [-(-int(x) // tile) for x in n]
+    plain = pkv.multi_query_schedule(qs, ctx, 6000)
+    # distinct keys: the plain order
+    assert pkv.multi_query_schedule(qs, ctx, 6000, group_keys=np.arange(7) * 3).tolist() == \
+        plain.tolist()
+    # sequences 0, 4 and 6 share a prefix (key 9), 2 and 5 another (key 4), 3 alone: groups by
+    # the most keys any tile of theirs reads (3: 5000, {0, 4, 6}: 1100, {2, 5}: 2 tile + 72),
+    # inside a group the plain order, a sequence's tiles adjacent and largest first
+    keys = np.array([9, 7, 4, 1, 9, 4, 9], np.int32)
+    items = pkv.multi_query_schedule(qs, ctx, 6000, group_keys=keys)
+    pairs = list(zip((items & ((1 << 20) - 1)).tolist(), (items >> 20).tolist()))
+    assert sorted(pairs) == sorted(zip((plain & ((1 << 20) - 1)).tolist(),
+                                       (plain >> 20).tolist()))
+    order = [3, 6, 0, 4, 2, 5]
+    assert pairs == [(s, t) for s in order for t in reversed(range(ntiles[s]))]
+    lib = pkv.lib()
+    buf = np.zeros(16, np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert lib.pkv_multi_query_schedule_grouped(ptr(qs), ptr(ctx), ptr(keys), 7, 6000, ptr(buf),
+                                                len(pairs) - 1) == -1
+    assert lib.pkv_multi_query_schedule_grouped(None, ptr(ctx), ptr(keys), 7, 6000, ptr(buf),
+                                                16) == -1
+    with pytest.raises(ValueError):
+        pkv.multi_query_schedule(qs, ctx, 6000, group_keys=keys[:3])
+
+
 def test_workspace_size_formula():
     d = _desc(h=40, d=128)
     assert pkv.decode_workspace_bytes(d, 64, 100) == 0        # single pass

@@ -89,8 +89,12 @@ def test_multi_query_schedule_is_bit_identical_to_the_grid():
     shuffled = items.copy()
     W.rng(7).shuffle(shuffled)
     shuf = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev, items=shuffled)
+    grouped_items = pkv.multi_query_schedule(qs, ctx, int(ctx.max()),
+                                             group_keys=np.arange(len(ctx)) % 3)
+    grouped = run_mq(q, kp, vp, tables, ctx, qs, scale, "f16", dev, items=grouped_items)
     assert np.array_equal(plain.view(np.uint16), sched.view(np.uint16))
     assert np.array_equal(plain.view(np.uint16), shuf.view(np.uint16))
+    assert np.array_equal(plain.view(np.uint16), grouped.view(np.uint16))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

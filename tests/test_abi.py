@@ -63,6 +63,7 @@ def test_decode_argument_errors():
     assert _decode(_desc(), mb=0) == pkv.PKV_EINVAL
     assert _decode(_desc(), scale=float("nan")) == pkv.PKV_EINVAL
     assert _decode(_desc(), S=0) == pkv.PKV_OK                    # nothing to do
+    assert _decode(_desc(), S=(1 << 20) + 1) == pkv.PKV_EUNSUPPORTED  # work items hold 20 bits
     # a split launch needs workspace
     d = _desc()
     big = pkv.lib().pkv_decode_single_pass_max() + 1000
@@ -150,6 +151,7 @@ def test_multi_query_argument_errors():
     assert _mq(_desc(), maxq=pkv.multi_query_tile() * 2048 + 1) == pkv.PKV_EUNSUPPORTED  # > 2^11 tiles
     assert _mq(_desc(), T=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), S=0) == pkv.PKV_OK                               # nothing to do
+    assert _mq(_desc(), S=(1 << 20) + 1) == pkv.PKV_EUNSUPPORTED          # > 2^20 sequences
     assert _mq(_desc(), T=0) == pkv.PKV_OK
     assert _mq(_desc(), maxq=0) == pkv.PKV_OK
 

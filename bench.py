@@ -24,6 +24,8 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import math
 import os
@@ -120,6 +122,19 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     return ap.parse_args()
+
+
+@contextlib.contextmanager
+def gc_paused():
+    """Python's cyclic garbage collector off while steps are timed, as timeit does: a full
+    collection walks every object torch has created and takes tens of milliseconds, which
+    would otherwise land inside one timed step."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def calibrate_copy(mib: int):
@@ -330,8 +345,7 @@ class DecodeBatch:
         self.next_id = self.S
         self.roots = []
         if sp.get("refork"):
-            for gi in range(sp["groups"]):
-                self._fork_group(gi)
+            self._fork_groups()
         elif sp["groups"]:
             per = self.S // sp["groups"]
             for gi in range(sp["groups"]):
@@ -365,16 +379,16 @@ class DecodeBatch:
         self.alg_bytes = []      # algorithmic bytes of one attention launch, per step
         self.last = None
 
-    def _fork_group(self, gi):
-        """Group gi afresh: member 0 holds the group's prompt, the other members fork it."""
+    def _fork_groups(self):
+        """Every group afresh: member 0 holds the group's prompt, the other members fork it
+        (one batched block-manager call for the prompts and one for the forks)."""
         per = self.S // self.sp["groups"]
-        first = gi * per
-        for s in range(first, first + per):
-            self.seq_ids[s] = self.next_id
-            self.next_id += 1
-        self.alloc.add_seq(int(self.seq_ids[first]), int(self.sp["prompts"][gi]))
-        for s in range(first + 1, first + per):
-            self.alloc.fork(int(self.seq_ids[first]), int(self.seq_ids[s]))
+        self.seq_ids[:] = np.arange(self.next_id, self.next_id + self.S, dtype=np.int64)
+        self.next_id += self.S
+        firsts = self.seq_ids[::per]
+        self.alloc.add_seqs(firsts, self.sp["prompts"])
+        members = self.seq_ids.reshape(-1, per)
+        self.alloc.fork_many(np.repeat(firsts, per - 1), members[:, 1:].reshape(-1))
 
     def _fork_member(self, s, sid):
         """Member s of its group: a fork of the group's prefix root plus its own tail."""
@@ -389,10 +403,8 @@ class DecodeBatch:
         (the fork step replaces every group after each step)."""
         if self.sp.get("refork"):
             if (self.cur_len > self.init_lens).any():
-                for sid in self.seq_ids:
-                    self.alloc.free_seq(int(sid))
-                for gi in range(self.sp["groups"]):
-                    self._fork_group(gi)
+                self.alloc.free_seqs(self.seq_ids)
+                self._fork_groups()
                 self.cur_len = self.init_lens.copy()
             return
         done = np.nonzero(self.cur_len - self.init_lens >= self.growth)[0]
@@ -508,11 +520,12 @@ def sweep(args):
                     z.record()
                     hs.append((ctypes.c_void_p * 2)(a.cuda_event, z.cuda_event))
                 torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for i in range(args.steps):
-                    b.step(hs[i])
-                torch.cuda.synchronize()
-                wall = time.perf_counter() - t0
+                with gc_paused():
+                    t0 = time.perf_counter()
+                    for i in range(args.steps):
+                        b.step(hs[i])
+                    torch.cuda.synchronize()
+                    wall = time.perf_counter() - t0
                 launch = float(np.mean([a.elapsed_time(z) for a, z in evs])) / 1e3
                 used = int(sum(b.alloc.block_table(int(s)).__len__() for s in b.seq_ids))
                 waste = b.alloc.wasted_slots()
@@ -689,15 +702,16 @@ def multi_query_bench(args):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, z in evs:
-        pkv.reshape_and_cache(kn, vn, kp, vp, sl)
-        a.record()
-        pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len,
-                                        work_items=items)
-        z.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with gc_paused():
+        t0 = time.perf_counter()
+        for a, z in evs:
+            pkv.reshape_and_cache(kn, vn, kp, vp, sl)
+            a.record()
+            pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
+                                            w.max_len, work_items=items)
+            z.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     launch_s = float(np.mean([a.elapsed_time(z) for a, z in evs])) / 1e3
     peak = MFMA_PEAK_TFLOPS[dt]
     achieved = flops / launch_s / 1e12
@@ -815,15 +829,16 @@ def main():
              if args.flush_mall else None)
     torch.cuda.synchronize()
     host = 0.0
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.view(torch.int64).sum()   # reads 1 GiB: evicts the MALL, leaves no dirty lines
-        h0 = time.perf_counter()
-        b.step(handles[i])
-        host += time.perf_counter() - h0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with gc_paused():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.view(torch.int64).sum()   # reads 1 GiB: evicts the MALL, no dirty lines
+            h0 = time.perf_counter()
+            b.step(handles[i])
+            host += time.perf_counter() - h0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     attn_ms = [a.elapsed_time(z) for per_step in evs for a, z in per_step]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
     kv_total = float(np.sum(b.kv_bytes))

@@ -332,6 +332,17 @@ pkv_status_t pkv_alloc_append_slots(pkv_alloc_t* a, const int64_t* seqs, int32_t
                                     int32_t* slots, int32_t* cow_pairs, int32_t* num_cow,
                                     int32_t* num_done);
 pkv_status_t pkv_alloc_free_seq(pkv_alloc_t* a, int64_t seq);
+/* Batched forms for a scheduler that starts, forks (beam search, parallel sampling: "KV-Cache
+ * Sharing (Copy-on-Write)") or ends many sequences per step with one host call each:
+ * add_seq(seqs[i], lens[i]), fork(parents[i], children[i]) and free_seq(seqs[i]) for
+ * i = 0..n-1 in order (host arrays).  Processing stops at the first error, which is returned;
+ * *num_done (host out) is the number of calls that succeeded, whose effects stay. */
+pkv_status_t pkv_alloc_add_seqs(pkv_alloc_t* a, const int64_t* seqs, const int32_t* lens,
+                                int32_t n, int32_t* num_done);
+pkv_status_t pkv_alloc_fork_many(pkv_alloc_t* a, const int64_t* parents, const int64_t* children,
+                                 int32_t n, int32_t* num_done);
+pkv_status_t pkv_alloc_free_seqs(pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                                 int32_t* num_done);
 /* Copies up to `cap` physical block ids of seq's table into out (host); *n = table length. */
 pkv_status_t pkv_alloc_block_table(const pkv_alloc_t* a, int64_t seq, int32_t* out, int32_t cap,
                                    int32_t* n);

@@ -73,6 +73,9 @@ _SIGNATURES = {
     "pkv_alloc_append_slot": (_i32, [_p, _i64, _pi32, _pi32, _pi32]),
     "pkv_alloc_append_slots": (_i32, [_p, _p, _i32, _p, _p, _pi32, _pi32]),
     "pkv_alloc_free_seq": (_i32, [_p, _i64]),
+    "pkv_alloc_add_seqs": (_i32, [_p, _p, _p, _i32, _pi32]),
+    "pkv_alloc_fork_many": (_i32, [_p, _p, _p, _i32, _pi32]),
+    "pkv_alloc_free_seqs": (_i32, [_p, _p, _i32, _pi32]),
     "pkv_alloc_block_table": (_i32, [_p, _i64, _p, _i32, _pi32]),
     "pkv_alloc_export": (_i32, [_p, _p, _i32, _i32, _p, _p]),
     "pkv_alloc_seq_len": (_i32, [_p, _i64]),
@@ -467,6 +470,43 @@ class BlockAllocator:
 
     def free_seq(self, seq: int):
         _check(_lib().pkv_alloc_free_seq(self._h, seq), "pkv_alloc_free_seq")
+
+    def _batched(self, fn, name, arrays, n):
+        done = _i32()
+        st = getattr(_lib(), fn)(self._h, *[a.ctypes.data_as(ctypes.c_void_p) for a in arrays],
+                                 n, ctypes.byref(done))
+        if st != PKV_OK:
+            err = PkvError(st, name)
+            err.num_done = done.value
+            raise err
+
+    def add_seqs(self, seqs, lens):
+        """add_seq(seqs[i], lens[i]) for every i in one host call; on an error the calls before
+        it stay and the raised PkvError carries ``num_done``."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+        if lens.shape != seqs.shape or seqs.ndim != 1:
+            raise ValueError("one length per sequence")
+        self._batched("pkv_alloc_add_seqs", "pkv_alloc_add_seqs", (seqs, lens), seqs.shape[0])
+
+    def fork_many(self, parents, children):
+        """fork(parents[i], children[i]) for every i in one host call (same error rule)."""
+        import numpy as np
+        parents = np.ascontiguousarray(np.asarray(parents, dtype=np.int64))
+        children = np.ascontiguousarray(np.asarray(children, dtype=np.int64))
+        if parents.shape != children.shape or parents.ndim != 1:
+            raise ValueError("one parent per child")
+        self._batched("pkv_alloc_fork_many", "pkv_alloc_fork_many", (parents, children),
+                      parents.shape[0])
+
+    def free_seqs(self, seqs):
+        """free_seq(seqs[i]) for every i in one host call (same error rule)."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        if seqs.ndim != 1:
+            raise ValueError("a 1-D list of sequences")
+        self._batched("pkv_alloc_free_seqs", "pkv_alloc_free_seqs", (seqs,), seqs.shape[0])
 
     def block_table(self, seq: int):
         n = _i32()

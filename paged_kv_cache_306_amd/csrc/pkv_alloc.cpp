@@ -200,6 +200,44 @@ pkv_status_t pkv_alloc_free_seq(pkv_alloc_t* a, int64_t seq) {
   return PKV_OK;
 }
 
+// Batched forms: the same calls in order, stopping at the first error (returned), with
+// *num_done the number of calls that succeeded.
+pkv_status_t pkv_alloc_add_seqs(pkv_alloc_t* a, const int64_t* seqs, const int32_t* lens,
+                                int32_t n, int32_t* num_done) {
+  if (!a || n < 0 || (n > 0 && (!seqs || !lens)) || !num_done) return PKV_EINVAL;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_status_t st = pkv_alloc_add_seq(a, seqs[i], lens[i]);
+    if (st != PKV_OK) return st;
+    ++*num_done;
+  }
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_fork_many(pkv_alloc_t* a, const int64_t* parents, const int64_t* children,
+                                 int32_t n, int32_t* num_done) {
+  if (!a || n < 0 || (n > 0 && (!parents || !children)) || !num_done) return PKV_EINVAL;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_status_t st = pkv_alloc_fork(a, parents[i], children[i]);
+    if (st != PKV_OK) return st;
+    ++*num_done;
+  }
+  return PKV_OK;
+}
+
+pkv_status_t pkv_alloc_free_seqs(pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                                 int32_t* num_done) {
+  if (!a || n < 0 || (n > 0 && !seqs) || !num_done) return PKV_EINVAL;
+  *num_done = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_status_t st = pkv_alloc_free_seq(a, seqs[i]);
+    if (st != PKV_OK) return st;
+    ++*num_done;
+  }
+  return PKV_OK;
+}
+
 pkv_status_t pkv_alloc_block_table(const pkv_alloc_t* a, int64_t seq, int32_t* out, int32_t cap,
                                    int32_t* n) {
   if (!a || !n || cap < 0 || (cap > 0 && !out)) return PKV_EINVAL;

@@ -48,20 +48,52 @@ int main(int argc, char** argv) {
         return fail("add_seq_cached status", step);
       }
       ++next;
-    } else if (op < 2 || live.empty()) {
+    } else if ((op < 2 || live.empty()) && rng() % 2) {
       int32_t len = static_cast<int32_t>(rng() % (4 * BS));
       pkv_status_t st = pkv_alloc_add_seq(a, next, len);
       if (st == PKV_OK) live.push_back(next);
       else if (st != PKV_ENOMEM) return fail("add_seq status", step);
       ++next;
-    } else if (op < 4) {
+    } else if (op < 2 || live.empty()) {  // batched: up to 3 new sequences in one call
+      const int32_t n = static_cast<int32_t>(1 + rng() % 3);
+      std::vector<int64_t> ids(n);
+      std::vector<int32_t> lens(n);
+      for (int32_t i = 0; i < n; ++i) {
+        ids[i] = next++;
+        lens[i] = static_cast<int32_t>(rng() % (4 * BS));
+      }
+      int32_t done = -1;
+      pkv_status_t st = pkv_alloc_add_seqs(a, ids.data(), lens.data(), n, &done);
+      if ((st != PKV_OK && st != PKV_ENOMEM) || done < 0 || done > n ||
+          (st == PKV_OK && done != n))
+        return fail("add_seqs status", step);
+      for (int32_t i = 0; i < done; ++i) live.push_back(ids[i]);
+    } else if (op < 4 && rng() % 2) {
       int64_t p = live[rng() % live.size()];
       if (pkv_alloc_fork(a, p, next) != PKV_OK) return fail("fork", step);
       live.push_back(next++);
-    } else if (op < 5) {
+    } else if (op < 4) {  // batched: up to 4 children of random parents in one call
+      const int32_t n = static_cast<int32_t>(1 + rng() % 4);
+      std::vector<int64_t> parents(n), children(n);
+      for (int32_t i = 0; i < n; ++i) {
+        parents[i] = live[rng() % live.size()];
+        children[i] = next++;
+      }
+      int32_t done = -1;
+      if (pkv_alloc_fork_many(a, parents.data(), children.data(), n, &done) != PKV_OK ||
+          done != n)
+        return fail("fork_many", step);
+      for (int64_t c : children) live.push_back(c);
+    } else if (op < 5 && (rng() % 2 || live.size() < 2)) {
       size_t i = rng() % live.size();
       if (pkv_alloc_free_seq(a, live[i]) != PKV_OK) return fail("free", step);
       live.erase(live.begin() + static_cast<long>(i));
+    } else if (op < 5) {  // batched: the last two live sequences in one call
+      std::vector<int64_t> ids(live.end() - 2, live.end());
+      int32_t done = -1;
+      if (pkv_alloc_free_seqs(a, ids.data(), 2, &done) != PKV_OK || done != 2)
+        return fail("free_seqs", step);
+      live.resize(live.size() - 2);
     } else {
       const int32_t n = static_cast<int32_t>(std::min<size_t>(live.size(), 1 + rng() % 6));
       std::vector<int64_t> seqs(live.begin(), live.begin() + n);
@@ -108,6 +140,11 @@ int main(int argc, char** argv) {
   if (pkv_alloc_append_slot(a, -42, &slot, &src, &dst) != PKV_EINVAL) return fail("unknown", -1);
   if (pkv_alloc_free_seq(a, -42) != PKV_EINVAL) return fail("unknown free", -1);
   if (pkv_alloc_add_seq(nullptr, 1, 1) != PKV_EINVAL) return fail("null", -1);
+  int32_t done = -1;
+  const int64_t bad[2] = {-42, -43};
+  if (pkv_alloc_free_seqs(a, bad, 2, &done) != PKV_EINVAL || done != 0)
+    return fail("unknown free_seqs", -1);
+  if (pkv_alloc_fork_many(a, bad, bad, 1, nullptr) != PKV_EINVAL) return fail("null done", -1);
   pkv_alloc_destroy(a);
   std::printf("ok %d steps, %lld sequences\n", steps, static_cast<long long>(next));
   return 0;

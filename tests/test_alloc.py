@@ -117,6 +117,60 @@ def test_export_dense_tables():
         a.export([5], 2)
 
 
+def test_batched_calls_match_the_model():
+    """add_seqs / fork_many / free_seqs: the same state as the one-by-one calls on the oracle's
+    model; an error stops the batch with the calls before it applied."""
+    NB, BS = 400, 16
+    order = W.rng(77).permutation(NB)
+    a = pkv.BlockAllocator(NB, BS, free_order=order)
+    m = oracle.BlockManager(NB, BS, free_order=order)
+    roots = list(range(0, 32, 8))
+    lens = [512 + 3, 100, 17, 33]
+    a.add_seqs(roots, lens)
+    for sid, L in zip(roots, lens):
+        m.add_seq(sid, L)
+    parents = [r for r in roots for _ in range(7)]
+    children = [r + j for r in roots for j in range(1, 8)]
+    a.fork_many(parents, children)
+    for p_, c in zip(parents, children):
+        m.fork(p_, c)
+    seqs = roots + children
+    _same_state(a, m, seqs)
+    slots, pairs = a.append_slots(np.array(seqs, np.int64))
+    mslots, mpairs, _ = m.append_slots(seqs)
+    assert slots.tolist() == mslots and [tuple(x) for x in pairs.tolist()] == mpairs
+    gone = children[::2] + [roots[1]]
+    a.free_seqs(gone)
+    for sid in gone:
+        m.free_seq(sid)
+    left = [sid for sid in seqs if sid not in gone]
+    _same_state(a, m, left)
+    # errors: a duplicate id, an unknown parent, an unknown sequence; earlier calls stay
+    with pytest.raises(pkv.PkvError) as e:
+        a.add_seqs([100, 101, 0, 102], [5, 6, 7, 8])
+    assert e.value.status == pkv.PKV_EINVAL and e.value.num_done == 2
+    m.add_seq(100, 5)
+    m.add_seq(101, 6)
+    with pytest.raises(pkv.PkvError) as e:
+        a.fork_many([100, 999], [200, 201])
+    assert e.value.num_done == 1 and a.seq_len(200) == 5 and a.seq_len(201) == -1
+    m.fork(100, 200)
+    with pytest.raises(pkv.PkvError) as e:
+        a.free_seqs([101, 555, 200])
+    assert e.value.num_done == 1 and a.seq_len(101) == -1 and a.seq_len(200) == 5
+    m.free_seq(101)
+    _same_state(a, m, [sid for sid in left] + [100, 200])
+    with pytest.raises(pkv.PkvError) as e:
+        a.add_seqs([300], [NB * BS])                  # more blocks than the pool has free
+    assert e.value.status == pkv.PKV_ENOMEM and e.value.num_done == 0
+    with pytest.raises(ValueError):
+        a.fork_many([1, 2], [3])
+    a.add_seqs([], [])                                # empty batches are fine
+    a.fork_many([], [])
+    a.free_seqs([])
+    _same_state(a, m, [sid for sid in left] + [100, 200])
+
+
 def test_errors():
     with pytest.raises(pkv.PkvError):
         pkv.BlockAllocator(4, 4, free_order=[0, 1, 1, 2])

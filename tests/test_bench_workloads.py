@@ -16,10 +16,9 @@ def _fork_step_manager():
     b = types.SimpleNamespace(sp=sp, S=sp["S"], init_lens=sp["lens"],
                               seq_ids=np.arange(sp["S"], dtype=np.int64), next_id=sp["S"])
     b.alloc = pkv.BlockAllocator(sp["NB"], sp["BS"], free_order=sp["order"])
-    b._fork_group = types.MethodType(bench.DecodeBatch._fork_group, b)
+    b._fork_groups = types.MethodType(bench.DecodeBatch._fork_groups, b)
     b.recycle = types.MethodType(bench.DecodeBatch.recycle, b)
-    for gi in range(sp["groups"]):
-        b._fork_group(gi)
+    b._fork_groups()
     b.cur_len = b.init_lens.copy()
     return sp, b
 

@@ -150,9 +150,11 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
-def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
-    """Plain nontemporal read of exactly the K/V tiles one decode layer of `workload` reads."""
-    import torch
+def decode_tile_list(workload, seed):
+    """The 4 KiB (block, head) tiles one decode layer of `workload` reads (start lengths + the
+    appended token, seeded placement), as indices into a buffer holding the K pool and then
+    the V pool: sequences longest first, then logical block, then head, K before V.
+    Returns (tile indices, tiles in the buffer, tile bytes, spec)."""
     import paged_kv_cache_306_amd as pkv
     sp = workload_spec(workload, seed, 16, "permuted")
     H, NB = sp["H"], sp["NB"]
@@ -167,9 +169,15 @@ def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
         blk = np.asarray(alloc.block_table(s), np.int64)
         k_tiles = (blk[:, None] * H + heads[None, :]).reshape(-1)
         parts.append(np.stack([k_tiles, NB * H + k_tiles], axis=1).reshape(-1))
-    idx = np.concatenate(parts)
-    nbytes = 2 * NB * H * tile
-    assert tile == 4096 and idx.max() < 2 * NB * H
+    return np.concatenate(parts), 2 * NB * H, tile, sp
+
+
+def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
+    """Plain nontemporal read of exactly the K/V tiles one decode layer of `workload` reads."""
+    import torch
+    idx, n_buf_tiles, tile, _ = decode_tile_list(workload, seed)
+    nbytes = n_buf_tiles * tile
+    assert tile == 4096 and idx.max() < n_buf_tiles
     dev = torch.device("cuda:0")
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     order = torch.from_numpy(idx.astype(np.int32)).to(dev)

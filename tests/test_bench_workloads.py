@@ -55,3 +55,21 @@ def test_prefix_hit_batch_shape():
         rows = w.tables[16 * p:16 * p + 16, :64]
         assert (rows == rows[0]).all()
     assert len({tuple(w.tables[16 * p, :64]) for p in range(4)}) == 4
+
+
+def test_decode_tile_list_is_exactly_the_decode_reads():
+    """bench.py --ceiling's own-tiles case reads every K and V (block, head) tile the decode
+    launch reads, each once, and nothing else: ceil(L / 16) blocks per sequence, every head."""
+    for wl in ("llama13b_layer", "full_step_40"):
+        idx, n_buf, tile, sp = bench.decode_tile_list(wl, 2)
+        H, NB = sp["H"], sp["NB"]
+        lens = sp["lens"] + 1
+        nblk = -(-lens // 16)
+        assert tile == 16 * 128 * 2 and n_buf == 2 * NB * H
+        assert len(idx) == 2 * H * int(nblk.sum())
+        assert len(np.unique(idx)) == len(idx) and idx.min() >= 0 and idx.max() < n_buf
+        k, v = idx[idx < NB * H], idx[idx >= NB * H] - NB * H
+        assert np.array_equal(np.sort(k), np.sort(v))            # K and V of the same tiles
+        blocks = np.unique(k // H)
+        assert len(blocks) == int(nblk.sum())                     # no block shared or skipped
+        assert (np.bincount(k % H, minlength=H) == int(nblk.sum())).all()

@@ -260,12 +260,12 @@ def ceiling_bench(args):
         print(json.dumps(rows[-1]), flush=True)
 
     # The decode launch's own bytes: every K and V (block, head) tile that one decode layer of
-    # the LLaMA-13B-shaped layer and of the 40-layer step reads (start lengths + the appended
-    # token), at their seeded physical places, in one launch of that size -- sequences longest
-    # first, then logical block, then head, K before V.  Each workload's two pools sit back to
-    # back in a buffer of their own.
+    # the LLaMA-13B-shaped layer, of the 40-layer step and of the long-context batch reads
+    # (start lengths + the appended token), at their seeded physical places, in one launch of
+    # that size -- sequences longest first, then logical block, then head, K before V.  Each
+    # workload's two pools sit back to back in a buffer of their own.
     del buf
-    for wl in ("llama13b_layer", "full_step_40"):
+    for wl in ("llama13b_layer", "full_step_40", "long_context"):
         rows.append(decode_tiles_ceiling(probe, wl, args.seed, wgs, sink, stream))
         print(json.dumps(rows[-1]), flush=True)
     print(json.dumps({"ceiling_bytes_per_launch": nbytes, "workgroups": wgs,

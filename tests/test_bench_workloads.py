@@ -60,7 +60,7 @@ def test_prefix_hit_batch_shape():
 def test_decode_tile_list_is_exactly_the_decode_reads():
     """bench.py --ceiling's own-tiles case reads every K and V (block, head) tile the decode
     launch reads, each once, and nothing else: ceil(L / 16) blocks per sequence, every head."""
-    for wl in ("llama13b_layer", "full_step_40"):
+    for wl in ("llama13b_layer", "full_step_40", "long_context"):
         idx, n_buf, tile, sp = bench.decode_tile_list(wl, 2)
         H, NB = sp["H"], sp["NB"]
         lens = sp["lens"] + 1

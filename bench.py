@@ -203,24 +203,48 @@ def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
             "frac_of_peak": round(read / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def ceiling_bench(args):
-    """Achievable HBM read rate on this GPU for the decode kernel's access patterns: one
-    contiguous stream, and whole tiles visited in a seeded random order (a paged gather reads
-    whole (block, head) tiles: 2, 4 and 8 KiB at fp16, head_dim 128, block size 8, 16, 32),
-    plus the same 4 KiB tiles in address order (4 GiB buffer), and exactly the tiles one decode
-    launch of the LLaMA-13B-shaped layer and of the 40-layer step reads.  HIP events, median
-    of 20."""
+def load_probe():
+    """pkv_probe_read from the in-tree probe library (include/pkv_probe.h), or None if it is
+    not built."""
     import ctypes
-    import torch
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_306_amd",
                         "libpkv_probe.so")
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+        return None
     probe = ctypes.CDLL(path).pkv_probe_read
     probe.restype = ctypes.c_int32
     probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                       ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                       ctypes.c_void_p]
+    return probe
+
+
+def own_tiles_read_rate(workload, seed):
+    """GB/s of a plain nontemporal read of exactly the K/V tiles one decode launch of
+    `workload` reads, in one launch of that size (the decode launch's practical ceiling), or
+    None when the probe library is missing."""
+    import torch
+    probe = load_probe()
+    if probe is None:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    row = decode_tiles_ceiling(probe, workload, seed, 4096, sink, stream)
+    torch.cuda.empty_cache()
+    return row["GB/s"]
+
+
+def ceiling_bench(args):
+    """Achievable HBM read rate on this GPU for the decode kernel's access patterns: one
+    contiguous stream, and whole tiles visited in a seeded random order (a paged gather reads
+    whole (block, head) tiles: 2, 4 and 8 KiB at fp16, head_dim 128, block size 8, 16, 32),
+    plus the same 4 KiB tiles in address order (4 GiB buffer), and exactly the tiles one decode
+    launch of the LLaMA-13B-shaped layer, of the 40-layer step and of the long-context batch
+    reads.  HIP events, median of 20."""
+    import torch
+    probe = load_probe()
+    if probe is None:
+        raise RuntimeError("libpkv_probe.so is not built (run __graft_entry__.build())")
     dev = torch.device("cuda:0")
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
@@ -880,6 +904,14 @@ def main():
                      "kernel": kname, "avg_launch_us": round(attn_avg_s * 1e6, 2),
                      "alg_bytes_per_launch": int(alg_per_launch)},
     }
+    # the decode launch against a plain read of exactly its own tiles (measured here, after the
+    # timed steps; 16-token blocks at the seeded placement, pools small enough for a copy)
+    if (args.workload in ("llama13b_layer", "long_context") and args.block_size == 16
+            and args.placement == "permuted"):
+        own = own_tiles_read_rate(args.workload, args.seed)
+        if own:
+            res["roofline"]["own_tiles_read_GBs"] = own
+            res["roofline"]["frac_of_own_tiles_read"] = round(achieved / own, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_units, args.cpu_bytes)
     print(json.dumps(res), flush=True)

@@ -102,3 +102,59 @@ def test_calls_run_on_the_given_stream():
     ref = oracle.paged_attention_decode(q, ek, ev, tables, lens, scale, dt)
     check_close(oracle.decode(runs["side"][0], dt), ref, dt, "stepper on a side stream")
     check_close(oracle.decode(runs["side"][1], dt), ref, dt, "decode on a side stream")
+
+
+def test_multi_query_and_block_copies_run_on_the_given_stream():
+    import torch
+    dev = device()
+    H, D, BS, dt = 4, 128, 16, "f16"
+    pairs_ctx = [(1000, 3), (300, 260), (17, 17), (129, 1)]
+    g = W.rng(777)
+    ctx = np.array([c for c, _ in pairs_ctx], np.int32)
+    new = np.array([n for _, n in pairs_ctx], np.int32)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    tables, nb = W.permuted_block_tables(g, ctx, BS, pool_factor=1.3)
+    q = W.normal_values(g, (int(qs[-1]), H, D), dt)
+    kp = W.normal_values(g, (nb, H, BS, D), dt)
+    vp = W.normal_values(g, (nb, H, BS, D), dt)
+    used = sorted({int(b) for b in tables.ravel() if b >= 0})
+    unused = [b for b in range(nb) if b not in set(used)]
+    cow = np.array([[used[0], unused[0]], [used[5], unused[1]]], np.int32)
+    scale = 0.0883883
+    items = pkv.multi_query_schedule(qs, ctx, int(ctx.max()))
+
+    runs = {}
+    for name, on_side in (("default", False), ("side", True)):
+        qd, kd, vd = to_dev(q, dt, dev), to_dev(kp, dt, dev), to_dev(vp, dt, dev)
+        out = torch.full_like(qd, float("nan"))
+        kc, vc = to_dev(kp, dt, dev), to_dev(vp, dt, dev)     # pools for the block copies
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream() if on_side else torch.cuda.current_stream()
+        done, y = _busy_default_stream(dev) if on_side else (None, None)
+        with torch.cuda.stream(stream):
+            bt = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+            cl = torch.from_numpy(ctx).to(dev)
+            qsd = torch.from_numpy(qs).to(dev)
+            it = torch.from_numpy(items).to(dev)
+            pr = torch.from_numpy(cow).to(dev)
+            pkv.paged_attention_multi_query(out, qd, kd, vd, bt, cl, qsd, scale,
+                                            int(new.max()), int(ctx.max()), work_items=it,
+                                            stream=stream)
+            pkv.copy_blocks([kc], [vc], pr, stream=stream)
+            host = [torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in (out, kc, vc)]
+            for h, t in zip(host, (out, kc, vc)):
+                h.copy_(t, non_blocking=True)
+        stream.synchronize()
+        if on_side:
+            assert not done.query(), "the default stream finished first; the check proves nothing"
+        torch.cuda.synchronize()
+        del y
+        runs[name] = [W.from_torch(h, dt) for h in host]
+
+    for a, b in zip(runs["default"], runs["side"]):
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    ek, ev = oracle.copy_blocks([kp, vp], [tuple(p) for p in cow.tolist()])
+    assert np.array_equal(runs["side"][1].view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(runs["side"][2].view(np.uint16), ev.view(np.uint16))
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, dt)
+    check_close(oracle.decode(runs["side"][0], dt), ref, dt, "multi-query on a side stream")

@@ -153,6 +153,27 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
     const int32_t* work_items, int32_t num_items, uint32_t flags, void* workspace,
     size_t workspace_bytes, pkv_stream_t stream);
 
+/* The same attention as pkv_paged_attention_decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument, and nothing is allocated by the call.  The split-context
+ * partials go to a scratch array of PKV_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds in each GPU's memory until the process ends.  A call whose partials need more than
+ * that (pkv_decode_workspace_bytes(desc, num_seqs, max_context_len) after the clamp to
+ * max_blocks_per_seq * block_size) returns PKV_ENOMEM before any device call.  Every call on
+ * one GPU shares that GPU's array and leaves its contents behind (no call relies on them):
+ * two such calls whose launches overlap on one GPU (on different streams) race and must be
+ * ordered by the caller.  Arguments, results and other errors are those of
+ * pkv_paged_attention_decode; PKV_EHIP also when the array's device address cannot be
+ * obtained. */
+#define PKV_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, void* out,
+                                                const void* q, const void* k_pool,
+                                                const void* v_pool, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq,
+                                                const int32_t* context_lens, int32_t num_seqs,
+                                                int32_t max_context_len, float scale,
+                                                pkv_stream_t stream);
+
 /* ---------------------------------------------------------------------------------------
  * Multi-query paged attention: several new tokens of each sequence at once.
  * ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" -> "Prefix

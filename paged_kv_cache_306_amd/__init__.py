@@ -13,7 +13,7 @@ import os
 __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
     "decode_schedule",
-    "paged_attention_decode", "reshape_and_cache", "copy_blocks", "BlockAllocator",
+    "paged_attention_decode", "paged_attention_decode_noalloc", "reshape_and_cache", "copy_blocks", "BlockAllocator",
     "DecodeStepper", "swap_blocks", "LIB_PATH",
 ]
 
@@ -59,6 +59,8 @@ _SIGNATURES = {
                                                     _sz, _p]),
     "pkv_paged_attention_decode": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                                           _p, _sz, _p]),
+    "pkv_paged_attention_decode_noalloc": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32,
+                                                  _i32, _f32, _p]),
     "pkv_multi_query_tile": (_i32, []),
     "pkv_multi_query_schedule": (_i32, [_p, _p, _i32, _i32, _p, _i32]),
     "pkv_multi_query_schedule_grouped": (_i32, [_p, _p, _p, _i32, _i32, _p, _i32]),
@@ -224,6 +226,34 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
             *args, _dev(work_items, "work_items", torch.int32), int(work_items.numel()),
             PKV_DECODE_SHARED_KV if shared_kv else 0, ws_ptr, ws_bytes, _stream_ptr(stream))
         _check(st, "pkv_paged_attention_decode_scheduled")
+    return out
+
+
+# bytes of the per-GPU scratch array pkv_paged_attention_decode_noalloc uses (include/pkv.h)
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   scale: float, max_context_len: int, stream=None):
+    """paged_attention_decode without a workspace: the split-context partials go to the
+    library's per-GPU scratch array, and nothing is allocated (include/pkv.h).  Calls on one
+    GPU share that array, so calls on different streams must not overlap."""
+    import torch
+    desc = desc_for_pool(k_pool)
+    S = q.shape[0]
+    if q.shape != out.shape or q.shape[1:] != (desc.num_heads, desc.head_dim):
+        raise ValueError("q/out shape mismatch")
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool/v_pool mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables/context_lens shape mismatch")
+    st = _lib().pkv_paged_attention_decode_noalloc(
+        ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), S, int(max_context_len), float(scale),
+        _stream_ptr(stream))
+    _check(st, "pkv_paged_attention_decode_noalloc")
     return out
 
 

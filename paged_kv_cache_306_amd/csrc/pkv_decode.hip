@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 namespace pkv {
@@ -524,6 +525,35 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
+// Split-context scratch for callers that cannot allocate (pkv_paged_attention_decode_noalloc):
+// one array per GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, so its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PKV_DECODE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static pkv_status_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PKV_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, const void* q,
                                     const void* k_pool, const void* v_pool,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -652,6 +682,31 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, work_items, num_items, flags, workspace,
                      workspace_bytes, stream);
+}
+
+pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, void* out,
+                                                const void* q, const void* k_pool,
+                                                const void* v_pool, const int32_t* block_tables,
+                                                int32_t max_blocks_per_seq,
+                                                const int32_t* context_lens, int32_t num_seqs,
+                                                int32_t max_context_len, float scale,
+                                                pkv_stream_t stream) {
+  pkv_status_t st = check_desc(desc);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0) return PKV_EINVAL;
+  // the partials this call needs, from the same bound the launch is sized with; rejected
+  // before any device call when they exceed the array
+  const int max_len = effective_max_len(max_context_len, max_blocks_per_seq, desc->block_size);
+  const size_t need = num_seqs > 0 ? pkv_decode_workspace_bytes(desc, num_seqs, max_len) : 0;
+  if (need > static_cast<size_t>(PKV_DECODE_NOALLOC_SCRATCH_BYTES)) return PKV_ENOMEM;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, max_context_len, scale, nullptr, 0, 0u, ws,
+                     ws ? static_cast<size_t>(PKV_DECODE_NOALLOC_SCRATCH_BYTES) : 0, stream);
 }
 
 }  // extern "C"

@@ -310,3 +310,24 @@ def test_probe_library_exports_and_rejects_bad_arguments():
         st = f(a["buf"], a["bytes"], a["tile"], a["order"], a["tiles"], a["nt"], a["sink"],
                a["wgs"], None)
         assert st == 1, change
+
+
+def test_noalloc_bound_matches_header_and_oversize_is_refused_on_the_host():
+    """The scratch bound of pkv_paged_attention_decode_noalloc is the header's, and a call
+    whose partials exceed it returns PKV_ENOMEM before any device call."""
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    m = re.search(r"#define PKV_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m[1]) << int(m[2]) == pkv.DECODE_NOALLOC_SCRATCH_BYTES
+    lib = pkv.lib()
+    d = _desc(h=40)
+    S, ml = 64, 400_000
+    assert pkv.decode_workspace_bytes(d, S, ml) > pkv.DECODE_NOALLOC_SCRATCH_BYTES
+    args = lambda desc, S, ml, mb: (ctypes.byref(desc) if desc else None, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, mb, FAKE, S, ml, 0.1, None)
+    f = lib.pkv_paged_attention_decode_noalloc
+    assert f(*args(d, S, ml, -(-ml // 16))) == pkv.PKV_ENOMEM
+    assert f(*args(None, S, ml, 10)) == pkv.PKV_EINVAL
+    assert f(*args(_desc(d=96), S, ml, 10)) == pkv.PKV_EUNSUPPORTED
+    assert f(*args(d, -1, ml, 10)) == pkv.PKV_EINVAL
+    assert f(*args(d, S, ml, 0)) == pkv.PKV_EINVAL
+    assert f(*args(d, 0, ml, 10)) == pkv.PKV_OK               # nothing to do

@@ -260,6 +260,14 @@ pkv_status_t pkv_reshape_and_cache(const pkv_cache_desc_t* desc, const void* k, 
                                    void* k_pool, void* v_pool, const int32_t* slot_mapping,
                                    int32_t num_tokens, pkv_stream_t stream);
 
+/* Host check of that precondition, for a caller that holds the slots in host memory (the step
+ * driver runs it on every step's slots before they are uploaded; the binding runs it on a
+ * host copy when PKV_DEBUG=1 is set in the environment): PKV_EINVAL if two slots in
+ * [0, num_blocks * block_size) are equal (slots outside that range are skipped by the kernel
+ * and ignored here), else PKV_OK.  slot_mapping: host, int32 [num_tokens]. */
+pkv_status_t pkv_check_slot_mapping(const pkv_cache_desc_t* desc, const int32_t* slot_mapping,
+                                    int32_t num_tokens);
+
 /* ---------------------------------------------------------------------------------------
  * Copy whole blocks, in every layer, for copy-on-write of shared prefix blocks.
  * ("PagedAttention: Efficient LLM Serving with vLLM", "Advanced Features" ->
@@ -278,6 +286,13 @@ pkv_status_t pkv_reshape_and_cache(const pkv_cache_desc_t* desc, const void* k, 
 pkv_status_t pkv_copy_blocks(const pkv_cache_desc_t* desc, void* const* k_pools,
                              void* const* v_pools, int32_t num_layers, const int32_t* pairs,
                              int32_t num_pairs, pkv_stream_t stream);
+
+/* Host check of those preconditions (run by the step driver on every step's pairs before
+ * they are uploaded, and by the binding on a host copy when PKV_DEBUG=1): PKV_EINVAL if,
+ * among the pairs whose src and dst are both in [0, num_blocks), a destination repeats or is
+ * also a source; else PKV_OK.  pairs: host, int32 [num_pairs][2]. */
+pkv_status_t pkv_check_copy_pairs(const pkv_cache_desc_t* desc, const int32_t* pairs,
+                                  int32_t num_pairs);
 
 /* ---------------------------------------------------------------------------------------
  * Copy blocks between two pools of the same shape -- out of HBM into a pinned host swap pool
@@ -352,6 +367,13 @@ pkv_status_t pkv_alloc_append_slot(pkv_alloc_t* a, int64_t seq, int32_t* slot, i
 pkv_status_t pkv_alloc_append_slots(pkv_alloc_t* a, const int64_t* seqs, int32_t n,
                                     int32_t* slots, int32_t* cow_pairs, int32_t* num_cow,
                                     int32_t* num_done);
+/* The number of blocks append_slots(seqs[0..n-1]) would take from the pool -- one per sequence
+ * that starts a new block, one per copy-on-write of a shared block -- into *blocks (host
+ * out), without changing anything; the same sequence may be listed more than once.  A
+ * scheduler compares it with pkv_alloc_num_free to decide, before a step, whether to preempt
+ * ("vLLM: The Serving Engine").  PKV_EINVAL for an unknown sequence or a null argument. */
+pkv_status_t pkv_alloc_append_need(const pkv_alloc_t* a, const int64_t* seqs, int32_t n,
+                                   int32_t* blocks);
 pkv_status_t pkv_alloc_free_seq(pkv_alloc_t* a, int64_t seq);
 /* Batched forms for a scheduler that starts, forks (beam search, parallel sampling: "KV-Cache
  * Sharing (Copy-on-Write)") or ends many sequences per step with one host call each:
@@ -417,9 +439,33 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *      prologue for layer 0 when there was no copy), then
  *      pkv_paged_attention_decode_scheduled(q[l] -> out[l]) with the lengths including the
  *      new token.
- * Everything after step 1 is asynchronous on `stream`.  If step 1 fails (PKV_ENOMEM: the pool
- * ran out; PKV_EINVAL: unknown sequence) nothing is launched, and the sequences before the
- * failing one have already been extended by one slot (*num_done reports how many).
+ * Everything after step 1 is asynchronous on `stream`.
+ *
+ * Errors.  Before step 1 the call makes every check pkv_stepper_check makes (below) and
+ * returns its error, if any, with nothing changed: the block manager, the pools, the staging
+ * areas and the device index area are as before, nothing is launched and *num_done is 0.  So
+ * the pool running out (PKV_ENOMEM), an unknown or repeated sequence, a context that outgrows
+ * max_blocks_per_seq (PKV_EINVAL) or a workspace too small for the split-context partials of
+ * this step's longest context (PKV_ENOMEM) are reported before any sequence is extended.
+ * After step 1 the slots and copy pairs about to be uploaded are checked with
+ * pkv_check_slot_mapping and pkv_check_copy_pairs; a failure there (PKV_EINVAL) would mean the
+ * block manager broke its own invariants: the sequences are then extended but nothing is
+ * launched.  Only PKV_EHIP (a launch the runtime refused) can come back after a launch.
+ *
+ * pkv_stepper_check(alloc, desc, max_seqs, max_blocks_per_seq, seqs, n, io, workspace,
+ * workspace_bytes, max_len) makes the checks of a step of a stepper created with
+ * (alloc, desc, max_seqs, max_blocks_per_seq), host only, without changing anything: the
+ * descriptor; n <= max_seqs; the io pointers (non-null; pools and new K/V 16-byte aligned;
+ * scale finite); every sequence known and listed once; each one's length after the append
+ * within max_blocks_per_seq * block_size; the blocks the append takes
+ * (pkv_alloc_append_need) within pkv_alloc_num_free; the attention grid within its limits;
+ * the workspace >= pkv_decode_workspace_bytes(desc, n, longest context after the append)
+ * and 16-byte aligned.  *max_len (host out) receives that longest context.
+ *
+ * Streams.  Steps may be issued on different streams: when a step's stream differs from the
+ * previous step's, the new stream first waits for everything the previous stream had queued
+ * (an event of the stepper's own), since the two steps share the staging areas, the device
+ * index area and the split-context workspace.
  *
  * The stepper allocates only pinned host memory and HIP events of its own; the caller owns the
  * device buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned: two areas used by
@@ -455,6 +501,10 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
                               void* const* attn_events, int32_t* max_len, int32_t* num_cow,
                               int32_t* num_done, pkv_stream_t stream);
 const void* pkv_stepper_last_index(const pkv_stepper_t* st);
+pkv_status_t pkv_stepper_check(const pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
+                               int32_t max_seqs, int32_t max_blocks_per_seq, const int64_t* seqs,
+                               int32_t n, const pkv_layer_io_t* io, const void* workspace,
+                               size_t workspace_bytes, int32_t* max_len);
 
 #ifdef __cplusplus
 }

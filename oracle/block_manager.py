@@ -187,6 +187,24 @@ class BlockManager:
                 pairs.append(cow)
         return slots, pairs, len(slots)
 
+    def append_need(self, seqs) -> int:
+        """Blocks ``append_slots(seqs)`` would take from the pool (new blocks at a block
+        boundary, fresh blocks for copy-on-write), found by running it on a copy of this
+        manager that is given one spare block per append, and counting.  ValueError for an
+        unknown sequence."""
+        import copy
+        seqs = [int(s) for s in seqs]
+        if any(s not in self.tables for s in seqs):
+            raise ValueError("bad sequence")
+        twin = copy.deepcopy(self)
+        spare = list(range(self.num_blocks, self.num_blocks + len(seqs)))
+        twin.ref += [0] * len(spare)
+        twin.ident += [0] * len(spare)
+        twin._free = spare[::-1] + twin._free     # used only once the real pool is empty
+        before = twin.num_free()
+        twin.append_slots(seqs)
+        return before - twin.num_free()
+
     def free_seq(self, seq: int) -> None:
         if seq not in self.tables:
             raise ValueError("bad sequence")

@@ -14,7 +14,7 @@ __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
     "decode_schedule",
     "paged_attention_decode", "paged_attention_decode_noalloc", "reshape_and_cache", "copy_blocks", "BlockAllocator",
-    "DecodeStepper", "swap_blocks", "LIB_PATH",
+    "DecodeStepper", "swap_blocks", "check_slot_mapping", "check_copy_pairs", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -67,13 +67,16 @@ _SIGNATURES = {
     "pkv_paged_attention_multi_query": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p, _i32,
                                                _i32, _i32, _i32, _f32, _p, _i32, _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
+    "pkv_check_slot_mapping": (_i32, [_pdesc, _p, _i32]),
     "pkv_copy_blocks": (_i32, [_pdesc, _p, _p, _i32, _p, _i32, _p]),
+    "pkv_check_copy_pairs": (_i32, [_pdesc, _p, _i32]),
     "pkv_alloc_create": (_p, [_i32, _i32, _p]),
     "pkv_alloc_destroy": (None, [_p]),
     "pkv_alloc_add_seq": (_i32, [_p, _i64, _i32]),
     "pkv_alloc_fork": (_i32, [_p, _i64, _i64]),
     "pkv_alloc_append_slot": (_i32, [_p, _i64, _pi32, _pi32, _pi32]),
     "pkv_alloc_append_slots": (_i32, [_p, _p, _i32, _p, _p, _pi32, _pi32]),
+    "pkv_alloc_append_need": (_i32, [_p, _p, _i32, _pi32]),
     "pkv_alloc_free_seq": (_i32, [_p, _i64]),
     "pkv_alloc_add_seqs": (_i32, [_p, _p, _p, _i32, _pi32]),
     "pkv_alloc_fork_many": (_i32, [_p, _p, _p, _i32, _pi32]),
@@ -93,6 +96,7 @@ _SIGNATURES = {
     "pkv_stepper_destroy": (None, [_p]),
     "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
     "pkv_stepper_last_index": (_p, [_p]),
+    "pkv_stepper_check": (_i32, [_p, _pdesc, _i32, _i32, _p, _i32, _p, _p, _sz, _pi32]),
 }
 
 
@@ -321,6 +325,29 @@ def paged_attention_multi_query(out, q, k_pool, v_pool, block_tables, context_le
     return out
 
 
+def _debug_checks() -> bool:
+    """PKV_DEBUG=1: check the preconditions of the device index arrays on a host copy before
+    each launch (synchronizes; for debugging)."""
+    return os.environ.get("PKV_DEBUG", "") == "1"
+
+
+def check_slot_mapping(desc: CacheDesc, slots):
+    """Raise PkvError unless the in-pool slots (host int32 array) are distinct."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+    _check(_lib().pkv_check_slot_mapping(ctypes.byref(desc), a.ctypes.data_as(ctypes.c_void_p),
+                                         int(a.shape[0])), "pkv_check_slot_mapping")
+
+
+def check_copy_pairs(desc: CacheDesc, pairs):
+    """Raise PkvError unless the in-pool (src, dst) pairs (host int32 [n][2]) have distinct
+    destinations that are never also sources."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    _check(_lib().pkv_check_copy_pairs(ctypes.byref(desc), a.ctypes.data_as(ctypes.c_void_p),
+                                       int(a.shape[0])), "pkv_check_copy_pairs")
+
+
 def reshape_and_cache(k, v, k_pool, v_pool, slot_mapping, stream=None):
     """Write token i's K/V rows into slot slot_mapping[i] of the pools (include/pkv.h)."""
     import torch
@@ -330,6 +357,8 @@ def reshape_and_cache(k, v, k_pool, v_pool, slot_mapping, stream=None):
         raise ValueError("k/v shape mismatch")
     if slot_mapping.shape != (N,):
         raise ValueError("slot_mapping shape mismatch")
+    if _debug_checks():
+        check_slot_mapping(desc, slot_mapping.cpu().numpy())
     st = _lib().pkv_reshape_and_cache(
         ctypes.byref(desc), _dev(k, "k", k_pool.dtype), _dev(v, "v", k_pool.dtype),
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
@@ -350,6 +379,8 @@ def copy_blocks(k_pools, v_pools, pairs, stream=None):
     n = pairs.shape[0] if pairs.numel() else 0
     if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
         raise ValueError("pairs must be [n][2]")
+    if _debug_checks() and n:
+        check_copy_pairs(desc, pairs.cpu().numpy())
     L = len(k_pools)
     kp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in k_pools])
     vp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in v_pools])
@@ -498,6 +529,16 @@ class BlockAllocator:
                                        tables.shape[1], tables.ctypes.data_as(ctypes.c_void_p),
                                        lens.ctypes.data_as(ctypes.c_void_p)), "pkv_alloc_export")
 
+    def append_need(self, seqs) -> int:
+        """Blocks ``append_slots(seqs)`` would take from the pool; nothing changes."""
+        import numpy as np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        need = _i32()
+        _check(_lib().pkv_alloc_append_need(self._h, seqs.ctypes.data_as(ctypes.c_void_p),
+                                            int(seqs.shape[0]), ctypes.byref(need)),
+               "pkv_alloc_append_need")
+        return need.value
+
     def free_seq(self, seq: int):
         _check(_lib().pkv_alloc_free_seq(self._h, seq), "pkv_alloc_free_seq")
 
@@ -638,11 +679,10 @@ class DecodeStepper:
                                      ctypes.byref(self._max_len), ctypes.byref(self._ncow),
                                      ctypes.byref(self._ndone), _stream_ptr(stream))
         if st != PKV_OK:
+            # every error but a refused launch leaves the block manager and pools unchanged
             err = PkvError(st, "pkv_stepper_step")
             err.num_done = self._ndone.value
             raise err
-        if self._max_len.value > self.max_context_len:
-            raise PkvError(PKV_ENOMEM, "pkv_stepper_step (context grew past the workspace bound)")
         return self._max_len.value, self._ncow.value
 
     def index_views(self, n: int, num_cow: int, num_items: int = 0):

@@ -16,7 +16,7 @@ PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["pkv_decode.hip", "pkv_multi_query.hip", "pkv_cache_ops.hip", "pkv_step.hip"]
-CXX_SOURCES = ["pkv_alloc.cpp"]
+CXX_SOURCES = ["pkv_alloc.cpp", "pkv_step_check.cpp"]
 PROBE_SOURCES = ["pkv_probe.hip"]
 # Per-source hipcc flags.  The multi-query kernel keeps its MFMA accumulators in ordinary
 # VGPRs (gfx950 MFMAs take C/D there too): with the accumulation-register form the compiler

@@ -40,38 +40,24 @@
 
 namespace pkv {
 
-// Compile-time tuning knobs; the defaults measured best on MI355X: waves per workgroup (4:
-// three workgroups per CU at 167 VGPRs), tokens per partition of a long sequence, the longest
-// sequence attended in one pass, K bytes per wave per chunk, and the two-deep load pipeline
-// (0 gives the plain loop, kept for comparison).
-#ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
-#endif
-#ifndef PKV_PART_TOKENS
-#define PKV_PART_TOKENS 2048
-#endif
-#ifndef PKV_SINGLE_MAX
-#define PKV_SINGLE_MAX 4096
-#endif
-#ifndef PKV_CHUNK_BYTES
-#define PKV_CHUNK_BYTES 8192
-#endif
-#ifndef PKV_PIPELINE
-#define PKV_PIPELINE 1
-#endif
-
-constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+// Tuning constants, the values that measured best on MI355X: waves per workgroup (4: three
+// workgroups per CU at 167 VGPRs), tokens per partition of a long sequence, the longest
+// sequence attended in one pass, and K bytes per wave per chunk.
+constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
+constexpr int kPartTokens = 2048;
+constexpr int kSingleMax = 4096;
+constexpr int kChunkBytesPerWave = 8192;
 // Longest run of tokens one workgroup attends: bounds the LDS copy of its block ids.
 constexpr int kMaxPartTokens = 4096;
-static_assert(PKV_PART_TOKENS <= kMaxPartTokens && PKV_SINGLE_MAX <= kMaxPartTokens, "part");
+static_assert(kPartTokens <= kMaxPartTokens && kSingleMax <= kMaxPartTokens, "part");
 
 template <class Ty, int D, int BS>
 struct DecodeCfg {
   static constexpr int kEPL = 16 / Ty::kBytes;         // elements per lane per 16-byte load
   static constexpr int kLPT = D / kEPL;                // lanes per token row
   static constexpr int kTPL = 64 / kLPT;               // token rows per wave-wide load
-  static constexpr int kChunkBytes = PKV_CHUNK_BYTES;  // K bytes per wave per iteration
+  static constexpr int kChunkBytes = kChunkBytesPerWave;  // K bytes per wave per iteration
   static constexpr int kChunkByBytes = kChunkBytes / (D * Ty::kBytes);
   static constexpr int kChunk = kChunkByBytes > BS ? kChunkByBytes : BS;  // tokens
   static constexpr int kBlocksPerChunk = kChunk / BS;
@@ -85,7 +71,6 @@ struct DecodeCfg {
 
 // A sequence of at most kSingleMax tokens is attended by one workgroup per head; a longer
 // one is cut into partitions of part_tokens tokens whose partial results are merged.
-constexpr int kSingleMax = PKV_SINGLE_MAX;
 __host__ __device__ __forceinline__ int partition_len(int L, int part_tokens) {
   return L <= kSingleMax ? (L > 0 ? L : 1) : part_tokens;
 }
@@ -242,7 +227,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   };
   constexpr int kStride = kDecodeWaves * C::kChunk;
   if (t1 > t0) {
-#if PKV_PIPELINE
     // Software pipeline over this wave's chunks c(k) = first + k * kStride, k < n: the loads
     // of chunk k+1 are in flight while chunk k is folded.  The loop body issues
     // unconditionally so the compiler waits only for the older chunk's loads.
@@ -268,13 +252,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
         consume(c, ka, va);
       }
     }
-#else
-    for (int c0 = t0 + wave * C::kChunk; c0 < t1; c0 += kStride) {
-      u32x4 kr[C::kLoads], vr[C::kLoads];
-      issue(c0, kr, vr);
-      consume(c0, kr, vr);
-    }
-#endif
   }
 
   // ---- merge the kStates (wave, row) states of this workgroup
@@ -342,7 +319,6 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int kPartTokens = PKV_PART_TOKENS;
 
 static int effective_max_len(int32_t max_context_len, int32_t max_blocks, int32_t block_size) {
   const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;

@@ -3,6 +3,8 @@
 
 #include <stdint.h>
 
+#include <vector>
+
 #include "pkv.h"
 
 namespace pkv {
@@ -42,5 +44,13 @@ pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, con
                                     const int32_t* work_items, int32_t num_items, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, pkv_stream_t stream,
                                     void* ev_start, void* ev_stop);
+
+// Host checks of a cache append's slots (distinct within [0, num_slots); others are skipped)
+// and of a block copy's pairs (among in-range pairs, destinations distinct and never a
+// source).  `scratch` is reused between calls to avoid allocating.
+bool slots_distinct(const int32_t* slots, int32_t n, int64_t num_slots,
+                    std::vector<int32_t>& scratch);
+bool copy_pairs_valid(const int32_t* pairs, int32_t n, int32_t num_blocks,
+                      std::vector<int64_t>& scratch);
 
 }  // namespace pkv

@@ -50,22 +50,13 @@ namespace {
 // faster at fp16 and 1.5% at bf16 (each change alone was not faster).  Two tiles per wave
 // (each K/V fragment feeding two products) halves the LDS bytes per flop but needs 184 VGPRs
 // and two waves per SIMD; it tied or lost.  All shapes give bit-identical outputs.
-#ifndef PKV_MQ_WAVES
-#define PKV_MQ_WAVES 8
-#endif
-#ifndef PKV_MQ_WAVE_TILES
-#define PKV_MQ_WAVE_TILES 1
-#endif
-constexpr int kMqWaves = PKV_MQ_WAVES;          // waves per workgroup
-constexpr int kMqQt = PKV_MQ_WAVE_TILES;        // 16-query MFMA tiles per wave
+constexpr int kMqWaves = 8;                                 // waves per workgroup
+constexpr int kMqQt = 1;                                    // 16-query MFMA tiles per wave
 constexpr int kMqThreads = 64 * kMqWaves;
 constexpr int kMqWaveQueries = 16 * kMqQt;
 constexpr int kMqTileQueries = kMqWaves * kMqWaveQueries;   // new tokens per workgroup
 constexpr int kMqChunk = 32;                                // keys per compute step
-#ifndef PKV_MQ_SUB
-#define PKV_MQ_SUB 2
-#endif
-constexpr int kMqSub = PKV_MQ_SUB;                          // compute steps per LDS stage
+constexpr int kMqSub = 2;                                   // compute steps per LDS stage
 constexpr int kMqStage = kMqChunk * kMqSub;                 // keys staged per barrier
 constexpr float kMqSlack = 8.0f;  // log2 units a score may exceed the softmax reference by
 constexpr int kMqItemSeqBits = 20;                          // work item = sequence | tile << 20

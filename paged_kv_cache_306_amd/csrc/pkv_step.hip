@@ -94,6 +94,13 @@ struct pkv_stepper {
   int32_t max_blocks = 0;
   int32_t max_items = 0;                   // decode work items per step, at most
   std::vector<int32_t> keys, sorted_keys;  // per-step scratch for the sharing test
+  std::vector<int32_t> slot_scratch;       // per-step scratch for the index-data checks
+  std::vector<int64_t> pair_scratch;
+  // The stream of the last step that launched work, and an event that hands the shared areas
+  // (staging, device index area, workspace) over when a step comes on another stream.
+  hipStream_t last_stream = nullptr;
+  bool launched = false;
+  hipEvent_t handoff = nullptr;
   struct Stage {
     int32_t* host = nullptr;        // pinned: tables | lens | slots | pairs | items
     const char* host_dev = nullptr; // the same memory as the device sees it
@@ -140,6 +147,11 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
     }
     sg.host_dev = static_cast<const char*>(dptr);
   }
+  if (hipEventCreateWithFlags(&st->handoff, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    pkv_stepper_destroy(st);
+    return nullptr;
+  }
   return st;
 }
 
@@ -152,6 +164,7 @@ void pkv_stepper_destroy(pkv_stepper_t* st) {
     }
     if (sg.host) (void)hipHostFree(sg.host);
   }
+  if (st->handoff) (void)hipEventDestroy(st->handoff);
   delete st;
 }
 
@@ -165,44 +178,57 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   *max_len = 0;
   *num_cow = 0;
   *num_done = 0;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   if (n == 0) {
     // nothing to attend: timing events, if any, are recorded back to back (zero duration)
     if (attn_events)
       for (int64_t e = 0; e < 2 * static_cast<int64_t>(io->num_layers); ++e)
-        if (attn_events[e] && hipEventRecord(static_cast<hipEvent_t>(attn_events[e]),
-                                              static_cast<hipStream_t>(stream)) != hipSuccess)
+        if (attn_events[e] && hipEventRecord(static_cast<hipEvent_t>(attn_events[e]), hs) !=
+                                  hipSuccess)
           return PKV_EHIP;
     return PKV_OK;
   }
+  // Every check that can fail comes before anything changes: arguments, sequences, table
+  // width, pool capacity, workspace.
+  int32_t expect_len = 0;
+  pkv_status_t s = pkv_stepper_check(st->alloc, &st->desc, st->max_seqs, st->max_blocks, seqs,
+                                     n, io, workspace, workspace_bytes, &expect_len);
+  if (s != PKV_OK) return s;
   const int32_t L = io->num_layers;
-  if (L > 0 && (!io->k_pools || !io->v_pools || !io->q || !io->k_new || !io->v_new || !io->out))
-    return PKV_EINVAL;
-  for (int32_t l = 0; l < L; ++l)
-    if (!io->k_pools[l] || !io->v_pools[l] || !io->k_new[l] || !io->v_new[l] ||
-        reinterpret_cast<uintptr_t>(io->k_new[l]) % 16 ||
-        reinterpret_cast<uintptr_t>(io->v_new[l]) % 16 ||
-        reinterpret_cast<uintptr_t>(io->k_pools[l]) % 16 ||
-        reinterpret_cast<uintptr_t>(io->v_pools[l]) % 16)
-      return PKV_EINVAL;
 
-  st->cur ^= 1;
-  auto& sg = st->stage[st->cur];
+  auto& sg = st->stage[st->cur ^ 1];
   if (sg.pending) {
     // the prologue that read this host area two steps ago must be done with it
     if (hipEventSynchronize(sg.read) != hipSuccess) return PKV_EHIP;
     sg.pending = false;
   }
+  // A step on another stream than the last one first waits for all the last stream queued:
+  // the two share the staging areas, the device index area and the workspace.
+  (void)hipGetLastError();
+  if (st->launched && hs != st->last_stream &&
+      (hipEventRecord(st->handoff, st->last_stream) != hipSuccess ||
+       hipStreamWaitEvent(hs, st->handoff, 0) != hipSuccess))
+    return PKV_EHIP;
+  st->cur ^= 1;
+
   const int32_t MB = st->max_blocks;
   int32_t* tables = sg.host;
   int32_t* lens = tables + static_cast<size_t>(n) * MB;
   int32_t* slots = lens + n;
   int32_t* pairs = slots + n;
 
-  pkv_status_t s = pkv_alloc_append_slots(st->alloc, seqs, n, slots, pairs, num_cow, num_done);
+  // cannot fail after the checks above (sequences known, room in the pool and the table)
+  s = pkv_alloc_append_slots(st->alloc, seqs, n, slots, pairs, num_cow, num_done);
   if (s != PKV_OK) return s;
   s = pkv_alloc_export(st->alloc, seqs, n, MB, tables, lens);
   if (s != PKV_OK) return s;
   *max_len = *std::max_element(lens, lens + n);
+  // the block manager's own guarantees, checked on what is about to be uploaded
+  if (*max_len != expect_len ||
+      !pkv::slots_distinct(slots, n, static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size,
+                           st->slot_scratch) ||
+      !pkv::copy_pairs_valid(pairs, *num_cow, st->desc.num_blocks, st->pair_scratch))
+    return PKV_EINVAL;
   // Sequences whose first physical block is the same share a prefix: schedule them side by
   // side and read K/V with cache-allocating loads; otherwise longest first, nontemporal.
   st->keys.resize(static_cast<size_t>(n));
@@ -234,8 +260,6 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int64_t append_wgs = (total_vecs + kPrologueThreads - 1) / kPrologueThreads;
   if (copy_wgs + append_wgs > INT32_MAX) return PKV_EUNSUPPORTED;
 
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
   const int32_t* slots_host_dev =
       reinterpret_cast<const int32_t*>(sg.host_dev) + static_cast<size_t>(n) * MB + n;
   // The marker that frees this staging area is the prologue launch's own completion (the
@@ -255,6 +279,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size);
   if (hipGetLastError() != hipSuccess) return PKV_EHIP;
   sg.pending = true;
+  st->launched = true;
+  st->last_stream = hs;
 
   const int32_t* d_tables = reinterpret_cast<const int32_t*>(sg.dev);
   const int32_t* d_lens = d_tables + static_cast<size_t>(n) * MB;

@@ -1,7 +1,8 @@
 // Randomized stress of the host block manager through its C ABI, built with AddressSanitizer
 // and UndefinedBehaviorSanitizer by tests/test_alloc_sanitized.py.  After every operation:
 // the sum of reference counts equals the number of table entries, free + used = pool size,
-// and every table holds ceil(len / block_size) valid ids.
+// and every table holds ceil(len / block_size) valid ids; an append batch takes exactly the
+// blocks pkv_alloc_append_need predicted, and fails for lack of blocks exactly when it said so.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -97,11 +98,19 @@ int main(int argc, char** argv) {
     } else {
       const int32_t n = static_cast<int32_t>(std::min<size_t>(live.size(), 1 + rng() % 6));
       std::vector<int64_t> seqs(live.begin(), live.begin() + n);
-      std::vector<int32_t> slots(n), pairs(2 * n);
-      int32_t ncow = -1, ndone = -1;
+      if (rng() % 3 == 0) seqs.push_back(seqs[0]);  // a sequence listed twice
+      const int32_t m = static_cast<int32_t>(seqs.size());
+      std::vector<int32_t> slots(m), pairs(2 * m);
+      int32_t need = -1, ncow = -1, ndone = -1;
+      if (pkv_alloc_append_need(a, seqs.data(), m, &need) != PKV_OK || need < 0 || need > m)
+        return fail("append_need", step);
+      const int32_t free_before = pkv_alloc_num_free(a);
       pkv_status_t st =
-          pkv_alloc_append_slots(a, seqs.data(), n, slots.data(), pairs.data(), &ncow, &ndone);
+          pkv_alloc_append_slots(a, seqs.data(), m, slots.data(), pairs.data(), &ncow, &ndone);
       if (st != PKV_OK && st != PKV_ENOMEM) return fail("append status", step);
+      if ((st == PKV_OK) != (need <= free_before)) return fail("append_need vs ENOMEM", step);
+      if (st == PKV_OK && free_before - pkv_alloc_num_free(a) != need)
+        return fail("append_need vs blocks taken", step);
       for (int32_t i = 0; i < ndone; ++i)
         if (slots[i] < 0 || slots[i] >= NB * BS) return fail("slot range", step);
       for (int32_t i = 0; i < ncow; ++i)

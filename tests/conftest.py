@@ -20,13 +20,19 @@ def pytest_terminal_summary(terminalreporter):
     if not rows:
         return
     agg = {}
-    for test, dtype, n, err, ulps in rows:
-        a = agg.setdefault((test, dtype), [0, 0.0, 0.0])
+    for test, dtype, n, err, ulps, kerr, exact in rows:
+        a = agg.setdefault((test, dtype), [0, 0.0, 0.0, 0.0, 0.0])
         a[0] += n
-        a[1], a[2] = max(a[1], err), max(a[2], ulps)
+        a[1], a[2], a[3] = max(a[1], err), max(a[2], ulps), max(a[3], kerr)
+        a[4] += exact * n
     tr = terminalreporter
     tr.section("parity errors vs the float64 oracle")
-    tr.write_line(f"{'test':64s} {'dtype':5s} {'elements':>10s} {'max abs':>9s} {'max ulp':>8s}")
-    for (test, dtype), (n, err, ulps) in agg.items():
+    tr.write_line("elements: outputs compared; max abs: |gpu - oracle|; max ulp: in output ulps; "
+                  "kernel err: distance from the oracle to the reals that round to the gpu "
+                  "output; =RNE: share of outputs equal to the oracle rounded to nearest even")
+    tr.write_line(f"{'test':60s} {'dtype':5s} {'elements':>10s} {'max abs':>9s} {'max ulp':>8s} "
+                  f"{'kernel err':>10s} {'=RNE':>7s}")
+    for (test, dtype), (n, err, ulps, kerr, exact) in agg.items():
         name = test.split("::", 1)[-1]
-        tr.write_line(f"{name[:64]:64s} {dtype:5s} {n:10d} {err:9.3g} {ulps:8.1f}")
+        tr.write_line(f"{name[:60]:60s} {dtype:5s} {n:10d} {err:9.3g} {ulps:8.1f} {kerr:10.3g} "
+                      f"{exact / max(n, 1):7.4f}")

@@ -331,3 +331,109 @@ def test_noalloc_bound_matches_header_and_oversize_is_refused_on_the_host():
     assert f(*args(d, -1, ml, 10)) == pkv.PKV_EINVAL
     assert f(*args(d, S, ml, 0)) == pkv.PKV_EINVAL
     assert f(*args(d, 0, ml, 10)) == pkv.PKV_OK               # nothing to do
+
+
+def test_host_checks_of_slots_and_copy_pairs():
+    """Distinct slots per append; copy destinations distinct and never a source (both among
+    in-pool entries only: out-of-pool entries are skipped by the kernels)."""
+    import numpy as np
+    d = _desc(nb=8, bs=16)                       # slots 0..127
+    pkv.check_slot_mapping(d, np.array([3, 17, 127, 0, -1, -5, 128, 128], np.int32))
+    pkv.check_slot_mapping(d, np.zeros(0, np.int32))
+    for bad in ([3, 17, 3], [127, 0, 127], [5, -1, 5]):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.check_slot_mapping(d, np.array(bad, np.int32))
+        assert e.value.status == pkv.PKV_EINVAL
+    # one shared source copied to several fresh blocks (copy-on-write of a shared block): fine
+    pkv.check_copy_pairs(d, [[2, 5], [2, 6], [2, 7], [1, 4]])
+    pkv.check_copy_pairs(d, [[2, 5], [9, 5], [5, -1]])   # the pairs naming block 9 / -1 are skipped
+    for bad in ([[2, 5], [3, 5]],            # destination repeated
+                [[2, 5], [5, 6]],            # a destination is also a source
+                [[4, 4]]):                   # a block copied onto itself
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.check_copy_pairs(d, bad)
+        assert e.value.status == pkv.PKV_EINVAL
+    lib = pkv.lib()
+    assert lib.pkv_check_slot_mapping(None, FAKE, 1) == pkv.PKV_EINVAL
+    assert lib.pkv_check_slot_mapping(ctypes.byref(d), None, 1) == pkv.PKV_EINVAL
+    assert lib.pkv_check_copy_pairs(ctypes.byref(d), None, 1) == pkv.PKV_EINVAL
+    assert lib.pkv_check_copy_pairs(ctypes.byref(d), None, 0) == pkv.PKV_OK
+
+
+def _alloc_state(a, seqs):
+    return (a.num_free(), a.wasted_slots(), [a.block_table(s) for s in seqs],
+            [a.seq_len(s) for s in seqs], [a.refcount(b) for b in range(a.num_blocks)])
+
+
+def test_stepper_check_reports_every_error_before_anything_changes():
+    """The checks pkv_stepper_step makes before step 1, host only: each error is reported and
+    the block manager is left exactly as it was."""
+    import numpy as np
+    lib = pkv.lib()
+    H, BS, D, NB, L = 4, 16, 128, 12, 2
+    d = pkv.CacheDesc(NB, H, BS, D, 1)
+    a = pkv.BlockAllocator(NB, BS, free_order=np.arange(NB)[::-1])
+    a.add_seq(0, 40)        # 3 blocks, last one partly filled
+    a.add_seq(1, 32)        # 2 full blocks: the next token starts a third
+    a.fork(0, 2)            # shares sequence 0's partial block: its append copies it
+    live = [0, 1, 2]
+    aligned = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(6 * L)]
+    arrs = [(ctypes.c_void_p * L)(*aligned[k * L:(k + 1) * L]) for k in range(6)]
+
+    def io(scale=0.1, layers=L, arrays=arrs):
+        return pkv.LayerIO(layers, *[ctypes.cast(x, ctypes.c_void_p) for x in arrays], scale)
+
+    def check(seqs, io_=None, ws=None, wsb=0, max_seqs=8, mb=8, desc=d):
+        seqs = np.asarray(seqs, np.int64)
+        ml = ctypes.c_int32(-7)
+        st = lib.pkv_stepper_check(a._h, ctypes.byref(desc) if desc else None, max_seqs, mb,
+                                   seqs.ctypes.data_as(ctypes.c_void_p), len(seqs),
+                                   ctypes.byref(io_ or io()), ws, wsb, ctypes.byref(ml))
+        return st, ml.value
+
+    before = _alloc_state(a, live)
+    assert check([0, 1, 2]) == (pkv.PKV_OK, 41)
+    assert a.append_need([0, 1, 2]) == 2          # sequence 1's new block + one copy
+    assert check([0, 1, 5])[0] == pkv.PKV_EINVAL  # unknown sequence
+    assert check([0, 1, 0])[0] == pkv.PKV_EINVAL  # listed twice
+    assert check([0, 1, 2], max_seqs=2)[0] == pkv.PKV_EINVAL
+    assert check([0, 1, 2], mb=2)[0] == pkv.PKV_EINVAL       # 41 tokens need 3 blocks
+    assert check([0, 1, 2], desc=None)[0] == pkv.PKV_EINVAL
+    assert check([0, 1, 2], desc=pkv.CacheDesc(NB, H, 12, D, 1))[0] == pkv.PKV_EUNSUPPORTED
+    assert check([0, 1, 2], io(scale=float("nan")))[0] == pkv.PKV_EINVAL
+    bad = [list(x) for x in arrs]
+    bad[0][1] = None                                          # a null pool
+    assert check([0], io(arrays=[(ctypes.c_void_p * L)(*x) for x in bad]))[0] == pkv.PKV_EINVAL
+    bad = [list(x) for x in arrs]
+    bad[3][0] = 0x10008                                       # new K not 16-byte aligned
+    assert check([0], io(arrays=[(ctypes.c_void_p * L)(*x) for x in bad]))[0] == pkv.PKV_EINVAL
+    assert check([0], io(layers=0, arrays=[None] * 6))[0] == pkv.PKV_OK   # no layers: no I/O
+    # the pool runs out: with 11 of 12 blocks in use, three sequences that each start a new
+    # block need 3
+    for s, n in ((3, 64), (4, 32)):
+        a.add_seq(s, n)
+        live.append(s)
+    before = _alloc_state(a, live)                 # 11 in use, 1 free
+    assert a.num_free() == 1 and a.append_need([1, 3, 4]) == 3
+    assert check([1, 3, 4])[0] == pkv.PKV_ENOMEM
+    assert check([1])[0] == pkv.PKV_OK
+    # a context long enough to split needs a workspace of the right size, 16-byte aligned
+    big = lib.pkv_decode_single_pass_max() + 100
+    a2 = pkv.BlockAllocator(400, BS)
+    a2.add_seq(7, big)
+    mb = -(-(big + 1) // BS)
+    need = pkv.decode_workspace_bytes(pkv.CacheDesc(400, H, BS, D, 1), 1, big + 1)
+    assert need > 0
+
+    def check2(ws, wsb):
+        ml = ctypes.c_int32()
+        seqs = np.array([7], np.int64)
+        return lib.pkv_stepper_check(a2._h, ctypes.byref(pkv.CacheDesc(400, H, BS, D, 1)), 1, mb,
+                                     seqs.ctypes.data_as(ctypes.c_void_p), 1, ctypes.byref(io()),
+                                     ws, wsb, ctypes.byref(ml))
+    assert check2(None, 0) == pkv.PKV_ENOMEM
+    assert check2(FAKE, need - 1) == pkv.PKV_ENOMEM
+    assert check2(ctypes.c_void_p(0x1008), need) == pkv.PKV_EINVAL
+    assert check2(FAKE, need) == pkv.PKV_OK
+    assert _alloc_state(a, live) == before
+    assert a2.seq_len(7) == big

@@ -315,3 +315,82 @@ def test_move_seqs_matches_the_model(seed):
         live_cpu = [s for r in groups if where[r] == "cpu" for s in groups[r]]
         _same_state(a_gpu, m_gpu, live_gpu)
         _same_state(a_cpu, m_cpu, live_cpu)
+
+
+def test_append_need_worked_examples():
+    """Blocks an append batch takes, worked by hand ("KV-Cache Sharing (Copy-on-Write)": a
+    shared block is copied for every writer but the last, which writes in place)."""
+    for mk in (lambda: pkv.BlockAllocator(64, 16), lambda: oracle.BlockManager(64, 16)):
+        a = mk()
+        a.add_seq(0, 40)                   # 3 blocks, 8 tokens in the last
+        for c in range(1, 8):
+            a.fork(0, c)                   # 8 holders of the partial block
+        assert a.append_need(list(range(8))) == 7
+        assert a.append_need([3]) == 1 and a.append_need([3, 5]) == 2
+        a.add_seq(10, 32)                  # full: its next token starts a block
+        assert a.append_need([10]) == 1
+        a.add_seq(11, 31)                  # one free slot, then a new block
+        assert a.append_need([11]) == 0 and a.append_need([11, 11]) == 1
+        assert a.append_need([11, 11, 11]) == 1
+        assert a.append_need([2, 2]) == 1  # the copy is private: the second write is in place
+        assert a.append_need([]) == 0
+        free = a.num_free()
+        assert free == 64 - 3 - 2 - 2
+    with pytest.raises(pkv.PkvError):
+        pkv.BlockAllocator(8, 16).append_need([99])
+    with pytest.raises(ValueError):
+        oracle.BlockManager(8, 16).append_need([99])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_append_need_matches_the_model_and_the_blocks_taken(seed):
+    """pkv_alloc_append_need against the model's count (an append run on a copy), and against
+    the blocks a real append then takes, over random adds, forks, cached prompts, frees and
+    batches that list a sequence more than once."""
+    g = W.rng(500 + seed)
+    NB, BS = 80, int(g.choice([8, 16, 32]))
+    order = g.permutation(NB)
+    a = pkv.BlockAllocator(NB, BS, free_order=order)
+    m = oracle.BlockManager(NB, BS, free_order=order)
+    live, next_id, checked = [], 0, 0
+    for _ in range(300):
+        op = g.random()
+        if op < 0.15 or not live:
+            L = int(g.integers(0, 3 * BS))
+            if -(-L // BS) <= m.num_free():
+                if g.random() < 0.5:
+                    toks = g.integers(0, 2, size=L).astype(np.int32)   # prefixes repeat
+                    assert a.add_seq_cached(next_id, toks) == m.add_seq_cached(next_id, toks)
+                else:
+                    a.add_seq(next_id, L)
+                    m.add_seq(next_id, L)
+                live.append(next_id)
+            next_id += 1
+        elif op < 0.35:
+            p = int(g.choice(live))
+            a.fork(p, next_id)
+            m.fork(p, next_id)
+            live.append(next_id)
+            next_id += 1
+        elif op < 0.45:
+            s = int(live.pop(int(g.integers(len(live)))))
+            a.free_seq(s)
+            m.free_seq(s)
+        else:
+            batch = [int(x) for x in g.choice(live, size=int(g.integers(1, 7)), replace=True)]
+            need = a.append_need(batch)
+            assert need == m.append_need(batch), batch
+            if need <= m.num_free():
+                free = a.num_free()
+                slots, pairs = a.append_slots(batch)
+                mslots, mpairs, _ = m.append_slots(batch)
+                assert slots.tolist() == mslots
+                assert free - a.num_free() == need     # exactly the blocks it said
+                checked += 1
+            else:
+                with pytest.raises(pkv.PkvError):
+                    a.append_slots(batch)
+                _, _, done = m.append_slots(batch)
+                assert done < len(batch)
+        _same_state(a, m, live)
+    assert checked > 50

@@ -64,8 +64,9 @@ def kernel_source_hash(sources=None) -> str:
 
 
 def measured_traffic(profile=COUNTER_PROFILE, sources=None):
-    """Scaled HBM bytes per launch from a committed counter profile, or None when there is
-    none or it was taken on different kernel sources."""
+    """Scaled HBM bytes per launch from a committed counter profile, with the counter scale
+    factors and what they were calibrated on, or None when there is no profile or it was
+    taken on different kernel sources."""
     try:
         with open(profile) as f:
             lines = f.read().splitlines()
@@ -79,9 +80,15 @@ def measured_traffic(profile=COUNTER_PROFILE, sources=None):
     if fields.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        out = {"bytes": int(fields["traffic_bytes_per_launch"])}
     except (KeyError, ValueError):
         return None
+    for k in ("fetch_scale", "write_scale"):
+        if k in fields:
+            out[k] = float(fields[k])
+    if "calibration" in fields:
+        out["calibration"] = fields["calibration"]
+    return out
 
 
 GROWTH = 64   # tokens a sequence grows before it is replaced
@@ -104,7 +111,7 @@ def parse():
                     help="host-only: KV blocks saved by the prefix cache on a chat workload")
     ap.add_argument("--sweep", action="store_true",
                     help="block size x placement sweep of the llama13b_layer and long_context "
-                         "workloads: one JSON line per configuration")
+                         "workloads, 3 interleaved rounds: one JSON line per configuration")
     ap.add_argument("--dtype", choices=("f16", "bf16"), default="f16",
                     help="storage type of the prefix_hit workload")
     ap.add_argument("--flush-mall", action="store_true",
@@ -121,6 +128,9 @@ def parse():
                          "contiguous stream and whole 2/4/8 KiB tiles in random order")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
+    ap.add_argument("--calibrate-read", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain nontemporal reads of MIB MiB with the probe library "
+                         "(to scale the FETCH_SIZE counter)")
     return ap.parse_args()
 
 
@@ -135,6 +145,96 @@ def gc_paused():
         yield
     finally:
         gc.enable()
+
+
+def hip_runtime():
+    """The HIP runtime this process already uses (torch's), found among the loaded objects, so
+    that events created here are valid in torch's and libpkv's calls."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    with open("/proc/self/maps") as f:
+        paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln})
+    if not paths:
+        raise RuntimeError("no HIP runtime loaded")
+    hip = ctypes.CDLL(paths[0])
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    return hip
+
+
+# hipEventDisableSystemFence: the event's completion does not write back and invalidate the
+# caches for the host's sake -- timing needs none of that, and the flush would otherwise sit
+# between the timed kernel and the next one.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvents:
+    """steps x pairs of HIP timing events (start, stop) for the step driver's attention
+    launches, which record them themselves (their own start and end).  ``fence`` False creates
+    them with hipEventDisableSystemFence."""
+
+    def __init__(self, steps: int, pairs: int, fence: bool = False):
+        import ctypes
+        self.hip = hip_runtime()
+        flags = 0 if fence else HIP_EVENT_DISABLE_SYSTEM_FENCE
+        self.handles = []
+        for _ in range(steps):
+            arr = (ctypes.c_void_p * (2 * pairs))()
+            for e in range(2 * pairs):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), flags) != 0:
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                arr[e] = ev.value
+            self.handles.append(arr)
+        self.pairs = pairs
+        # record every event once so that a pair is never read before it was taken
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+        for arr in self.handles:
+            for e in range(2 * pairs):
+                self.hip.hipEventRecord(ctypes.c_void_p(arr[e]), ctypes.c_void_p(stream))
+
+    def elapsed_ms(self):
+        """Every pair's duration in ms (after the work has finished), step-major."""
+        import ctypes
+        out = []
+        ms = ctypes.c_float()
+        for arr in self.handles:
+            for l in range(self.pairs):
+                if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(arr[2 * l]),
+                                                ctypes.c_void_p(arr[2 * l + 1])) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                out.append(ms.value)
+        return out
+
+    def destroy(self):
+        import ctypes
+        for arr in self.handles:
+            for e in range(2 * self.pairs):
+                self.hip.hipEventDestroy(ctypes.c_void_p(arr[e]))
+        self.handles = []
+
+
+def calibrate_read(mib: int):
+    """Five plain nontemporal reads of a device buffer of MIB MiB by the probe library (the
+    decode kernel's load form, each byte once): FETCH_SIZE of this run over the bytes read
+    gives the counter's scale factor for reads."""
+    import torch
+    probe = load_probe()
+    if probe is None:
+        raise RuntimeError("libpkv_probe.so is not built")
+    n = mib << 20
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(5):
+        if probe(buf.data_ptr(), n, 0, None, 0, 1, sink.data_ptr(), 4096, stream) != 0:
+            raise RuntimeError("pkv_probe_read failed")
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_read_bytes": n, "reads": 5}), flush=True)
 
 
 def calibrate_copy(mib: int):
@@ -389,7 +489,14 @@ class DecodeBatch:
         else:
             for s in range(self.S):
                 self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
-        self.cur_len = self.init_lens.copy()
+        # Every sequence of a batch grows one token per step and all are replaced together, so
+        # one counter (tokens grown since the last replacement) describes every length; the
+        # per-step byte counts are tabulated by it once, outside the timed steps.
+        self.grown = 0
+        g = np.arange(self.growth + 2)[:, None]
+        lens_by_grown = self.init_lens[None, :] + g
+        self.tot_by_grown = lens_by_grown.sum(axis=1)
+        self.nblk_by_grown = ((lens_by_grown + self.BS - 1) // self.BS).sum(axis=1)
 
         shape = (self.NB, self.H, self.BS, self.D)
         tensors = {k: [] for k in ("kp", "vp", "q", "kn", "vn", "out")}
@@ -430,17 +537,22 @@ class DecodeBatch:
         if tail:
             self.alloc.append_slots(np.full(tail, sid, np.int64))
 
+    @property
+    def cur_len(self):
+        return self.init_lens + self.grown
+
     def recycle(self):
         """Replace sequences that grew `growth` tokens by fresh ones of their start length
         (the fork step replaces every group after each step)."""
         if self.sp.get("refork"):
-            if (self.cur_len > self.init_lens).any():
+            if self.grown:
                 self.alloc.free_seqs(self.seq_ids)
                 self._fork_groups()
-                self.cur_len = self.init_lens.copy()
+                self.grown = 0
             return
-        done = np.nonzero(self.cur_len - self.init_lens >= self.growth)[0]
-        for s in done:
+        if self.grown < self.growth:
+            return
+        for s in range(self.S):
             self.alloc.free_seq(int(self.seq_ids[s]))
             self.seq_ids[s] = self.next_id
             self.next_id += 1
@@ -448,17 +560,16 @@ class DecodeBatch:
                 self._fork_member(s, int(self.seq_ids[s]))
             else:
                 self.alloc.add_seq(int(self.seq_ids[s]), int(self.init_lens[s]))
-            self.cur_len[s] = self.init_lens[s]
+        self.grown = 0
 
     def step(self, events=None):
         self.recycle()
         max_len, ncow = self.stepper.step(self.seq_ids, events)
         self.cow_pairs.append(ncow)
-        self.cur_len += 1
+        self.grown += 1
         self.last = (max_len, ncow)
-        tot = int(self.cur_len.sum())
-        kv = 2 * tot * self.H * self.D * self.e
-        nblk = int(((self.cur_len + self.BS - 1) // self.BS).sum())
+        kv = 2 * int(self.tot_by_grown[self.grown]) * self.H * self.D * self.e
+        nblk = int(self.nblk_by_grown[self.grown])
         self.kv_bytes.append(kv * self.layers)
         self.alg_bytes.append(kv + 2 * self.S * self.H * self.D * self.e + 4 * nblk + 4 * self.S)
 
@@ -478,32 +589,37 @@ def host_cpu() -> dict:
 
 
 def cpu_baseline(batch, units_wanted, bytes_wanted):
-    """Time the float64 oracle on (sequence, head) units of the same workload."""
+    """Time the float64 oracle on (sequence, head) units of the same workload: layer 0, or for
+    a multi-layer batch the first and the last layer (half of the budget each)."""
     import torch
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
     tables, lens = batch.alloc.export(batch.seq_ids, batch.MB)
-    q = W.from_torch(batch.q, batch.dtype)
-    units, seqs, kv = [], [], 0
-    for s in range(batch.S):
-        if len(units) >= units_wanted or kv >= bytes_wanted:
-            break
-        seqs.append(s)
-        for h in range(batch.H):
-            if len(units) < units_wanted and kv < bytes_wanted:
-                units.append((s, h))
-                kv += 2 * int(lens[s]) * batch.D * batch.e
+    layers = [0] if batch.layers == 1 else [0, batch.layers - 1]
+    units, kv = [], 0
     prepared = {}
-    for s in seqs:
-        n = -(-int(lens[s]) // batch.BS)
-        idx = torch.from_numpy(tables[s, :n].astype(np.int64)).to(batch.k_pool.device)
-        prepared[s] = (W.from_torch(batch.k_pool.index_select(0, idx), batch.dtype),
-                       W.from_torch(batch.v_pool.index_select(0, idx), batch.dtype),
-                       np.arange(n, dtype=np.int32)[None, :])
+    for li, l in enumerate(layers):
+        share_units = units_wanted * (li + 1) // len(layers)
+        share_bytes = bytes_wanted * (li + 1) / len(layers)
+        kp, vp = batch.t["kp"][l], batch.t["vp"][l]
+        q = W.from_torch(batch.t["q"][l], batch.dtype)
+        for s in range(batch.S):
+            if len(units) >= share_units or kv >= share_bytes:
+                break
+            n = -(-int(lens[s]) // batch.BS)
+            idx = torch.from_numpy(tables[s, :n].astype(np.int64)).to(kp.device)
+            prepared[(l, s)] = (q, W.from_torch(kp.index_select(0, idx), batch.dtype),
+                                W.from_torch(vp.index_select(0, idx), batch.dtype),
+                                np.arange(n, dtype=np.int32)[None, :])
+            for h in range(batch.H):
+                if len(units) < share_units and kv < share_bytes:
+                    units.append((l, s, h))
+                    kv += 2 * int(lens[s]) * batch.D * batch.e
+
     def unit(u):
-        s, h = u
-        kc, vc, tab = prepared[s]
+        l, s, h = u
+        q, kc, vc, tab = prepared[(l, s)]
         oracle.decode_unit(q[s:s + 1], kc, vc, tab, lens[s:s + 1], batch.scale, batch.dtype,
                            0, h)
 
@@ -520,10 +636,11 @@ def cpu_baseline(batch, units_wanted, bytes_wanted):
             t0 = time.perf_counter()
             list(ex.map(unit, units))
             dt_all = time.perf_counter() - t0
+    per_layer = {l: sum(1 for u in units if u[0] == l) for l in layers}
+    where = ", ".join(f"layer {l}: {n} units" for l, n in per_layer.items())
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(units)} (sequence, head) units of the first {len(seqs)} "
-                      f"sequences of the same batch (layer 0), {kv / 1e6:.1f} MB of K+V, "
-                      f"float64 numpy, {dt:.2f} s",
+            "sample": f"{len(units)} (sequence, head) units of the same batch ({where}), "
+                      f"{kv / 1e6:.1f} MB of K+V, float64 numpy, {dt:.2f} s",
             "seq_layer_per_s": len(units) / batch.H / dt,
             "all_cores": {"value": kv / dt_all / 1e9, "threads": threads,
                           "seq_layer_per_s": len(units) / batch.H / dt_all,
@@ -531,10 +648,16 @@ def cpu_baseline(batch, units_wanted, bytes_wanted):
             "host_cpu": host_cpu()}
 
 
-def sweep(args):
-    """Block-size x placement microbenchmark: attention throughput and KV waste."""
+def sweep(args, reps: int = 3):
+    """Block-size x placement microbenchmark: the decode launch and whole step of the
+    LLaMA-13B-shaped layer and of the long-context batch at block sizes 8, 16, 32, with
+    seeded random (scattered) and contiguous block placement, plus the KV waste.  Every
+    configuration is built once; then ``reps`` rounds time each in turn (the order rotating
+    from round to round), so every cell gets ``reps`` interleaved readings in one process.
+    One JSON line per configuration: the median and the spread (min, max) of its readings."""
     import torch
-    dev = torch.device("cuda:0")
+    dev = device_or_die()
+    cells = []
     for wl in ("llama13b_layer", "long_context"):
         for bs in (8, 16, 32):
             for placement in ("permuted", "contiguous"):
@@ -542,37 +665,53 @@ def sweep(args):
                 b = DecodeBatch(args, dev)
                 for _ in range(max(args.warmup, 50)):
                     b.step()
+                cells.append({"wl": wl, "bs": bs, "placement": placement, "batch": b,
+                              "launch_us": [], "step_ms": [], "alg_GBs": []})
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        order = cells[rep % len(cells):] + cells[:rep % len(cells)]
+        if rep % 2:
+            order = order[::-1]
+        for c in order:
+            b = c["batch"]
+            warm = TimingEvents(10, 1)
+            for i in range(10):                 # re-warm after the other configurations
+                b.step(warm.handles[i])
+            events = TimingEvents(args.steps, 1)
+            torch.cuda.synchronize()
+            with gc_paused():
+                t0 = time.perf_counter()
+                for i in range(args.steps):
+                    b.step(events.handles[i])
                 torch.cuda.synchronize()
-                import ctypes
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(args.steps)]
-                hs = []
-                for a, z in evs:
-                    a.record()
-                    z.record()
-                    hs.append((ctypes.c_void_p * 2)(a.cuda_event, z.cuda_event))
-                torch.cuda.synchronize()
-                with gc_paused():
-                    t0 = time.perf_counter()
-                    for i in range(args.steps):
-                        b.step(hs[i])
-                    torch.cuda.synchronize()
-                    wall = time.perf_counter() - t0
-                launch = float(np.mean([a.elapsed_time(z) for a, z in evs])) / 1e3
-                used = int(sum(b.alloc.block_table(int(s)).__len__() for s in b.seq_ids))
-                waste = b.alloc.wasted_slots()
-                kv = float(np.mean(b.kv_bytes[-args.steps:]))
-                print(json.dumps({
-                    "sweep": "block_size x placement", "workload": f"{wl}_{b.dtype}",
-                    "block_size": bs, "placement": placement,
-                    "ms_per_step": round(wall / args.steps * 1e3, 4),
-                    "kv_GBs": round(kv * args.steps / wall / 1e9, 1),
-                    "decode_launch_us": round(launch * 1e6, 1),
-                    "decode_alg_GBs": round(float(np.mean(b.alg_bytes[-args.steps:])) / launch / 1e9, 1),
-                    "allocated_slots": used * bs, "wasted_slots": int(waste),
-                    "waste_frac": round(waste / max(1, used * bs), 5)}), flush=True)
-                del b
-                torch.cuda.empty_cache()
+                wall = time.perf_counter() - t0
+            launch = float(np.mean(events.elapsed_ms())) / 1e3
+            events.destroy()
+            warm.destroy()
+            c["launch_us"].append(launch * 1e6)
+            c["step_ms"].append(wall / args.steps * 1e3)
+            c["alg_GBs"].append(float(np.mean(b.alg_bytes[-args.steps:])) / launch / 1e9)
+    for c in cells:
+        b = c["batch"]
+        used = int(sum(len(b.alloc.block_table(int(x))) for x in b.seq_ids))
+        waste = b.alloc.wasted_slots()
+        stat = lambda v, nd: {"median": round(float(np.median(v)), nd),
+                              "min": round(float(np.min(v)), nd), "max": round(float(np.max(v)), nd)}
+        print(json.dumps({
+            "sweep": "block_size x placement", "workload": f"{c['wl']}_{b.dtype}",
+            "block_size": c["bs"], "placement": c["placement"], "reps": reps,
+            "steps_per_rep": args.steps,
+            "decode_launch_us": stat(c["launch_us"], 1), "ms_per_step": stat(c["step_ms"], 4),
+            "decode_alg_GBs": stat(c["alg_GBs"], 1),
+            "allocated_slots": used * c["bs"], "wasted_slots": int(waste),
+            "waste_frac": round(waste / max(1, used * c["bs"]), 5)}), flush=True)
+
+
+def device_or_die():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    return torch.device("cuda:0")
 
 
 def swap_bench(args, layers: int = 8, tokens: int = 16384):
@@ -764,8 +903,8 @@ def multi_query_bench(args):
         "new_tokens_per_s": round(T * args.steps / wall, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": (measured_traffic(MQ_COUNTER_PROFILE, MQ_KERNEL_SOURCES)
-                                 if dt == "f16" else None),
+                     "traffic": ((measured_traffic(MQ_COUNTER_PROFILE, MQ_KERNEL_SOURCES) or {})
+                                 .get("bytes") if dt == "f16" else None),
                      "kernel": f"multi_query_kernel<{dt.upper()},{D},{BS}>",
                      "avg_launch_us": round(launch_s * 1e6, 2),
                      "alg_flops_per_launch": flops},
@@ -824,6 +963,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    if args.calibrate_read:
+        calibrate_read(args.calibrate_read)
+        return
     if args.ceiling:
         ceiling_bench(args)
         return
@@ -839,24 +981,18 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     b = DecodeBatch(args, dev)
-    for _ in range(args.warmup):
-        b.step()
+    L = b.layers
+    # the step driver's attention launches take these events themselves (start and end); the
+    # warm-up steps take events of their own, so they are the same steps as the timed ones
+    warm_events = TimingEvents(args.warmup, L)
+    events = TimingEvents(args.steps, L)
+    for i in range(args.warmup):
+        b.step(warm_events.handles[i])
     torch.cuda.synchronize()
+    warm_events.destroy()
     b.kv_bytes.clear()
     b.alg_bytes.clear()
-    import ctypes
     import paged_kv_cache_306_amd as pkv
-    L = b.layers
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(L)] for _ in range(args.steps)]
-    handles = []
-    for per_step in evs:      # create the events; the step driver re-records them
-        arr = (ctypes.c_void_p * (2 * L))()
-        for l, (a, z) in enumerate(per_step):
-            a.record()
-            z.record()
-            arr[2 * l], arr[2 * l + 1] = a.cuda_event, z.cuda_event
-        handles.append(arr)
     flush = (torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
              if args.flush_mall else None)
     torch.cuda.synchronize()
@@ -867,12 +1003,14 @@ def main():
             if flush is not None:
                 flush.view(torch.int64).sum()   # reads 1 GiB: evicts the MALL, no dirty lines
             h0 = time.perf_counter()
-            b.step(handles[i])
+            b.step(events.handles[i])
             host += time.perf_counter() - h0
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    attn_ms = [a.elapsed_time(z) for per_step in evs for a, z in per_step]
+    attn_ms = events.elapsed_ms()
+    events.destroy()
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
+    attn_med_s = float(np.median(attn_ms)) / 1e3
     kv_total = float(np.sum(b.kv_bytes))
     value = kv_total / wall / 1e9
     alg_per_launch = float(np.mean(b.alg_bytes))
@@ -900,10 +1038,19 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if default else None,
+                     "traffic": None,
                      "kernel": kname, "avg_launch_us": round(attn_avg_s * 1e6, 2),
+                     "median_launch_us": round(attn_med_s * 1e6, 2),
+                     "achieved_at_median": round(alg_per_launch / attn_med_s / 1e9, 1),
+                     "launches": len(attn_ms),
                      "alg_bytes_per_launch": int(alg_per_launch)},
     }
+    traffic = measured_traffic() if default else None
+    if traffic:
+        res["roofline"]["traffic"] = traffic["bytes"]
+        res["roofline"]["traffic_counter_scale"] = {
+            "FETCH_SIZE": traffic.get("fetch_scale"), "WRITE_SIZE": traffic.get("write_scale"),
+            "calibrated_on": traffic.get("calibration")}
     # the decode launch against a plain read of exactly its own tiles (measured here, after the
     # timed steps; 16-token blocks at the seeded placement, pools small enough for a copy)
     if (args.workload in ("llama13b_layer", "long_context") and args.block_size == 16

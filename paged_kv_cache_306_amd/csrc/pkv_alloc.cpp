@@ -190,45 +190,79 @@ pkv_status_t pkv_alloc_append_slots(pkv_alloc_t* a, const int64_t* seqs, int32_t
   return PKV_OK;
 }
 
-// The blocks pkv_alloc_append_slots(seqs) would take, without changing anything: the same
-// decisions, made on per-call copies of each listed sequence's length and table size and of
-// the reference counts that copy-on-write lowers.
+// The blocks pkv_alloc_append_slots(seqs) would take, without changing anything.
+//
+// Sequences listed once (the usual case): one new block per sequence whose length is a
+// multiple of the block size; and for a block with r references that k listed sequences are
+// about to write into, min(k, r - 1) copies (each writer but the last copies while the count
+// is above one).  Sequences listed more than once: the same decisions, replayed on per-call
+// copies of each listed sequence's length and table size and of the reference counts that
+// copy-on-write lowers.
 pkv_status_t pkv_alloc_append_need(const pkv_alloc_t* a, const int64_t* seqs, int32_t n,
                                    int32_t* blocks) {
   if (!a || n < 0 || (n > 0 && !seqs) || !blocks) return PKV_EINVAL;
-  struct Sim {
-    const pkv_alloc::Seq* seq;
-    int32_t len;
-    int32_t table_size;
-    bool last_private;  // an earlier append of this call left its last block unshared
-  };
-  std::unordered_map<int64_t, Sim> sims;
-  std::unordered_map<int32_t, int32_t> lowered;  // block -> references dropped by copies
+  thread_local std::vector<int64_t> ids;
+  thread_local std::vector<int32_t> shared;  // target blocks with more than one reference
+  ids.assign(seqs, seqs + n);
+  std::sort(ids.begin(), ids.end());
+  const bool distinct = std::adjacent_find(ids.begin(), ids.end()) == ids.end();
   int64_t need = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = sims.find(seqs[i]);
-    if (it == sims.end()) {
-      auto s = a->seqs.find(seqs[i]);
-      if (s == a->seqs.end()) return PKV_EINVAL;
-      it = sims.emplace(seqs[i], Sim{&s->second, s->second.len,
-                                     static_cast<int32_t>(s->second.table.size()), false}).first;
-    }
-    Sim& m = it->second;
-    if (m.len == INT32_MAX) return PKV_EINVAL;
-    const int32_t j = m.len / a->block_size;
-    if (j == m.table_size) {
-      ++need;  // a new block, held by this sequence alone
-      ++m.table_size;
-      m.last_private = true;
-    } else if (!m.last_private) {
-      const int32_t b = m.seq->table[j];
-      if (a->ref[b] - lowered[b] > 1) {
-        ++need;  // a fresh block for the copy; the shared one loses a reference
-        ++lowered[b];
+  if (distinct) {
+    shared.clear();
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = a->seqs.find(seqs[i]);
+      if (it == a->seqs.end()) return PKV_EINVAL;
+      const pkv_alloc::Seq& s = it->second;
+      if (s.len == INT32_MAX) return PKV_EINVAL;
+      const int32_t j = s.len / a->block_size;
+      if (j == static_cast<int32_t>(s.table.size())) {
+        ++need;
+      } else if (a->ref[s.table[j]] > 1) {
+        shared.push_back(s.table[j]);
       }
-      m.last_private = true;
     }
-    ++m.len;
+    std::sort(shared.begin(), shared.end());
+    for (size_t i = 0; i < shared.size();) {
+      size_t k = i;
+      while (k < shared.size() && shared[k] == shared[i]) ++k;
+      need += std::min<int64_t>(static_cast<int64_t>(k - i), a->ref[shared[i]] - 1);
+      i = k;
+    }
+  } else {
+    struct Sim {
+      const pkv_alloc::Seq* seq;
+      int32_t len;
+      int32_t table_size;
+      bool last_private;  // an earlier append of this call left its last block unshared
+    };
+    std::unordered_map<int64_t, Sim> sims;
+    std::unordered_map<int32_t, int32_t> lowered;  // block -> references dropped by copies
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = sims.find(seqs[i]);
+      if (it == sims.end()) {
+        auto s = a->seqs.find(seqs[i]);
+        if (s == a->seqs.end()) return PKV_EINVAL;
+        it = sims.emplace(seqs[i], Sim{&s->second, s->second.len,
+                                       static_cast<int32_t>(s->second.table.size()), false})
+                 .first;
+      }
+      Sim& m = it->second;
+      if (m.len == INT32_MAX) return PKV_EINVAL;
+      const int32_t j = m.len / a->block_size;
+      if (j == m.table_size) {
+        ++need;  // a new block, held by this sequence alone
+        ++m.table_size;
+        m.last_private = true;
+      } else if (!m.last_private) {
+        const int32_t b = m.seq->table[j];
+        if (a->ref[b] - lowered[b] > 1) {
+          ++need;  // a fresh block for the copy; the shared one loses a reference
+          ++lowered[b];
+        }
+        m.last_private = true;
+      }
+      ++m.len;
+    }
   }
   *blocks = static_cast<int32_t>(std::min<int64_t>(need, INT32_MAX));
   return PKV_OK;

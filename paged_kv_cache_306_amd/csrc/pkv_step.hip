@@ -136,11 +136,17 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   for (int k = 0; k < 2; ++k) {
     auto& sg = st->stage[k];
     sg.dev = static_cast<char*>(d_index) + k * bytes;
+    // The staging area is fine-grained (coherent) host memory, so the prologue's reads of it
+    // always fetch what the host last wrote and never leave a copy in the GPU's caches.  The
+    // host only needs to know that the prologue has finished reading it before refilling it,
+    // which the launch's completion signal tells without a system-scope release: the marker
+    // is created without that fence (a cache writeback and invalidate between kernels).
     void* dptr = nullptr;
-    if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes, hipHostMallocMapped) !=
-            hipSuccess ||
+    if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes,
+                      hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
         hipHostGetDevicePointer(&dptr, sg.host, 0) != hipSuccess ||
-        hipEventCreateWithFlags(&sg.read, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&sg.read, hipEventDisableTiming | hipEventDisableSystemFence) !=
+            hipSuccess) {
       (void)hipGetLastError();
       pkv_stepper_destroy(st);
       return nullptr;

@@ -97,7 +97,8 @@ pkv_status_t pkv_stepper_check(const pkv_alloc_t* alloc, const pkv_cache_desc_t*
       return PKV_EINVAL;
 
   // every sequence known and listed once; its length after the append fits the table width
-  std::vector<int64_t> sorted(seqs, seqs + n);
+  thread_local std::vector<int64_t> sorted;
+  sorted.assign(seqs, seqs + n);
   std::sort(sorted.begin(), sorted.end());
   if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return PKV_EINVAL;
   int64_t longest = 0;

@@ -19,7 +19,7 @@ def _fork_step_manager():
     b._fork_groups = types.MethodType(bench.DecodeBatch._fork_groups, b)
     b.recycle = types.MethodType(bench.DecodeBatch.recycle, b)
     b._fork_groups()
-    b.cur_len = b.init_lens.copy()
+    b.grown = 0
     return sp, b
 
 
@@ -32,7 +32,7 @@ def test_fork_step_copies_224_blocks_every_step():
     for _ in range(4):
         b.recycle()
         slots, pairs = b.alloc.append_slots(b.seq_ids)
-        b.cur_len += 1
+        b.grown += 1
         # 8 holders of each group's partial block: the first 7 writers copy, the last writes
         # in place
         assert len(pairs) == 7 * 32

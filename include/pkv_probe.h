@@ -1,5 +1,6 @@
-/* Read-bandwidth probes (libpkv_probe.so) -- a measurement aid, not part of the paged-attention
- * path.  bench.py --ceiling uses them to measure what HBM delivers on this chip for the two
+/* Measurement probes (libpkv_probe.so) -- aids, not part of the paged-attention path.
+ *
+ * Read bandwidth.  bench.py --ceiling uses them to measure what HBM delivers on this chip for the two
  * access patterns that bound the decode kernel: one contiguous stream, and whole fixed-size
  * tiles visited in a given (random) order, which is how decode gathers K/V through a block
  * table ("PagedAttention: Efficient LLM Serving with vLLM", "The PagedAttention Algorithm":
@@ -35,6 +36,30 @@ extern "C" {
 int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes, const int32_t* order,
                        int64_t num_tiles, int32_t nontemporal, uint32_t* sink,
                        int32_t workgroups, void* stream);
+
+/* Sustained matrix-core rate: enqueue one launch of `workgroups` workgroups of 256 threads,
+ * each wave running `iters` rounds of eight back-to-back v_mfma_f32_16x16x32_f16 products on
+ * independent accumulators (16 x 16 x 32 x 2 flops each).  lds = 0: operands in registers;
+ * lds != 0: every product's A operand is one 16-byte-per-lane LDS read, 1 KiB per wave and
+ * product -- the LDS-to-product ratio of the multi-query kernel's K and V fragment reads.
+ *
+ *   out     device float [workgroups * 256], written (keeps the products live).
+ *   clocks  device uint64 [2]: shader-clock cycles and 100 MHz real-time ticks that wave 0 of
+ *           workgroup 0 spent in its loop (their ratio is the shader clock during the launch).
+ *
+ * Returns 0 on success, 1 for invalid arguments (nothing enqueued), 2 when the launch fails.
+ */
+int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out,
+                       uint64_t* clocks, void* stream);
+
+/* Shader-clock sampler: enqueue one 64-thread workgroup that polls the shader-clock and the
+ * 100 MHz real-time counters until `ticks` real-time ticks (1 .. 10^8, at most one second)
+ * have passed, then writes clocks[0] = shader-clock cycles and clocks[1] = real-time ticks of
+ * that window.  Launched on a stream of its own beside other work, it gives the mean shader
+ * clock while that work runs (it holds one wave slot).  Returns 0, 1 (invalid arguments,
+ * nothing enqueued) or 2 (launch failed).
+ */
+int32_t pkv_probe_clock(int64_t ticks, uint64_t* clocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """Build libpkv.so in-tree: the HIP kernels for gfx950 (hipcc) plus the host block manager
-(g++, plain C++); and libpkv_probe.so, the read-bandwidth probes bench.py --ceiling uses.
+(g++, plain C++); and libpkv_probe.so, the measurement probes bench.py uses (read bandwidth,
+matrix-core rate, shader clock).
 ``python -m paged_kv_cache_306_amd.build`` or ``build()``."""
 from __future__ import annotations
 
@@ -21,7 +22,8 @@ PROBE_SOURCES = ["pkv_probe.hip"]
 # Per-source hipcc flags.  The multi-query kernel keeps its MFMA accumulators in ordinary
 # VGPRs (gfx950 MFMAs take C/D there too): with the accumulation-register form the compiler
 # copies every accumulator between the two register files on each loop iteration.
-EXTRA_HIPCC_FLAGS = {"pkv_multi_query.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_HIPCC_FLAGS = {"pkv_multi_query.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                     "pkv_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -75,8 +77,8 @@ def build(verbose: bool = False) -> str:
     probe_objs = []
     for src in PROBE_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
+        _run([_hipcc(), *HIPCC_FLAGS, *EXTRA_HIPCC_FLAGS.get(src, []), "-I", INCLUDE, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
         probe_objs.append(obj)
     _link(probe_objs, PROBE_LIB, verbose)
     return LIB

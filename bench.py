@@ -127,9 +127,9 @@ def parse():
                     help="only measure the achievable HBM read rate (libpkv_probe.so): a "
                          "contiguous stream and whole 2/4/8 KiB tiles in random order")
     ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="only measure the sustained 16x16x32 fp16 matrix-core rate and shader "
-                         "clock (libpkv_probe.so): products alone, and each fed by a 1 KiB LDS "
-                         "read per wave as the multi-query kernel's K/V fragments are")
+                    help="only measure the sustained 16x16x32 fp16 matrix-core rate "
+                         "(libpkv_probe.so): products alone, and each fed by a 1 KiB LDS read "
+                         "per wave as the multi-query kernel's K/V fragments are")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     ap.add_argument("--calibrate-read", type=int, default=0, metavar="MIB",
@@ -324,8 +324,8 @@ def load_probe():
 
 
 def load_probe_lib():
-    """The in-tree probe library (include/pkv_probe.h) with the matrix-core and clock probes'
-    signatures set, or None if it is not built."""
+    """The in-tree probe library (include/pkv_probe.h) with the matrix-core probe's signature
+    set, or None if it is not built."""
     import ctypes
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_306_amd",
                         "libpkv_probe.so")
@@ -334,60 +334,29 @@ def load_probe_lib():
     lib = ctypes.CDLL(path)
     lib.pkv_probe_mfma.restype = ctypes.c_int32
     lib.pkv_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.pkv_probe_clock.restype = ctypes.c_int32
-    lib.pkv_probe_clock.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+                                   ctypes.c_void_p, ctypes.c_void_p]
     return lib
-
-
-def shader_clock_ghz(clocks):
-    """Mean shader clock from a probe's (shader-clock cycles, 100 MHz real-time ticks)."""
-    c = clocks.cpu().tolist()
-    return c[0] / (c[1] / 1e8) / 1e9 if c[1] > 0 else None
-
-
-def sample_clock(launch, n, seconds):
-    """Mean shader clock while `launch` runs n times: the one-wave clock sampler of the probe
-    library polls the clock counters for 80% of the expected span of those launches on a
-    stream of its own, started just before them; both streams are non-blocking pool streams.
-    Returns (GHz, sampled seconds), or None when the probe library is missing."""
-    import torch
-    lib = load_probe_lib()
-    if lib is None:
-        return None
-    clocks = torch.zeros(2, dtype=torch.int64, device="cuda:0")
-    s_clk, s_run = torch.cuda.Stream(), torch.cuda.Stream()
-    ticks = max(1, min(int(0.8 * n * seconds * 1e8), 100_000_000))
-    torch.cuda.synchronize()
-    if lib.pkv_probe_clock(ticks, clocks.data_ptr(), s_clk.cuda_stream) != 0:
-        raise RuntimeError("pkv_probe_clock failed")
-    with torch.cuda.stream(s_run):
-        for _ in range(n):
-            launch()
-    torch.cuda.synchronize()
-    return shader_clock_ghz(clocks), int(clocks[1].item()) / 1e8
 
 
 def mfma_ceiling(args):
     """Sustained 16x16x32 fp16 matrix-core rate on all CUs (16 waves per CU, eight independent
-    accumulators per wave) and the shader clock during it: products alone, and each product's
-    A operand read from LDS (1 KiB per wave and product, the multi-query kernel's ratio of K/V
-    fragment bytes to products).  HIP events, median of 5 launches after one warm-up."""
+    accumulators per wave): products alone, and each product's A operand read from LDS (1 KiB
+    per wave and product, the multi-query kernel's ratio of K/V fragment bytes to products).
+    HIP events, median of 5 launches after one warm-up."""
     import torch
     lib = load_probe_lib()
     if lib is None:
         raise RuntimeError("libpkv_probe.so is not built (run __graft_entry__.build())")
     wgs, iters = 256 * 4, 20000
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
-    clocks = torch.zeros(2, dtype=torch.int64, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     flops = wgs * 4 * iters * 8 * 2.0 * 16 * 16 * 32
     for lds in (0, 1):
         def launch():
-            if lib.pkv_probe_mfma(lds, iters, wgs, out.data_ptr(), clocks.data_ptr(), stream) != 0:
+            if lib.pkv_probe_mfma(lds, iters, wgs, out.data_ptr(), stream) != 0:
                 raise RuntimeError("pkv_probe_mfma failed")
         launch()
-        ts, ghz = [], []
+        ts = []
         for _ in range(5):
             a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -395,15 +364,11 @@ def mfma_ceiling(args):
             z.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(z) / 1e3)
-            ghz.append(shader_clock_ghz(clocks))
-        t, clk = float(np.median(ts)), float(np.median(ghz))
+        t = float(np.median(ts))
         tf = flops / t / 1e12
-        peak = MFMA_PEAK_TFLOPS["f16"]
         print(json.dumps({"pattern": "mfma_f16_16x16x32" + ("+lds_1KiB" if lds else ""),
                           "us": round(t * 1e6, 1), "TFLOP/s": round(tf, 1),
-                          "frac_of_peak": round(tf / peak, 4), "clock_GHz": round(clk, 3),
-                          "frac_at_clock": round(tf / (peak * clk / PEAK_CLOCK_GHZ), 4)}),
-              flush=True)
+                          "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS["f16"], 4)}), flush=True)
 
 
 def own_tiles_read_rate(workload, seed):
@@ -486,7 +451,6 @@ def ceiling_bench(args):
 WORKLOADS = ("llama13b_layer", "long_context", "shared_prefix", "fork_step", "full_step_40",
              "prefix_hit")
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16 matrix peak
-PEAK_CLOCK_GHZ = 2.4   # the shader clock those peaks assume (256 CUs)
 
 
 def workload_spec(name: str, seed: int, block_size: int, placement: str):
@@ -975,10 +939,6 @@ def multi_query_bench(args):
     peak = MFMA_PEAK_TFLOPS[dt]
     achieved = flops / launch_s / 1e12
     value = flops * args.steps / wall / 1e12
-    # shader clock during the launches (outside the timed region): the matrix peak assumes
-    # the 2.4 GHz peak clock, which this launch does not run at
-    clk = sample_clock(lambda: pkv.paged_attention_multi_query(
-        out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len, work_items=items), 10, launch_s)
     res = {
         "metric": "multi-query paged attention TFLOP/s after a prefix-cache hit, LLaMA-13B "
                   "shape", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -999,10 +959,7 @@ def multi_query_bench(args):
                                  .get("bytes") if dt == "f16" else None),
                      "kernel": f"multi_query_kernel<{dt.upper()},{D},{BS}>",
                      "avg_launch_us": round(launch_s * 1e6, 2),
-                     "alg_flops_per_launch": flops,
-                     "clock_GHz": round(clk[0], 3) if clk else None,
-                     "frac_at_clock": (round(achieved / (peak * clk[0] / PEAK_CLOCK_GHZ), 4)
-                                       if clk else None)},
+                     "alg_flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = multi_query_cpu_baseline(w, q, kp, vp, dt)

@@ -44,22 +44,10 @@ int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes, const
  * product -- the LDS-to-product ratio of the multi-query kernel's K and V fragment reads.
  *
  *   out     device float [workgroups * 256], written (keeps the products live).
- *   clocks  device uint64 [2]: shader-clock cycles and 100 MHz real-time ticks that wave 0 of
- *           workgroup 0 spent in its loop (their ratio is the shader clock during the launch).
  *
  * Returns 0 on success, 1 for invalid arguments (nothing enqueued), 2 when the launch fails.
  */
-int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out,
-                       uint64_t* clocks, void* stream);
-
-/* Shader-clock sampler: enqueue one 64-thread workgroup that polls the shader-clock and the
- * 100 MHz real-time counters until `ticks` real-time ticks (1 .. 10^8, at most one second)
- * have passed, then writes clocks[0] = shader-clock cycles and clocks[1] = real-time ticks of
- * that window.  Launched on a stream of its own beside other work, it gives the mean shader
- * clock while that work runs (it holds one wave slot).  Returns 0, 1 (invalid arguments,
- * nothing enqueued) or 2 (launch failed).
- */
-int32_t pkv_probe_clock(int64_t ticks, uint64_t* clocks, void* stream);
+int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out, void* stream);
 
 #ifdef __cplusplus
 }

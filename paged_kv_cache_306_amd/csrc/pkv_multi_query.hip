@@ -59,6 +59,8 @@ constexpr int kMqChunk = 32;                                // keys per compute 
 constexpr int kMqSub = 2;                                   // compute steps per LDS stage
 constexpr int kMqStage = kMqChunk * kMqSub;                 // keys staged per barrier
 constexpr float kMqSlack = 8.0f;  // log2 units a score may exceed the softmax reference by
+constexpr int kMqXcds = 8;        // XCDs of the chip, each with its own L2
+constexpr int kMqXcdChunk = 64;   // items an XCD runs per head (its resident workgroups)
 constexpr int kMqItemSeqBits = 20;                          // work item = sequence | tile << 20
 constexpr int kMqItemSeqMask = (1 << kMqItemSeqBits) - 1;
 constexpr int kMqMaxTiles = 1 << (31 - kMqItemSeqBits);
@@ -174,9 +176,26 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t vs0[kMqStage * D];
   __shared__ __attribute__((aligned(16))) uint16_t vs1[kMqStage * D];
 
-  // Head-fastest order: neighbouring workgroups read the same blocks' other heads.
-  const int h = blockIdx.x % num_heads;
-  const int j = blockIdx.x / num_heads;
+  // Which (item, head) this workgroup computes.  Workgroups are dealt to the XCDs in turn
+  // (workgroup b to XCD b % 8), and each XCD has an L2 of its own.  With a head count that is
+  // a multiple of 8, XCD x takes heads x, x + 8, ... and runs kMqXcdChunk consecutive items
+  // of one of them before the next, so its L2 holds one head's K/V at a time and the blocks
+  // that the items share (a prefix-cache hit's prompt) come from HBM about once per head
+  // rather than once per head per pass over the L2.  Otherwise heads go fastest.
+  int h, j;
+  if (num_heads % kMqXcds == 0) {
+    const int hx = num_heads / kMqXcds;                  // heads per XCD
+    const int x = static_cast<int>(blockIdx.x % kMqXcds);
+    const int k = static_cast<int>(blockIdx.x / kMqXcds);  // this XCD's k-th workgroup
+    const int items = static_cast<int>(gridDim.x) / num_heads;
+    const int chunk = k / (kMqXcdChunk * hx), within = k % (kMqXcdChunk * hx);
+    const int in_chunk = min(kMqXcdChunk, items - chunk * kMqXcdChunk);  // last chunk: fewer
+    h = x + kMqXcds * (within / in_chunk);
+    j = chunk * kMqXcdChunk + within % in_chunk;
+  } else {
+    h = static_cast<int>(blockIdx.x % num_heads);
+    j = static_cast<int>(blockIdx.x / num_heads);
+  }
   int s, tile;
   if (work) {
     const int item = work[j];

@@ -1,7 +1,7 @@
 // Measurement probes for gfx950 (declared in pkv_probe.h): read bandwidth for a contiguous
 // stream and for a visit of whole fixed-size tiles in a given order (the access pattern of a
-// paged K/V gather); the sustained rate of back-to-back 16x16x32 fp16 matrix products, alone
-// or each fed by one 16-byte LDS read per lane; and a one-wave sampler of the shader clock.
+// paged K/V gather); and the sustained rate of back-to-back 16x16x32 fp16 matrix products,
+// alone or each fed by one 16-byte LDS read per lane.
 // Measurement aids only; nothing on the paged-attention path calls them.
 #include <hip/hip_runtime.h>
 
@@ -110,14 +110,12 @@ hipError_t launch_tiles(const u32x4* p, const int32_t* order, int64_t num_tiles,
 // Back-to-back v_mfma_f32_16x16x32_f16 on eight independent accumulators per wave.  With
 // LDS, each product's A operand is a 16-byte-per-lane LDS read (1 KiB per wave and product,
 // the ratio of the multi-query kernel's K and V fragment reads); without, it stays in
-// registers.  Wave 0 of workgroup 0 records the shader-clock and 100 MHz real-time counters
-// around its loop.
+// registers.
 constexpr int kMfmaChains = 8;
 constexpr int kMfmaLdsVectors = 2048;  // 32 KiB
 
 template <bool LDS>
-__global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* __restrict__ out,
-                                                             uint64_t* __restrict__ clocks) {
+__global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) u32x4 lds[LDS ? kMfmaLdsVectors : 1];
   const f16x8 a0 = {(_Float16)0.001f, (_Float16)0.002f, (_Float16)0.003f, (_Float16)0.001f,
                     (_Float16)0.002f, (_Float16)0.001f, (_Float16)0.003f, (_Float16)0.002f};
@@ -125,8 +123,6 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* _
     for (int i = threadIdx.x; i < kMfmaLdsVectors; i += kThreads) lds[i] = __builtin_bit_cast(u32x4, a0);
     __syncthreads();
   }
-  const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   const f16x8 b = a0 * static_cast<_Float16>(threadIdx.x & 3);
   f32x4 c[kMfmaChains];
 #pragma unroll
@@ -146,31 +142,6 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* _
 #pragma unroll
   for (int j = 0; j < kMfmaChains; ++j) sum += c[j][0] + c[j][1] + c[j][2] + c[j][3];
   out[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = sum;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    clocks[0] = __builtin_amdgcn_s_memtime() - t0;
-    clocks[1] = __builtin_amdgcn_s_memrealtime() - r0;
-  }
-}
-
-// One wave that reads the shader-clock and real-time counters until `ticks` of the 100 MHz
-// real-time counter have passed (or kClockMaxPolls polls, whichever comes first), then stores
-// both deltas: the mean shader clock over that window, whatever else runs on the GPU.
-constexpr int64_t kClockMaxPolls = int64_t{1} << 26;
-
-__global__ __launch_bounds__(64) void clock_sampler_kernel(int64_t ticks,
-                                                           uint64_t* __restrict__ clocks) {
-  const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-  uint64_t t = t0, r = r0;
-  for (int64_t i = 0; i < kClockMaxPolls && static_cast<int64_t>(r - r0) < ticks; ++i) {
-    __builtin_amdgcn_s_sleep(2);
-    t = __builtin_amdgcn_s_memtime();
-    r = __builtin_amdgcn_s_memrealtime();
-  }
-  if (threadIdx.x == 0) {
-    clocks[0] = t - t0;
-    clocks[1] = r - r0;
-  }
 }
 
 }  // namespace
@@ -205,23 +176,13 @@ extern "C" int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_b
 }
 
 extern "C" int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out,
-                                  uint64_t* clocks, void* stream) {
-  if (!out || !clocks || iters < 1 || workgroups < 1 || workgroups > 65536) return 1;
+                                  void* stream) {
+  if (!out || iters < 1 || workgroups < 1 || workgroups > 65536) return 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (lds)
-    hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3(workgroups), dim3(kThreads), 0, s, iters, out,
-                       clocks);
+    hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3(workgroups), dim3(kThreads), 0, s, iters, out);
   else
-    hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3(workgroups), dim3(kThreads), 0, s, iters,
-                       out, clocks);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
-}
-
-extern "C" int32_t pkv_probe_clock(int64_t ticks, uint64_t* clocks, void* stream) {
-  if (!clocks || ticks < 1 || ticks > 100000000) return 1;  // at most one second
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(clock_sampler_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
-                     ticks, clocks);
+    hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3(workgroups), dim3(kThreads), 0, s, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

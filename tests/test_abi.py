@@ -292,7 +292,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
         pytest.skip("libpkv_probe.so is not built")
     lib = ctypes.CDLL(path)
     names = declared_symbols("pkv_probe.h")
-    assert names == ["pkv_probe_clock", "pkv_probe_mfma", "pkv_probe_read"]
+    assert names == ["pkv_probe_mfma", "pkv_probe_read"]
     for n in names:
         assert hasattr(lib, n), n
     f = lib.pkv_probe_read
@@ -313,17 +313,11 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     m = lib.pkv_probe_mfma
     m.restype = ctypes.c_int32
     m.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_void_p]
-    ok = dict(lds=1, iters=10, wgs=4, out=p, clocks=sink)
-    for change in (dict(out=None), dict(clocks=None), dict(iters=0), dict(wgs=0),
-                   dict(wgs=65537)):
+                  ctypes.c_void_p]
+    ok = dict(lds=1, iters=10, wgs=4, out=p)
+    for change in (dict(out=None), dict(iters=0), dict(wgs=0), dict(wgs=65537)):
         a = {**ok, **change}
-        assert m(a["lds"], a["iters"], a["wgs"], a["out"], a["clocks"], None) == 1, change
-    c = lib.pkv_probe_clock
-    c.restype = ctypes.c_int32
-    c.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
-    for ticks, clocks in ((0, sink), (100000001, sink), (1000, None)):
-        assert c(ticks, clocks, None) == 1, (ticks, clocks)
+        assert m(a["lds"], a["iters"], a["wgs"], a["out"], None) == 1, change
 
 
 def test_noalloc_bound_matches_header_and_oversize_is_refused_on_the_host():

@@ -132,8 +132,9 @@ def parse():
                          "contiguous stream and whole 2/4/8 KiB tiles in random order")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the sustained 16x16x32 fp16 matrix-core rate "
-                         "(libpkv_probe.so): products alone, and each fed by a 1 KiB LDS read "
-                         "per wave as the multi-query kernel's K/V fragments are")
+                         "(libpkv_probe.so): products alone, each fed by a 1 KiB LDS read per "
+                         "wave as the multi-query kernel's K/V fragments are, and each followed "
+                         "by independent vector instructions")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (to scale HBM counters)")
     ap.add_argument("--calibrate-read", type=int, default=0, metavar="MIB",
@@ -344,9 +345,11 @@ def load_probe_lib():
 
 def mfma_ceiling(args):
     """Sustained 16x16x32 fp16 matrix-core rate on all CUs (16 waves per CU, eight independent
-    accumulators per wave): products alone, and each product's A operand read from LDS (1 KiB
-    per wave and product, the multi-query kernel's ratio of K/V fragment bytes to products).
-    HIP events, median of 5 launches after one warm-up."""
+    accumulators per wave): products alone; each product's A operand read from LDS (1 KiB per
+    wave and product, the multi-query kernel's ratio of K/V fragment bytes to products); and
+    each product followed by 2, 4 or 8 independent v_fma_f32 or by 1 or 2 (v_mul_f32, v_exp_f32)
+    pairs, which shows how much vector work the SIMD overlaps with its products.  HIP events, median of 5
+    launches after one warm-up."""
     import torch
     lib = load_probe_lib()
     if lib is None:
@@ -355,9 +358,11 @@ def mfma_ceiling(args):
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     flops = wgs * 4 * iters * 8 * 2.0 * 16 * 16 * 32
-    for lds in (0, 1):
+    names = ["mfma_f16_16x16x32", "mfma_f16_16x16x32+lds_1KiB", "mfma+2_fma", "mfma+4_fma",
+             "mfma+8_fma", "mfma+1_mul_exp", "mfma+2_mul_exp"]
+    for mode, name in enumerate(names):
         def launch():
-            if lib.pkv_probe_mfma(lds, iters, wgs, out.data_ptr(), stream) != 0:
+            if lib.pkv_probe_mfma(mode, iters, wgs, out.data_ptr(), stream) != 0:
                 raise RuntimeError("pkv_probe_mfma failed")
         launch()
         ts = []
@@ -370,8 +375,7 @@ def mfma_ceiling(args):
             ts.append(a.elapsed_time(z) / 1e3)
         t = float(np.median(ts))
         tf = flops / t / 1e12
-        print(json.dumps({"pattern": "mfma_f16_16x16x32" + ("+lds_1KiB" if lds else ""),
-                          "us": round(t * 1e6, 1), "TFLOP/s": round(tf, 1),
+        print(json.dumps({"pattern": name, "us": round(t * 1e6, 1), "TFLOP/s": round(tf, 1),
                           "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS["f16"], 4)}), flush=True)
 
 

@@ -39,15 +39,18 @@ int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes, const
 
 /* Sustained matrix-core rate: enqueue one launch of `workgroups` workgroups of 256 threads,
  * each wave running `iters` rounds of eight back-to-back v_mfma_f32_16x16x32_f16 products on
- * independent accumulators (16 x 16 x 32 x 2 flops each).  lds = 0: operands in registers;
- * lds != 0: every product's A operand is one 16-byte-per-lane LDS read, 1 KiB per wave and
- * product -- the LDS-to-product ratio of the multi-query kernel's K and V fragment reads.
+ * independent accumulators (16 x 16 x 32 x 2 flops each).  mode:
+ *   0  operands in registers;
+ *   1  every product's A operand one 16-byte-per-lane LDS read, 1 KiB per wave and product --
+ *      the LDS-to-product ratio of the multi-query kernel's K and V fragment reads;
+ *   2, 3, 4  every product followed by 2, 4, 8 independent v_fma_f32;
+ *   5, 6     every product followed by 1, 2 independent (v_mul_f32, v_exp_f32) pairs.
  *
  *   out     device float [workgroups * 256], written (keeps the products live).
  *
  * Returns 0 on success, 1 for invalid arguments (nothing enqueued), 2 when the launch fails.
  */
-int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out, void* stream);
+int32_t pkv_probe_mfma(int32_t mode, int32_t iters, int32_t workgroups, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,8 @@
 // Measurement probes for gfx950 (declared in pkv_probe.h): read bandwidth for a contiguous
 // stream and for a visit of whole fixed-size tiles in a given order (the access pattern of a
 // paged K/V gather); and the sustained rate of back-to-back 16x16x32 fp16 matrix products,
-// alone or each fed by one 16-byte LDS read per lane.
+// alone, each fed by one 16-byte LDS read per lane, or interleaved with independent vector
+// instructions.
 // Measurement aids only; nothing on the paged-attention path calls them.
 #include <hip/hip_runtime.h>
 
@@ -107,14 +108,16 @@ hipError_t launch_tiles(const u32x4* p, const int32_t* order, int64_t num_tiles,
   return hipGetLastError();
 }
 
-// Back-to-back v_mfma_f32_16x16x32_f16 on eight independent accumulators per wave.  With
-// LDS, each product's A operand is a 16-byte-per-lane LDS read (1 KiB per wave and product,
-// the ratio of the multi-query kernel's K and V fragment reads); without, it stays in
-// registers.
+// Back-to-back v_mfma_f32_16x16x32_f16 on eight independent accumulators per wave.  LDS:
+// each product's A operand is a 16-byte-per-lane LDS read (1 KiB per wave and product, the
+// ratio of the multi-query kernel's K and V fragment reads); otherwise it stays in
+// registers.  NV > 0: every product is followed by NV vector instructions (v_fma_f32, or a
+// v_mul_f32 and a v_exp_f32 when EXP) on registers the products never read, which shows how
+// much independent vector work the SIMD overlaps with its matrix products.
 constexpr int kMfmaChains = 8;
 constexpr int kMfmaLdsVectors = 2048;  // 32 KiB
 
-template <bool LDS>
+template <bool LDS, int NV, bool EXP>
 __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) u32x4 lds[LDS ? kMfmaLdsVectors : 1];
   const f16x8 a0 = {(_Float16)0.001f, (_Float16)0.002f, (_Float16)0.003f, (_Float16)0.001f,
@@ -125,8 +128,12 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* _
   }
   const f16x8 b = a0 * static_cast<_Float16>(threadIdx.x & 3);
   f32x4 c[kMfmaChains];
+  float v[kMfmaChains];
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kMfmaChains; ++j) {
+    c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    v[j] = 1.0f + 0.001f * static_cast<float>(threadIdx.x + j);
+  }
   const uint32_t lane = threadIdx.x & 63;
   for (int it = 0; it < iters; ++it) {
     // eight consecutive 1 KiB rows (one per product), a different 8 KiB quarter each round
@@ -136,11 +143,19 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* _
       f16x8 a = a0;
       if constexpr (LDS) a = __builtin_bit_cast(f16x8, row[64 * j]);
       c[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c[j], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        float& x = v[(j + u) % kMfmaChains];
+        if constexpr (EXP)
+          x = __builtin_amdgcn_exp2f(x * -0.5f);
+        else
+          x = fmaf(x, 0.999f, 0.0001f);
+      }
     }
   }
   float sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMfmaChains; ++j) sum += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  for (int j = 0; j < kMfmaChains; ++j) sum += c[j][0] + c[j][1] + c[j][2] + c[j][3] + v[j];
   out[static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x] = sum;
 }
 
@@ -175,14 +190,20 @@ extern "C" int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_b
   return e == hipSuccess ? 0 : 2;
 }
 
-extern "C" int32_t pkv_probe_mfma(int32_t lds, int32_t iters, int32_t workgroups, float* out,
+extern "C" int32_t pkv_probe_mfma(int32_t mode, int32_t iters, int32_t workgroups, float* out,
                                   void* stream) {
-  if (!out || iters < 1 || workgroups < 1 || workgroups > 65536) return 1;
+  if (!out || iters < 1 || workgroups < 1 || workgroups > 65536 || mode < 0 || mode > 6) return 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g(workgroups), blk(kThreads);
   (void)hipGetLastError();
-  if (lds)
-    hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3(workgroups), dim3(kThreads), 0, s, iters, out);
-  else
-    hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3(workgroups), dim3(kThreads), 0, s, iters, out);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((mfma_rate_kernel<false, 0, false>), g, blk, 0, s, iters, out); break;
+    case 1: hipLaunchKernelGGL((mfma_rate_kernel<true, 0, false>), g, blk, 0, s, iters, out); break;
+    case 2: hipLaunchKernelGGL((mfma_rate_kernel<false, 2, false>), g, blk, 0, s, iters, out); break;
+    case 3: hipLaunchKernelGGL((mfma_rate_kernel<false, 4, false>), g, blk, 0, s, iters, out); break;
+    case 4: hipLaunchKernelGGL((mfma_rate_kernel<false, 8, false>), g, blk, 0, s, iters, out); break;
+    case 5: hipLaunchKernelGGL((mfma_rate_kernel<false, 1, true>), g, blk, 0, s, iters, out); break;
+    default: hipLaunchKernelGGL((mfma_rate_kernel<false, 2, true>), g, blk, 0, s, iters, out); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -314,10 +314,11 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     m.restype = ctypes.c_int32
     m.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                   ctypes.c_void_p]
-    ok = dict(lds=1, iters=10, wgs=4, out=p)
-    for change in (dict(out=None), dict(iters=0), dict(wgs=0), dict(wgs=65537)):
+    ok = dict(mode=1, iters=10, wgs=4, out=p)
+    for change in (dict(out=None), dict(iters=0), dict(wgs=0), dict(wgs=65537), dict(mode=-1),
+                   dict(mode=7)):
         a = {**ok, **change}
-        assert m(a["lds"], a["iters"], a["wgs"], a["out"], None) == 1, change
+        assert m(a["mode"], a["iters"], a["wgs"], a["out"], None) == 1, change
 
 
 def test_noalloc_bound_matches_header_and_oversize_is_refused_on_the_host():

@@ -27,8 +27,8 @@
 //     i % 4 of the 4 x 16-bit piece addressed by lane 4m + i / 4, so lane (r, g) addresses
 //     key row 4g + r / 4 (then 16 + 4g + r / 4) at head-dim column 16 t + 4 (r % 4);
 //   * O^T accumulates in 16 x 16 tiles: lane (r, g) holds output elements d = 16 t + 4 g + i
-//     of query r; one more tile, whose V^T rows are all ones, accumulates the softmax
-//     denominator from the same (rounded) probabilities, in every lane of the query.
+//     of query r.  The softmax denominator sums the same rounded probabilities: with v_dot2
+//     per lane at fp16, through one more tile whose V^T rows are all ones at bf16.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -91,6 +91,10 @@ struct Mma<F16> {
     const f16x2 v = {static_cast<_Float16>(x), static_cast<_Float16>(y)};
     hi = __builtin_bit_cast(uint32_t, v);
     lo = 0;
+  }
+  // l + both halves of a packed pair, each exactly as rounded (times 1.0), in fp32
+  static __device__ __forceinline__ float sum2(uint32_t w, float l) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{1.0f16, 1.0f16}, l, false);
   }
 };
 
@@ -317,17 +321,25 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   for (int qt = 0; qt < kMqQt; ++qt)
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) acc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Softmax reference (log2 units, equal in a query's four lanes) and the denominator: a
-  // 16 x 16 output tile whose V^T rows are all ones accumulates the sum of exactly the
-  // probabilities that enter the output products, in every lane of the query.
-  float m[kMqQt];
-  f32x4 den[kMqQt];
+  // Softmax reference m (log2 units, equal in a query's four lanes) and the denominator, the
+  // sum of exactly the probabilities that enter the output products.  fp16 adds its rounded
+  // probability pairs with v_dot2 into a per-lane partial (a query's four lanes are added at
+  // the end); bf16, whose probabilities enter in two parts, accumulates them through one more
+  // 16 x 16 output tile whose V^T rows are all ones, in every lane of the query (two products
+  // per step cost it less than eight v_dot2).
+  using den_t = std::conditional_t<Mma<Ty>::kSplit, f32x4, float>;
+  // The move test runs on raw scores against mraw = (m + kMqSlack) / scale, so a lane need
+  // not scale its largest score first; rounding here only shifts the point at which the exact
+  // test below is made.
+  const float inv_scale = 1.0f / scale_log2;
+  float m[kMqQt], mraw[kMqQt];
+  den_t den[kMqQt];
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
     m[qt] = -INFINITY;
-    den[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mraw[qt] = -INFINITY;
+    den[qt] = den_t{};
   }
-  const u32x4 ones = {Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes};
 
   // One chunk of keys for the query tiles of the wave.  mask: the chunk holds keys that some
   // query of the wave does not see (its own later positions, or keys past the workgroup's);
@@ -371,28 +383,34 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     // largest scaled one, and exp2(scale * s - m) is one FMA and one exp.  A lane first
     // checks its own scores; only when some lane of the wave would move is the maximum over
     // each query's four lanes taken (so the four lanes of a query always agree on m).
-    float lmax[kMqQt];
+    float rmax[kMqQt];
 #pragma unroll
-    for (int qt = 0; qt < kMqQt; ++qt)
-      lmax[qt] = fmaxf(fmaxf(fmaxf(z[qt][0], z[qt][1]), fmaxf(z[qt][2], z[qt][3])),
-                       fmaxf(fmaxf(z[qt][4], z[qt][5]), fmaxf(z[qt][6], z[qt][7]))) *
-                 scale_log2;
+    for (int qt = 0; qt < kMqQt; ++qt) {
+      // IEEE-754 maximum (a NaN propagates; a NaN score spoils its query either way): gfx950
+      // has it as a three-input instruction that takes the products' results as they are
+      auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+      const float a = mx(mx(z[qt][0], z[qt][1]), z[qt][2]);
+      const float b = mx(mx(z[qt][3], z[qt][4]), z[qt][5]);
+      rmax[qt] = mx(b, mx(mx(z[qt][6], z[qt][7]), a));
+    }
     float alpha[kMqQt];
     bool move = false;
 #pragma unroll
     for (int qt = 0; qt < kMqQt; ++qt) {
       alpha[qt] = 1.0f;
-      move |= lmax[qt] > m[qt] + kMqSlack;
+      move |= rmax[qt] > mraw[qt];  // raw-score form of: rmax * scale > m + kMqSlack
     }
     if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
       for (int qt = 0; qt < kMqQt; ++qt) {
-        float cm = fmaxf(lmax[qt], __shfl_xor(lmax[qt], 16, 64));
+        const float lmax = rmax[qt] * scale_log2;
+        float cm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
         // m is -inf until the query's first chunk (which holds key 0, seen by every query)
         if (cm > m[qt] + kMqSlack) {
           alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - cm);
           m[qt] = cm;
+          mraw[qt] = (cm + kMqSlack) * inv_scale;
         }
       }
       // the accumulators follow the moved reference (alpha = 1 where it did not move)
@@ -411,7 +429,10 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(z[qt][e], scale_log2, -m[qt]));
       uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
+      for (int w = 0; w < 4; ++w) {
+        Mma<Ty>::pack(p[2 * w], p[2 * w + 1], ph[w], pl[w]);
+        if constexpr (!Mma<Ty>::kSplit) den[qt] = Mma<Ty>::sum2(ph[w], den[qt]);
+      }
       pf[qt] = u32x4{ph[0], ph[1], ph[2], ph[3]};
       pfl[qt] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
@@ -433,10 +454,13 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
         if constexpr (Mma<Ty>::kSplit) acc[qt][t] = Mma<Ty>::run(a, pfl[qt], acc[qt][t]);
       }
     }
+    if constexpr (Mma<Ty>::kSplit) {
+      const u32x4 ones = {Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes, Mma<Ty>::kOnes};
 #pragma unroll
-    for (int qt = 0; qt < kMqQt; ++qt) {
-      den[qt] = Mma<Ty>::run(ones, pf[qt], den[qt]);
-      if constexpr (Mma<Ty>::kSplit) den[qt] = Mma<Ty>::run(ones, pfl[qt], den[qt]);
+      for (int qt = 0; qt < kMqQt; ++qt) {
+        den[qt] = Mma<Ty>::run(ones, pf[qt], den[qt]);
+        den[qt] = Mma<Ty>::run(ones, pfl[qt], den[qt]);
+      }
     }
   };
 
@@ -478,8 +502,15 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   for (int w = 0; w < kMqWaves; ++w) any_bad |= ks0[w] != 0;
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
+    float l;
+    if constexpr (Mma<Ty>::kSplit) {
+      l = den[qt][0];
+    } else {
+      l = den[qt] + __shfl_xor(den[qt], 16, 64);  // the query's four lanes
+      l += __shfl_xor(l, 32, 64);
+    }
     if (!qt_on[qt] || qi[qt] >= n) continue;
-    const float inv = any_bad ? NAN : 1.0f / den[qt][0];
+    const float inv = any_bad ? NAN : 1.0f / l;
     T* orow = out + static_cast<size_t>(q0 + qi[qt]) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {

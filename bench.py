@@ -1116,7 +1116,12 @@ def main():
                      "median_launch_us": round(attn_med_s * 1e6, 2),
                      "achieved_at_median": round(alg_per_launch / attn_med_s / 1e9, 1),
                      "launches": len(attn_ms), "launch_events_every_k_steps": every,
-                     "alg_bytes_per_launch": int(alg_per_launch)},
+                     "alg_bytes_per_launch": int(alg_per_launch),
+                     # share (of 1024) of the units dealt to the even XCDs, as the stepper
+                     # measured it on its first step (0: dealt evenly), and the halves' tokens
+                     # per 100 MHz tick of workgroup time in that measurement
+                     "xcd_split": b.stepper.xcd_split,
+                     "xcd_rates_even_odd": [round(x, 5) for x in b.stepper.xcd_rates()[:2]]},
     }
     traffic = measured_traffic() if default else None
     if traffic:

@@ -153,6 +153,19 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
     const int32_t* work_items, int32_t num_items, uint32_t flags, void* workspace,
     size_t workspace_bytes, pkv_stream_t stream);
 
+/* XCD-weighted dealing of attention units (host only; what the step driver's attention
+ * launches use, see "XCD balance" below).  The GPU deals workgroup b to XCD b % 8.  With a
+ * split P in 1..1023, the units u = item * num_heads + head (longest work first) are dealt so
+ * that the even XCDs receive unit u iff floor((u + 1) P / 1024) > floor(u P / 1024) -- a
+ * share P / 1024 of every stretch of the list -- each half in list order, spread over its four
+ * XCDs in turn.  pkv_decode_xcd_grid(units, P) is the number of workgroups such a launch takes
+ * (units itself for P = 0, the identity deal); pkv_decode_xcd_slot_unit(slot, units, P) the
+ * unit workgroup `slot` runs, or -1 for a slot with nothing to do.  Every unit goes to exactly
+ * one slot.  Both return -1 / -2 for bad arguments (negative sizes, P outside 0..1023, slot
+ * outside the grid).  Outputs do not depend on the deal. */
+int64_t pkv_decode_xcd_grid(int64_t units, int32_t split);
+int64_t pkv_decode_xcd_slot_unit(int64_t slot, int64_t units, int32_t split);
+
 /* The same attention as pkv_paged_attention_decode, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no workspace argument, and nothing is allocated by the call.  The split-context
@@ -467,9 +480,9 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * (an event of the stepper's own), since the two steps share the staging areas, the device
  * index area and the split-context workspace.
  *
- * The stepper allocates only pinned host memory and HIP events of its own; the caller owns the
- * device buffer d_index (pkv_stepper_index_bytes bytes, 16-byte aligned: two areas used by
- * alternate steps) and the workspace.  The host refills a staging area only after the
+ * The stepper allocates only pinned host memory (staging areas, calibration stamps) and HIP
+ * events of its own; the caller owns the device buffer d_index (pkv_stepper_index_bytes
+ * bytes, 16-byte aligned: two areas used by alternate steps) and the workspace.  The host refills a staging area only after the
  * prologue that read it (two steps earlier) has finished; that launch records its own
  * completion marker, so no event packet sits between kernels.  pkv_stepper_last_index returns the
  * device address of the packed index data of the last step.
@@ -477,6 +490,23 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * 2l takes the start and event 2l+1 the end of layer l's attention launch, recorded by the
  * launch itself (hipExtLaunchKernel) so that no event packet sits between kernels; a step with
  * n = 0 records them back to back on `stream`.
+ *
+ * XCD balance.  The eight XCDs of an MI355X do not stream K/V equally fast (measured: the odd
+ * ones take ~10% longer per token), so an even deal of the units leaves the fast half idle at
+ * the end of every attention launch.  The stepper measures the two halves on the first step
+ * with at least 128 units: that step's layer-0 attention launch deals unit b to workgroup b
+ * and each workgroup leaves its duration, XCD and token count in pinned host memory of the
+ * stepper's own; a later step reads them once that launch is done (never waiting for it) and
+ * from then on every attention launch deals the units with the split P = 1024 * speed(even) /
+ * (speed(even) + speed(odd)), bounded to 384..640 (pkv_decode_xcd_grid / _slot_unit above).
+ * P stays 0 (no weighting) when the halves differ by less than 1%, when the hardware does not
+ * place workgroup b on XCD b % 8, or after four steps without enough units.
+ * pkv_stepper_xcd_split returns the split in use (0: none; -1 for a null stepper);
+ * pkv_stepper_set_xcd_split fixes it (0..1023, 0: none) and stops the measurement, or with -1
+ * starts a new measurement on the next step (PKV_EINVAL otherwise).  pkv_stepper_xcd_rates
+ * gives the last measurement (host outs): each half's tokens per 100 MHz tick of workgroup
+ * time (0 until measured) and its outcome, a PKV_XCD_* value.  Outputs do not depend on the
+ * split.
  * ---------------------------------------------------------------------------------------*/
 typedef struct pkv_stepper pkv_stepper_t;
 
@@ -501,6 +531,16 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
                               void* const* attn_events, int32_t* max_len, int32_t* num_cow,
                               int32_t* num_done, pkv_stream_t stream);
 const void* pkv_stepper_last_index(const pkv_stepper_t* st);
+int32_t pkv_stepper_xcd_split(const pkv_stepper_t* st);
+pkv_status_t pkv_stepper_set_xcd_split(pkv_stepper_t* st, int32_t split);
+#define PKV_XCD_NONE 0       /* nothing measured (yet) */
+#define PKV_XCD_IN_FLIGHT 1  /* the stamped launch has not finished */
+#define PKV_XCD_MEASURED 2   /* rates measured, split set from them */
+#define PKV_XCD_TOO_FEW 3    /* the last stamped launch had too few workgroups per half */
+#define PKV_XCD_UNMAPPED 4   /* workgroup b did not run on XCD b % 8: no weighting */
+#define PKV_XCD_FAILED 5     /* the runtime reported an error on the stamped launch */
+pkv_status_t pkv_stepper_xcd_rates(const pkv_stepper_t* st, double* even, double* odd,
+                                   int32_t* outcome);
 pkv_status_t pkv_stepper_check(const pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
                                int32_t max_seqs, int32_t max_blocks_per_seq, const int64_t* seqs,
                                int32_t n, const pkv_layer_io_t* io, const void* workspace,

@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "lib", "PkvError", "CacheDesc", "decode_workspace_bytes", "decode_partition_tokens",
-    "decode_schedule",
+    "decode_schedule", "decode_xcd_grid", "decode_xcd_slot_unit",
     "paged_attention_decode", "paged_attention_decode_noalloc", "reshape_and_cache", "copy_blocks", "BlockAllocator",
     "DecodeStepper", "swap_blocks", "check_slot_mapping", "check_copy_pairs", "LIB_PATH",
 ]
@@ -52,6 +52,8 @@ _SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_pdesc, _i32, _i32]),
     "pkv_decode_partition_tokens": (_i32, [_pdesc, _i32, _i32]),
     "pkv_decode_single_pass_max": (_i32, []),
+    "pkv_decode_xcd_grid": (_i64, [_i64, _i32]),
+    "pkv_decode_xcd_slot_unit": (_i64, [_i64, _i64, _i32]),
     "pkv_decode_schedule": (_i32, [_pdesc, _p, _i32, _i32, _p, _i32]),
     "pkv_decode_schedule_grouped": (_i32, [_pdesc, _p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_decode_scheduled": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32,
@@ -96,6 +98,10 @@ _SIGNATURES = {
     "pkv_stepper_destroy": (None, [_p]),
     "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
     "pkv_stepper_last_index": (_p, [_p]),
+    "pkv_stepper_xcd_split": (_i32, [_p]),
+    "pkv_stepper_set_xcd_split": (_i32, [_p, _i32]),
+    "pkv_stepper_xcd_rates": (_i32, [_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), _pi32]),
     "pkv_stepper_check": (_i32, [_p, _pdesc, _i32, _i32, _p, _i32, _p, _p, _sz, _pi32]),
 }
 
@@ -166,7 +172,22 @@ def decode_partition_tokens(desc: CacheDesc, num_seqs: int, max_context_len: int
     return int(_lib().pkv_decode_partition_tokens(ctypes.byref(desc), num_seqs, max_context_len))
 
 
+def decode_xcd_grid(units: int, split: int) -> int:
+    """Workgroups an attention launch of ``units`` units takes under the XCD split (of 1024;
+    0: one per unit), pkv_decode_xcd_grid; -1 for bad arguments."""
+    return int(_lib().pkv_decode_xcd_grid(int(units), int(split)))
+
+
+def decode_xcd_slot_unit(slot: int, units: int, split: int) -> int:
+    """The unit workgroup ``slot`` runs under the XCD split, -1 for none
+    (pkv_decode_xcd_slot_unit); -2 for bad arguments."""
+    return int(_lib().pkv_decode_xcd_slot_unit(int(slot), int(units), int(split)))
+
+
 PKV_DECODE_SHARED_KV = 1
+# outcome of a stepper's XCD measurement (pkv_stepper_xcd_rates)
+PKV_XCD_NONE, PKV_XCD_IN_FLIGHT, PKV_XCD_MEASURED, PKV_XCD_TOO_FEW, PKV_XCD_UNMAPPED, \
+    PKV_XCD_FAILED = range(6)
 
 
 def decode_schedule(desc: CacheDesc, lens, max_context_len: int, group_keys=None):
@@ -684,6 +705,24 @@ class DecodeStepper:
             err.num_done = self._ndone.value
             raise err
         return self._max_len.value, self._ncow.value
+
+    @property
+    def xcd_split(self) -> int:
+        """Split (of 1024) the attention launches deal their units to the even XCDs with; 0:
+        unit b to workgroup b (pkv_stepper_xcd_split)."""
+        return int(_lib().pkv_stepper_xcd_split(self._h))
+
+    def xcd_rates(self):
+        """(even, odd, outcome): the halves' tokens per 100 MHz tick of workgroup time from the
+        last measurement and its PKV_XCD_* outcome (pkv_stepper_xcd_rates)."""
+        e, o, k = ctypes.c_double(), ctypes.c_double(), _i32()
+        _check(_lib().pkv_stepper_xcd_rates(self._h, ctypes.byref(e), ctypes.byref(o),
+                                             ctypes.byref(k)), "pkv_stepper_xcd_rates")
+        return e.value, o.value, k.value
+
+    def set_xcd_split(self, split: int) -> None:
+        """Fix the split (0..1023, 0: none), or measure it again on the next step (-1)."""
+        _check(_lib().pkv_stepper_set_xcd_split(self._h, int(split)), "pkv_stepper_set_xcd_split")
 
     def index_views(self, n: int, num_cow: int, num_items: int = 0):
         """Device views of the packed index data of the last step: (tables, lens, slots, pairs)

@@ -48,6 +48,8 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kPartTokens = 2048;
 constexpr int kSingleMax = 4096;
 constexpr int kChunkBytesPerWave = 8192;
+// s_getreg operand for HW_REG_XCC_ID (register 20), bits 3:0: the XCD a wave runs on.
+constexpr int kHwRegXccId = 20 | (3 << 11);
 // Longest run of tokens one workgroup attends: bounds the LDS copy of its block ids.
 constexpr int kMaxPartTokens = 4096;
 static_assert(kPartTokens <= kMaxPartTokens && kSingleMax <= kMaxPartTokens, "part");
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
     const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
     int num_seqs, int num_heads, int num_blocks, int max_len, float scale_log2, int part_tokens,
     int max_parts, const int32_t* __restrict__ work, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o) {
+    float* __restrict__ ws_o, int64_t units, int xcd_split, uint32_t* __restrict__ stamps) {
   using C = DecodeCfg<Ty, D, BS>;
   using T = typename Ty::store_t;
   __shared__ int sm_blk[C::kMaxBlocks];
@@ -142,12 +144,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   __shared__ float sm_l[C::kStates];
   __shared__ __attribute__((aligned(16))) float sm_acc[C::kStates][D];
 
-  // Flattened grid, head fastest: the workgroups of one (sequence, partition) run side by
-  // side and read adjacent head tiles of the same blocks.  Work item j is either listed by
-  // the host (sequence | partition << 20, longest first) or enumerated as (j / max_parts,
-  // j % max_parts).
-  const int h = blockIdx.x % num_heads;
-  const int j = blockIdx.x / num_heads;
+  // Unit b = (work item, head), head fastest: the workgroups of one (sequence, partition) run
+  // side by side and read adjacent head tiles of the same blocks.  Workgroup slot blockIdx.x
+  // runs unit blockIdx.x, or with xcd_split > 0 the unit that the XCD-weighted deal gives it
+  // (see xcd_slot_unit).  Work item j is either listed by the host (sequence | partition <<
+  // 20, longest first) or enumerated as (j / max_parts, j % max_parts).
+  int64_t unit = blockIdx.x;
+  if (xcd_split > 0) {
+    unit = xcd_slot_unit(blockIdx.x, units, xcd_split);
+    if (unit < 0) return;  // a slot past its half's share
+  }
+  const uint64_t stamp0 = stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+  const int h = static_cast<int>(unit % num_heads);
+  const int j = static_cast<int>(unit / num_heads);
   int s, p;
   if (work) {
     const int item = work[j];
@@ -290,6 +299,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
       }
     }
   }
+  // Calibration stamps: the workgroup's time in 100 MHz ticks, the XCD it ran on (valid bit
+  // 0x100), the tokens it attended and the low 32 bits of its start tick.
+  if (stamps && threadIdx.x == 0) {
+    const uint64_t stamp1 = __builtin_amdgcn_s_memrealtime();
+    const uint32_t xcc = static_cast<uint32_t>(__builtin_amdgcn_s_getreg(kHwRegXccId)) & 15u;
+    *reinterpret_cast<u32x4*>(stamps + 4 * static_cast<size_t>(blockIdx.x)) =
+        u32x4{static_cast<uint32_t>(stamp1 - stamp0), xcc | 0x100u,
+              static_cast<uint32_t>(t1 - t0), static_cast<uint32_t>(stamp0)};
+  }
 }
 
 // Merge the partitions of every (sequence, head) that was split.  One workgroup of D
@@ -360,6 +378,8 @@ struct DecodeArgs {
   hipStream_t stream;
   hipEvent_t ev_start;  // optional: takes the start of the launch (hipExtLaunchKernel)
   hipEvent_t ev_stop;   // optional: takes its end (the reduce kernel's, in split mode)
+  int xcd_split;        // 0: workgroup b runs unit b; else the XCD-weighted deal (1..1023)
+  uint32_t* stamps;     // optional, with xcd_split 0: 4 words per workgroup (see the kernel)
 };
 
 template <class Ty, int D, int BS>
@@ -367,7 +387,8 @@ static void launch_decode(const DecodeArgs& a) {
   using T = typename Ty::store_t;
   const int64_t items =
       a.work ? a.num_items : static_cast<int64_t>(a.num_seqs) * a.max_parts;
-  const int64_t wgs = items * a.num_heads;
+  const int64_t units = items * a.num_heads;
+  const int64_t wgs = a.xcd_split > 0 ? xcd_grid(units, a.xcd_split) : units;
   auto kernel = a.shared_kv ? decode_partition_kernel<Ty, D, BS, false>
                             : decode_partition_kernel<Ty, D, BS, true>;
   const bool reduce = a.part_tokens > 0;
@@ -383,14 +404,15 @@ static void launch_decode(const DecodeArgs& a) {
                             static_cast<const T*>(a.q), static_cast<const T*>(a.k_pool),
                             static_cast<const T*>(a.v_pool), a.block_tables, a.max_blocks,
                             a.context_lens, a.num_seqs, a.num_heads, a.num_blocks, a.max_len,
-                            a.scale_log2, a.part_tokens, a.max_parts, a.work, a.ws_ml, a.ws_o);
+                            a.scale_log2, a.part_tokens, a.max_parts, a.work, a.ws_ml, a.ws_o,
+                            units, a.xcd_split, a.stamps);
     else
       hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(wgs)), dim3(kDecodeThreads), 0,
                          a.stream, static_cast<T*>(a.out), static_cast<const T*>(a.q),
                          static_cast<const T*>(a.k_pool), static_cast<const T*>(a.v_pool),
                          a.block_tables, a.max_blocks, a.context_lens, a.num_seqs, a.num_heads,
                          a.num_blocks, a.max_len, a.scale_log2, a.part_tokens, a.max_parts,
-                         a.work, a.ws_ml, a.ws_o);
+                         a.work, a.ws_ml, a.ws_o, units, a.xcd_split, a.stamps);
     start = nullptr;
     if (!reduce) stop = nullptr;
   } else if (start) {
@@ -439,7 +461,8 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
                                 int32_t max_context_len, float scale, const int32_t* work,
                                 int32_t num_items, uint32_t flags, void* workspace,
                                 size_t workspace_bytes, pkv_stream_t stream,
-                                void* ev_start = nullptr, void* ev_stop = nullptr) {
+                                void* ev_start = nullptr, void* ev_stop = nullptr,
+                                int32_t xcd_split = 0, uint32_t* stamps = nullptr) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || !std::isfinite(scale) ||
@@ -489,6 +512,12 @@ static pkv_status_t decode_impl(const pkv_cache_desc_t* desc, void* out, const v
   a.stream = static_cast<hipStream_t>(stream);
   a.ev_start = static_cast<hipEvent_t>(ev_start);
   a.ev_stop = static_cast<hipEvent_t>(ev_stop);
+  // the weighted deal needs a few more workgroup slots than units; past the grid limit the
+  // units keep their own slots
+  const int64_t units = static_cast<int64_t>(work ? num_items : static_cast<int64_t>(num_seqs) * max_parts) *
+                        desc->num_heads;
+  a.xcd_split = xcd_split > 0 && xcd_grid(units, xcd_split) <= INT32_MAX ? xcd_split : 0;
+  a.stamps = stamps;
 
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
   switch (desc->dtype) {
@@ -537,11 +566,13 @@ pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, con
                                     int32_t max_context_len, float scale,
                                     const int32_t* work_items, int32_t num_items, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, pkv_stream_t stream,
-                                    void* ev_start, void* ev_stop) {
-  if (!work_items) return PKV_EINVAL;
+                                    void* ev_start, void* ev_stop, int32_t xcd_split,
+                                    uint32_t* stamps) {
+  if (!work_items || xcd_split < 0 || xcd_split >= kXcdSplitOne || (stamps && xcd_split != 0))
+    return PKV_EINVAL;
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, work_items, num_items, flags, workspace,
-                     workspace_bytes, stream, ev_start, ev_stop);
+                     workspace_bytes, stream, ev_start, ev_stop, xcd_split, stamps);
 }
 
 }  // namespace pkv
@@ -557,6 +588,18 @@ int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_se
 }
 
 int32_t pkv_decode_single_pass_max(void) { return kSingleMax; }
+
+int64_t pkv_decode_xcd_grid(int64_t units, int32_t split) {
+  if (units < 0 || split < 0 || split >= kXcdSplitOne) return -1;
+  return split == 0 ? units : xcd_grid(units, split);
+}
+
+int64_t pkv_decode_xcd_slot_unit(int64_t slot, int64_t units, int32_t split) {
+  if (units < 0 || split < 0 || split >= kXcdSplitOne || slot < 0 ||
+      slot >= pkv_decode_xcd_grid(units, split))
+    return -2;
+  return split == 0 ? slot : xcd_slot_unit(slot, units, split);
+}
 
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc_t* desc, int32_t num_seqs,
                                   int32_t max_context_len) {

@@ -36,6 +36,10 @@ inline pkv_status_t check_desc(const pkv_cache_desc_t* d) {
 
 // pkv_paged_attention_decode_scheduled with optional timing: ev_start / ev_stop (hipEvent_t,
 // created with timing, or null) take the start and end time of the attention launch itself.
+// xcd_split (0, or 1..1023 of 1024): the share of the units dealt to the even XCDs (0: unit b
+// to workgroup b).  stamps (with xcd_split 0 only, else null): device-visible memory of
+// 4 uint32 per unit that each workgroup that attends tokens fills with its duration in 100 MHz
+// ticks, its XCD | 0x100, its tokens and the low 32 bits of its start tick.
 pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, const void* q,
                                     const void* k_pool, const void* v_pool,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -43,7 +47,8 @@ pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, con
                                     int32_t max_context_len, float scale,
                                     const int32_t* work_items, int32_t num_items, uint32_t flags,
                                     void* workspace, size_t workspace_bytes, pkv_stream_t stream,
-                                    void* ev_start, void* ev_stop);
+                                    void* ev_start, void* ev_stop, int32_t xcd_split = 0,
+                                    uint32_t* stamps = nullptr);
 
 // Host checks of a cache append's slots (distinct within [0, num_slots); others are skipped)
 // and of a block copy's pairs (among in-range pairs, destinations distinct and never a

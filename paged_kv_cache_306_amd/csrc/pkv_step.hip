@@ -12,6 +12,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -109,7 +112,105 @@ struct pkv_stepper {
     bool pending = false;
   } stage[2];
   int cur = 0;
+  // XCD balance: the split the attention launches deal their units with (0: none), and its
+  // measurement from the stamps one attention launch leaves in pinned host memory.
+  enum Cal { kCalPending, kCalInFlight, kCalDone };
+  Cal cal = kCalPending;
+  int cal_attempts = 0;
+  int32_t xcd_split = 0;
+  int32_t cal_outcome = 0;          // PKV_XCD_* of the last measurement
+  double cal_rate[2] = {0.0, 0.0};  // tokens per tick of workgroup time, even and odd half
+  uint32_t* cal_host = nullptr;     // pinned, 4 words per unit
+  uint32_t* cal_dev = nullptr;      // the same memory as the device sees it
+  int64_t cal_capacity = 0;         // units
+  int64_t cal_units = 0;            // units of the stamped launch
+  hipEvent_t cal_done = nullptr;    // end of the stamped launch
 };
+
+namespace {
+
+// Measurement of the XCD halves: enough workgroups per half, a bound on the split, and the
+// difference below which the units stay evenly dealt.
+constexpr int64_t kCalMinUnits = 128;
+constexpr int64_t kCalMinPerHalf = 48;
+constexpr int kCalMaxAttempts = 4;
+constexpr int32_t kSplitMin = 384, kSplitMax = 640, kSplitDeadband = 5;  // of 1024
+
+// The split from the stamps of a launch that dealt unit b to workgroup b: each half's tokens
+// per tick of workgroup time (both halves ran every item's units alike), left in rate[], over
+// the workgroups that ended before the first XCD ran out of work -- after that the XCDs still
+// busy share the chip's bandwidth among fewer workgroups and would look faster than they are.
+// Returns -1 when the stamps are too few to tell, and 0 when the hardware did not place
+// workgroup b on XCD b % 8 (*outcome PKV_XCD_UNMAPPED) or the halves are within the deadband.
+int32_t split_from_stamps(const uint32_t* w, int64_t units, double rate[2], int32_t* outcome) {
+  // start and end ticks relative to the first stamped workgroup's start (32-bit wrap-safe)
+  bool have_ref = false;
+  uint32_t ref = 0;
+  int64_t last_end[pkv::kXcds];
+  for (int x = 0; x < pkv::kXcds; ++x) last_end[x] = -1;
+  for (int64_t b = 0; b < units; ++b) {
+    const uint32_t* s = w + 4 * b;
+    if (!(s[1] & 0x100u)) continue;  // a workgroup with nothing to attend
+    const uint32_t xcc = s[1] & 15u;
+    if (xcc != static_cast<uint32_t>(b % pkv::kXcds)) {
+      *outcome = PKV_XCD_UNMAPPED;
+      return 0;
+    }
+    if (!have_ref) {
+      ref = s[3];
+      have_ref = true;
+    }
+    const int64_t end = static_cast<int64_t>(static_cast<int32_t>(s[3] - ref)) + s[0];
+    last_end[xcc] = std::max(last_end[xcc], end);
+  }
+  int64_t cutoff = -1;  // the first XCD's last end
+  for (int x = 0; x < pkv::kXcds; ++x)
+    if (last_end[x] >= 0) cutoff = cutoff < 0 ? last_end[x] : std::min(cutoff, last_end[x]);
+  double tokens[2] = {0.0, 0.0}, ticks[2] = {0.0, 0.0};
+  int64_t count[2] = {0, 0};
+  for (int64_t b = 0; b < units; ++b) {
+    const uint32_t* s = w + 4 * b;
+    if (!(s[1] & 0x100u) || s[0] == 0 || s[2] == 0) continue;
+    const int64_t end = static_cast<int64_t>(static_cast<int32_t>(s[3] - ref)) + s[0];
+    if (end > cutoff) continue;
+    const int half = static_cast<int>(s[1] & 1u);
+    tokens[half] += s[2];
+    ticks[half] += s[0];
+    ++count[half];
+  }
+  if (count[0] < kCalMinPerHalf || count[1] < kCalMinPerHalf) {
+    *outcome = PKV_XCD_TOO_FEW;
+    return -1;
+  }
+  rate[0] = tokens[0] / ticks[0];
+  rate[1] = tokens[1] / ticks[1];
+  int32_t p = static_cast<int32_t>(std::lround(pkv::kXcdSplitOne * rate[0] / (rate[0] + rate[1])));
+  p = std::min(std::max(p, kSplitMin), kSplitMax);
+  *outcome = PKV_XCD_MEASURED;
+  return std::abs(p - static_cast<int32_t>(pkv::kXcdSplitOne / 2)) < kSplitDeadband ? 0 : p;
+}
+
+// Reads the stamps once their launch is done; never waits for it.
+void poll_calibration(pkv_stepper* st) {
+  const hipError_t e = hipEventQuery(st->cal_done);
+  if (e == hipErrorNotReady) return;
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    st->cal = pkv_stepper::kCalDone;
+    st->cal_outcome = PKV_XCD_FAILED;
+    return;
+  }
+  const int32_t p = split_from_stamps(st->cal_host, st->cal_units, st->cal_rate, &st->cal_outcome);
+  if (p >= 0) {
+    st->xcd_split = p;
+    st->cal = pkv_stepper::kCalDone;
+  } else {
+    st->cal = ++st->cal_attempts < kCalMaxAttempts ? pkv_stepper::kCalPending
+                                                    : pkv_stepper::kCalDone;
+  }
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -158,6 +259,20 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
     pkv_stepper_destroy(st);
     return nullptr;
   }
+  // Calibration stamps: written by the device straight into coherent host memory, read by
+  // the host after the launch's completion event.
+  st->cal_capacity = static_cast<int64_t>(st->max_items) * desc->num_heads;
+  void* cal_dptr = nullptr;
+  if (hipHostMalloc(reinterpret_cast<void**>(&st->cal_host),
+                    static_cast<size_t>(st->cal_capacity) * 16,
+                    hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+      hipHostGetDevicePointer(&cal_dptr, st->cal_host, 0) != hipSuccess ||
+      hipEventCreateWithFlags(&st->cal_done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    pkv_stepper_destroy(st);
+    return nullptr;
+  }
+  st->cal_dev = static_cast<uint32_t*>(cal_dptr);
   return st;
 }
 
@@ -171,6 +286,12 @@ void pkv_stepper_destroy(pkv_stepper_t* st) {
     if (sg.host) (void)hipHostFree(sg.host);
   }
   if (st->handoff) (void)hipEventDestroy(st->handoff);
+  if (st->cal_done) {
+    // a stamped launch still running writes into cal_host
+    if (st->cal == pkv_stepper::kCalInFlight) (void)hipEventSynchronize(st->cal_done);
+    (void)hipEventDestroy(st->cal_done);
+  }
+  if (st->cal_host) (void)hipHostFree(st->cal_host);
   delete st;
 }
 
@@ -202,6 +323,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   if (s != PKV_OK) return s;
   const int32_t L = io->num_layers;
 
+  if (st->cal == pkv_stepper::kCalInFlight) poll_calibration(st);
   auto& sg = st->stage[st->cur ^ 1];
   if (sg.pending) {
     // the prologue that read this host area two steps ago must be done with it
@@ -298,6 +420,11 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
     s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
     if (s != PKV_OK) return s;
   }
+  // The first step with enough units measures the XCD halves on its layer-0 attention.
+  const int64_t units = static_cast<int64_t>(num_items) * st->desc.num_heads;
+  const bool stamp = st->cal == pkv_stepper::kCalPending && L > 0 && units >= kCalMinUnits &&
+                     units <= st->cal_capacity;
+  if (stamp) std::memset(st->cal_host, 0, static_cast<size_t>(units) * 16);
   for (int32_t l = 0; l < L; ++l) {
     if (!(l == 0 && fuse_append)) {
       s = pkv_reshape_and_cache(&st->desc, io->k_new[l], io->v_new[l], io->k_pools[l],
@@ -305,18 +432,56 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       if (s != PKV_OK) return s;
     }
     // timing, when asked for, comes from the attention launch itself
+    const bool stamp_here = stamp && l == 0;
     s = pkv::decode_scheduled_timed(&st->desc, io->out[l], io->q[l], io->k_pools[l],
                                     io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
                                     d_items, num_items, decode_flags, workspace, workspace_bytes,
                                     stream, attn_events ? attn_events[2 * l] : nullptr,
-                                    attn_events ? attn_events[2 * l + 1] : nullptr);
+                                    attn_events ? attn_events[2 * l + 1] : nullptr,
+                                    stamp_here ? 0 : st->xcd_split,
+                                    stamp_here ? st->cal_dev : nullptr);
     if (s != PKV_OK) return s;
+    if (stamp_here) {
+      if (hipEventRecord(st->cal_done, hs) != hipSuccess) return PKV_EHIP;
+      st->cal = pkv_stepper::kCalInFlight;
+      st->cal_units = units;
+    }
   }
   return PKV_OK;
 }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {
   return st ? st->stage[st->cur].dev : nullptr;
+}
+
+int32_t pkv_stepper_xcd_split(const pkv_stepper_t* st) { return st ? st->xcd_split : -1; }
+
+pkv_status_t pkv_stepper_xcd_rates(const pkv_stepper_t* st, double* even, double* odd,
+                                   int32_t* outcome) {
+  if (!st || !even || !odd || !outcome) return PKV_EINVAL;
+  *even = st->cal_rate[0];
+  *odd = st->cal_rate[1];
+  *outcome = st->cal == pkv_stepper::kCalInFlight ? PKV_XCD_IN_FLIGHT : st->cal_outcome;
+  return PKV_OK;
+}
+
+pkv_status_t pkv_stepper_set_xcd_split(pkv_stepper_t* st, int32_t split) {
+  if (!st || split < -1 || split >= pkv::kXcdSplitOne) return PKV_EINVAL;
+  if (st->cal == pkv_stepper::kCalInFlight) {
+    // the stamped launch may still write into cal_host, which a new measurement reuses
+    if (hipEventSynchronize(st->cal_done) != hipSuccess) {
+      (void)hipGetLastError();
+      return PKV_EHIP;
+    }
+  }
+  if (split < 0) {
+    st->cal = pkv_stepper::kCalPending;
+    st->cal_attempts = 0;
+  } else {
+    st->xcd_split = split;
+    st->cal = pkv_stepper::kCalDone;
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -43,7 +43,7 @@ HBM_PEAK_GBS = 8000.0
 # used only while the kernel sources it was taken on are unchanged.
 CSRC = os.path.join(ROOT, "paged_kv_cache_306_amd", "csrc")
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "decode_llama13b_layer_fp16_counters.md")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_decode.hip", "pkv_device.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_decode.hip", "pkv_device.h", "pkv_xcd.h")]
 MQ_COUNTER_PROFILE = os.path.join(ROOT, "profiles", "multi_query_prefix_hit_fp16_counters.md")
 MQ_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("pkv_multi_query.hip", "pkv_device.h")]
 

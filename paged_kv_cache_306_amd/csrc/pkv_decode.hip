@@ -30,6 +30,7 @@
 #include "pkv.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_xcd.h"
 
 #include <hip/hip_ext.h>
 

@@ -764,7 +764,8 @@ def sweep(args, reps: int = 3):
             "decode_launch_us": stat(c["launch_us"], 1), "ms_per_step": stat(c["step_ms"], 4),
             "decode_alg_GBs": stat(c["alg_GBs"], 1),
             "allocated_slots": used * c["bs"], "wasted_slots": int(waste),
-            "waste_frac": round(waste / max(1, used * c["bs"]), 5)}), flush=True)
+            "waste_frac": round(waste / max(1, used * c["bs"]), 5),
+            "xcd_split": b.stepper.xcd_split}), flush=True)
 
 
 def device_or_die():

@@ -494,13 +494,17 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * XCD balance.  The eight XCDs of an MI355X do not stream K/V equally fast (measured: the odd
  * ones take ~10% longer per token), so an even deal of the units leaves the fast half idle at
  * the end of every attention launch.  The stepper measures the two halves on the first step
- * with at least 128 units: that step's layer-0 attention launch deals unit b to workgroup b
- * and each workgroup leaves its duration, XCD and token count in pinned host memory of the
- * stepper's own; a later step reads them once that launch is done (never waiting for it) and
- * from then on every attention launch deals the units with the split P = 1024 * speed(even) /
- * (speed(even) + speed(odd)), bounded to 384..640 (pkv_decode_xcd_grid / _slot_unit above).
+ * with at least 1536 units (enough to fill the chip twice; a smaller launch does not load the
+ * halves enough to tell them apart): that step's layer-0 attention launch deals unit b to
+ * workgroup b and each workgroup leaves its duration, XCD, token count and start tick in
+ * pinned host memory of the stepper's own; a later step reads them once that launch is done
+ * (never waiting for it), keeps the workgroups that ended before the first XCD ran out of
+ * work, and from then on every attention launch deals the units with the split
+ * P = 1024 * speed(even) / (speed(even) + speed(odd)), bounded to 384..640
+ * (pkv_decode_xcd_grid / _slot_unit above).
  * P stays 0 (no weighting) when the halves differ by less than 1%, when the hardware does not
- * place workgroup b on XCD b % 8, or after four steps without enough units.
+ * place workgroup b on XCD b % 8, or after four measuring launches without enough workgroups
+ * per half.
  * pkv_stepper_xcd_split returns the split in use (0: none; -1 for a null stepper);
  * pkv_stepper_set_xcd_split fixes it (0..1023, 0: none) and stops the measurement, or with -1
  * starts a new measurement on the next step (PKV_EINVAL otherwise).  pkv_stepper_xcd_rates

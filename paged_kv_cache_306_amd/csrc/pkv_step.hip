@@ -130,10 +130,12 @@ struct pkv_stepper {
 
 namespace {
 
-// Measurement of the XCD halves: enough workgroups per half, a bound on the split, and the
-// difference below which the units stay evenly dealt.
-constexpr int64_t kCalMinUnits = 128;
-constexpr int64_t kCalMinPerHalf = 48;
+// Measurement of the XCD halves: a launch that fills the chip (twice the 768 workgroups the
+// fp16 decode keeps resident; below that the halves do not compete for bandwidth and look
+// alike), enough measured workgroups per half, a bound on the split, and the difference below
+// which the units stay evenly dealt.
+constexpr int64_t kCalMinUnits = 1536;
+constexpr int64_t kCalMinPerHalf = 256;
 constexpr int kCalMaxAttempts = 4;
 constexpr int32_t kSplitMin = 384, kSplitMax = 640, kSplitDeadband = 5;  // of 1024
 

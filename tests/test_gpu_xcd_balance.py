@@ -13,22 +13,28 @@ from gpu_util import check_close, device, to_dev
 
 pytestmark = pytest.mark.gpu
 
-H, D, BS, DT = 8, 128, 16, "f16"
+D, BS, DT = 128, 16, "f16"
 STEPS = 2
 
 
-def _lengths(seed):
+def _lengths(seed, full=False):
     g = W.rng(seed)
+    if full:
+        # the LLaMA-13B layer's shape: 64 sequences x 40 heads = 2560 units, more than the
+        # chip holds at once, so the stepper measures its XCD halves under load
+        return g.integers(128, 2049, 64).astype(np.int64)
     # single-pass lengths and a few sequences long enough to be split into partitions
     return np.concatenate([g.integers(1, 2049, 36), g.integers(4097, 6001, 4)]).astype(np.int64)
 
 
-def _run(split, seed=77):
-    """One stepper over a fresh copy of the same batch; `split` None: the stepper measures it.
-    Returns (outputs per step, the split in use after the last step, oracle inputs)."""
+def _run(split, seed=77, full=False):
+    """One stepper over a fresh copy of the same batch (8 heads; the full batch: 40); `split`
+    None: the stepper measures it.  Returns (outputs per step, the split in use after the last
+    step, the measurement's rates and outcome, oracle inputs)."""
     import torch
     dev = device()
-    start = _lengths(seed)
+    H = 40 if full else 8
+    start = _lengths(seed, full)
     S = len(start)
     MB = int((start.max() + STEPS + BS - 1) // BS)
     NB = int(sum((L + STEPS + BS - 1) // BS for L in start) * 1.3) + 8
@@ -99,8 +105,14 @@ def test_outputs_do_not_depend_on_the_split():
             assert np.array_equal(outs[i].view(np.uint16), base[i].view(np.uint16)), (split, i)
 
 
+def test_small_batch_is_not_measured():
+    # 320 units fit on the chip at once: no measurement, the units stay evenly dealt
+    _, used, (even, odd, outcome), _ = _run(None)
+    assert used == 0 and outcome == pkv.PKV_XCD_NONE and even == 0 and odd == 0
+
+
 def test_stepper_measures_the_split():
-    outs, used, (even, odd, outcome), inputs = _run(None)
+    outs, used, (even, odd, outcome), inputs = _run(None, seed=78, full=True)
     print(f"[xcd] measured split {used} of 1024 for the even XCDs; tokens per tick "
           f"even {even:.4f} odd {odd:.4f}; outcome {outcome}", flush=True)
     assert outcome in (pkv.PKV_XCD_MEASURED, pkv.PKV_XCD_UNMAPPED)
@@ -117,7 +129,7 @@ def test_stepper_measures_the_split():
 def test_set_split_arguments():
     import torch
     dev = device()
-    NB, MB = 64, 4
+    H, NB, MB = 8, 64, 4
     a = pkv.BlockAllocator(NB, BS)
     a.add_seq(0, 5)
     kp = torch.zeros((NB, H, BS, D), dtype=torch.float16, device=dev)

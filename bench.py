@@ -240,7 +240,7 @@ def calibrate_read(mib: int):
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(5):
-        if probe(buf.data_ptr(), n, 0, None, 0, 1, sink.data_ptr(), 4096, stream) != 0:
+        if probe(buf.data_ptr(), n, 0, None, 0, 1, 0, sink.data_ptr(), 4096, stream) != 0:
             raise RuntimeError("pkv_probe_read failed")
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_read_bytes": n, "reads": 5}), flush=True)
@@ -281,8 +281,10 @@ def decode_tile_list(workload, seed):
     return np.concatenate(parts), 2 * NB * H, tile, sp
 
 
-def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
-    """Plain nontemporal read of exactly the K/V tiles one decode layer of `workload` reads."""
+def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream, split=0):
+    """Plain nontemporal read of exactly the K/V tiles one decode layer of `workload` reads;
+    with `split` (of 1024) the even XCDs read that share of them, as the decode deals its
+    units."""
     import torch
     idx, n_buf_tiles, tile, _ = decode_tile_list(workload, seed)
     nbytes = n_buf_tiles * tile
@@ -293,8 +295,8 @@ def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
     read = len(idx) * tile
 
     def launch():
-        st = probe(buf.data_ptr(), nbytes, tile, order.data_ptr(), len(idx), 1, sink.data_ptr(),
-                   wgs, stream)
+        st = probe(buf.data_ptr(), nbytes, tile, order.data_ptr(), len(idx), 1, split,
+                   sink.data_ptr(), wgs, stream)
         if st != 0:
             raise RuntimeError(f"pkv_probe_read returned {st}")
     for _ in range(3):
@@ -308,6 +310,7 @@ def decode_tiles_ceiling(probe, workload, seed, wgs, sink, stream):
     torch.cuda.synchronize()
     t = float(np.median([a.elapsed_time(z) for a, z in evs])) / 1e3
     return {"pattern": f"decode_tiles_{workload}", "tile_bytes": tile, "nontemporal": True,
+            "xcd_split": split,
             "bytes": int(read), "us": round(t * 1e6, 1), "GB/s": round(read / t / 1e9, 1),
             "frac_of_peak": round(read / t / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -323,8 +326,8 @@ def load_probe():
     probe = ctypes.CDLL(path).pkv_probe_read
     probe.restype = ctypes.c_int32
     probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                      ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
-                      ctypes.c_void_p]
+                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                      ctypes.c_int32, ctypes.c_void_p]
     return probe
 
 
@@ -379,19 +382,22 @@ def mfma_ceiling(args):
                           "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS["f16"], 4)}), flush=True)
 
 
-def own_tiles_read_rate(workload, seed):
+def own_tiles_read_rate(workload, seed, split=0):
     """GB/s of a plain nontemporal read of exactly the K/V tiles one decode launch of
-    `workload` reads, in one launch of that size (the decode launch's practical ceiling), or
-    None when the probe library is missing."""
+    `workload` reads, in one launch of that size (the decode launch's practical ceiling): with
+    the tiles dealt evenly to the XCDs, and with the decode's `split` when it has one.  Returns
+    (even, with the split or None), or None when the probe library is missing."""
     import torch
     probe = load_probe()
     if probe is None:
         return None
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
-    row = decode_tiles_ceiling(probe, workload, seed, 4096, sink, stream)
+    even = decode_tiles_ceiling(probe, workload, seed, 4096, sink, stream)["GB/s"]
+    weighted = (decode_tiles_ceiling(probe, workload, seed, 4096, sink, stream, split)["GB/s"]
+                if split > 0 else None)
     torch.cuda.empty_cache()
-    return row["GB/s"]
+    return even, weighted
 
 
 def ceiling_bench(args):
@@ -425,7 +431,7 @@ def ceiling_bench(args):
 
         def launch():
             st = probe(buf.data_ptr(), nbytes, tb, order.data_ptr() if order is not None else None,
-                       n_tiles, nt, sink.data_ptr(), wgs, stream)
+                       n_tiles, nt, 0, sink.data_ptr(), wgs, stream)
             if st != 0:
                 raise RuntimeError(f"pkv_probe_read returned {st}")
         for _ in range(3):
@@ -1134,10 +1140,15 @@ def main():
     # timed steps; 16-token blocks at the seeded placement, pools small enough for a copy)
     if (args.workload in ("llama13b_layer", "long_context") and args.block_size == 16
             and args.placement == "permuted"):
-        own = own_tiles_read_rate(args.workload, args.seed)
+        own = own_tiles_read_rate(args.workload, args.seed, b.stepper.xcd_split)
         if own:
-            res["roofline"]["own_tiles_read_GBs"] = own
-            res["roofline"]["frac_of_own_tiles_read"] = round(achieved / own, 4)
+            # the ceiling is the better of the two reads: evenly dealt, or weighted like the
+            # decode launches
+            best = max(x for x in own if x)
+            res["roofline"]["own_tiles_read_GBs"] = best
+            res["roofline"]["own_tiles_read_even_deal_GBs"] = own[0]
+            res["roofline"]["own_tiles_read_weighted_GBs"] = own[1]
+            res["roofline"]["frac_of_own_tiles_read"] = round(achieved / best, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_units, args.cpu_bytes)
     print(json.dumps(res), flush=True)

@@ -27,6 +27,11 @@ extern "C" {
  *                   when tile_bytes = 0.  Entries are not checked on the device.
  *   num_tiles       tiles to visit (0 < num_tiles, num_tiles * tile_bytes <= bytes).
  *   nontemporal     nonzero: nontemporal loads (the decode kernel's), else ordinary loads.
+ *   split           0, or with tiles 1..1023: the share (of 1024) of the visit that the waves
+ *                   of the even XCDs read (workgroup b runs on XCD b % 8; the first
+ *                   num_tiles * split / 1024 entries of `order`), the odd XCDs reading the
+ *                   rest -- the decode launches' weighting of the two halves; workgroups must
+ *                   then be a multiple of 8.
  *   sink            device uint32 [1]; written only when a data-dependent hash takes one
  *                   particular value, which keeps the loads from being removed.
  *   workgroups      grid size (1 .. 65536), 256 threads each.
@@ -34,7 +39,7 @@ extern "C" {
  * Returns 0 on success, 1 for invalid arguments (nothing enqueued), 2 when the launch fails.
  */
 int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes, const int32_t* order,
-                       int64_t num_tiles, int32_t nontemporal, uint32_t* sink,
+                       int64_t num_tiles, int32_t nontemporal, int32_t split, uint32_t* sink,
                        int32_t workgroups, void* stream);
 
 /* Sustained matrix-core rate: enqueue one launch of `workgroups` workgroups of 256 threads,

@@ -58,23 +58,37 @@ __global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4* __re
 
 // Whole tiles of VPL x 1 KiB (one wave-wide 16-byte load covers 1 KiB): wave w of the grid
 // visits order[w], order[w + waves], ...; TILES of them are in flight at once, so every lane
-// keeps kTileLoadsInFlight loads outstanding whatever the tile size.
+// keeps kTileLoadsInFlight loads outstanding whatever the tile size.  split > 0 (of 1024):
+// the waves of the even XCDs (workgroup b runs on XCD b % 8) visit the first
+// num_tiles * split / 1024 entries of the order and those of the odd XCDs the rest, each half
+// with its own waves -- the decode launches' weighting of the two halves.
 template <bool NT, int VPL>
 __global__ __launch_bounds__(kThreads) void read_tiles_kernel(const u32x4* __restrict__ p,
                                                               const int32_t* __restrict__ order,
-                                                              int64_t num_tiles,
+                                                              int64_t num_tiles, int split,
                                                               uint32_t* __restrict__ sink) {
   constexpr int TILES = kTileLoadsInFlight / VPL;
+  constexpr int kWavesPerGroup = kThreads / 64;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
-  const int64_t waves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  int64_t waves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
+  int64_t first = 0, last = num_tiles;
+  if (split > 0) {
+    const int x = static_cast<int>(blockIdx.x % 8);
+    const int64_t even_tiles = num_tiles * split / 1024;
+    first = (x & 1) ? even_tiles : 0;
+    last = (x & 1) ? num_tiles : even_tiles;
+    wave = ((static_cast<int64_t>(blockIdx.x / 8) * 4 + (x >> 1)) * kWavesPerGroup) +
+           (threadIdx.x >> 6);
+    waves = static_cast<int64_t>(gridDim.x / 2) * kWavesPerGroup;
+  }
   uint32_t acc = 0;
-  for (int64_t t0 = wave; t0 < num_tiles; t0 += TILES * waves) {
+  for (int64_t t0 = first + wave; t0 < last; t0 += TILES * waves) {
     u32x4 v[TILES][VPL];
 #pragma unroll
     for (int k = 0; k < TILES; ++k) {
       const int64_t t = t0 + k * waves;
-      const bool on = t < num_tiles;
+      const bool on = t < last;
       const int64_t base = static_cast<int64_t>(on ? order[t] : 0) * (64 * VPL) + lane;
 #pragma unroll
       for (int u = 0; u < VPL; ++u)
@@ -90,19 +104,19 @@ __global__ __launch_bounds__(kThreads) void read_tiles_kernel(const u32x4* __res
 
 template <bool NT>
 hipError_t launch_tiles(const u32x4* p, const int32_t* order, int64_t num_tiles, int tile_bytes,
-                        uint32_t* sink, int wgs, hipStream_t s) {
+                        int split, uint32_t* sink, int wgs, hipStream_t s) {
   switch (tile_bytes) {
     case 2048:
       hipLaunchKernelGGL((read_tiles_kernel<NT, 2>), dim3(wgs), dim3(kThreads), 0, s, p, order,
-                         num_tiles, sink);
+                         num_tiles, split, sink);
       break;
     case 4096:
       hipLaunchKernelGGL((read_tiles_kernel<NT, 4>), dim3(wgs), dim3(kThreads), 0, s, p, order,
-                         num_tiles, sink);
+                         num_tiles, split, sink);
       break;
     default:
       hipLaunchKernelGGL((read_tiles_kernel<NT, 8>), dim3(wgs), dim3(kThreads), 0, s, p, order,
-                         num_tiles, sink);
+                         num_tiles, split, sink);
       break;
   }
   return hipGetLastError();
@@ -163,9 +177,12 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float* _
 
 extern "C" int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_bytes,
                                   const int32_t* order, int64_t num_tiles, int32_t nontemporal,
-                                  uint32_t* sink, int32_t workgroups, void* stream) {
+                                  int32_t split, uint32_t* sink, int32_t workgroups,
+                                  void* stream) {
   if (!buf || !sink || bytes <= 0 || bytes % 16 ||
       reinterpret_cast<uintptr_t>(buf) % 16 || workgroups < 1 || workgroups > 65536)
+    return 1;
+  if (split < 0 || split >= 1024 || (split > 0 && (tile_bytes == 0 || workgroups % 8)))
     return 1;
   if (tile_bytes != 0 && tile_bytes != 2048 && tile_bytes != 4096 && tile_bytes != 8192)
     return 1;
@@ -184,8 +201,9 @@ extern "C" int32_t pkv_probe_read(const void* buf, int64_t bytes, int32_t tile_b
                          bytes / 16, sink);
     e = hipGetLastError();
   } else {
-    e = nontemporal ? launch_tiles<true>(p, order, num_tiles, tile_bytes, sink, workgroups, s)
-                    : launch_tiles<false>(p, order, num_tiles, tile_bytes, sink, workgroups, s);
+    e = nontemporal
+            ? launch_tiles<true>(p, order, num_tiles, tile_bytes, split, sink, workgroups, s)
+            : launch_tiles<false>(p, order, num_tiles, tile_bytes, split, sink, workgroups, s);
   }
   return e == hipSuccess ? 0 : 2;
 }

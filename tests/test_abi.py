@@ -298,17 +298,19 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     f = lib.pkv_probe_read
     f.restype = ctypes.c_int32
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
-                  ctypes.c_void_p]
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_void_p]
     p, sink, order = 1 << 20, 1 << 21, 1 << 22        # never dereferenced: rejected first
-    ok = dict(buf=p, bytes=1 << 20, tile=4096, order=order, tiles=256, nt=1, sink=sink, wgs=64)
+    ok = dict(buf=p, bytes=1 << 20, tile=4096, order=order, tiles=256, nt=1, split=0, sink=sink,
+              wgs=64)
     bad = [dict(buf=None), dict(sink=None), dict(bytes=0), dict(bytes=100), dict(buf=p + 8),
            dict(wgs=0), dict(wgs=65537), dict(tile=1024), dict(tile=3000), dict(order=None),
-           dict(tiles=0), dict(tiles=257)]
+           dict(tiles=0), dict(tiles=257), dict(split=-1), dict(split=1024),
+           dict(split=512, wgs=63), dict(split=512, tile=0)]
     for change in bad:
         a = {**ok, **change}
-        st = f(a["buf"], a["bytes"], a["tile"], a["order"], a["tiles"], a["nt"], a["sink"],
-               a["wgs"], None)
+        st = f(a["buf"], a["bytes"], a["tile"], a["order"], a["tiles"], a["nt"], a["split"],
+               a["sink"], a["wgs"], None)
         assert st == 1, change
     m = lib.pkv_probe_mfma
     m.restype = ctypes.c_int32

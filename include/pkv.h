@@ -545,6 +545,15 @@ pkv_status_t pkv_stepper_set_xcd_split(pkv_stepper_t* st, int32_t split);
 #define PKV_XCD_FAILED 5     /* the runtime reported an error on the stamped launch */
 pkv_status_t pkv_stepper_xcd_rates(const pkv_stepper_t* st, double* even, double* odd,
                                    int32_t* outcome);
+/* The measurement itself, host only: from `units` stamps of a launch that dealt unit b to
+ * workgroup b (4 uint32 each: duration in 100 MHz ticks, XCD | 0x100 for a workgroup that
+ * attended tokens, tokens, low 32 bits of its start tick), the split the stepper would take:
+ * -1 when too few workgroups per half ended before the first XCD ran out of work, 0 when
+ * workgroup b did not run on XCD b % 8 or the halves differ by less than 1%, else 384..640.
+ * even / odd / outcome (host outs) as pkv_stepper_xcd_rates gives them.  -2 for bad
+ * arguments. */
+int32_t pkv_xcd_split_from_stamps(const uint32_t* stamps, int64_t units, double* even,
+                                  double* odd, int32_t* outcome);
 pkv_status_t pkv_stepper_check(const pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
                                int32_t max_seqs, int32_t max_blocks_per_seq, const int64_t* seqs,
                                int32_t n, const pkv_layer_io_t* io, const void* workspace,

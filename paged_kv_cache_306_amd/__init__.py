@@ -102,6 +102,8 @@ _SIGNATURES = {
     "pkv_stepper_set_xcd_split": (_i32, [_p, _i32]),
     "pkv_stepper_xcd_rates": (_i32, [_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double), _pi32]),
+    "pkv_xcd_split_from_stamps": (_i32, [_p, _i64, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double), _pi32]),
     "pkv_stepper_check": (_i32, [_p, _pdesc, _i32, _i32, _p, _i32, _p, _p, _sz, _pi32]),
 }
 
@@ -176,6 +178,18 @@ def decode_xcd_grid(units: int, split: int) -> int:
     """Workgroups an attention launch of ``units`` units takes under the XCD split (of 1024;
     0: one per unit), pkv_decode_xcd_grid; -1 for bad arguments."""
     return int(_lib().pkv_decode_xcd_grid(int(units), int(split)))
+
+
+def xcd_split_from_stamps(stamps):
+    """The split the step driver takes from a stamped launch's stamps (uint32 numpy [units][4]:
+    duration ticks, XCD | 0x100, tokens, start tick), with the halves' rates and the outcome:
+    (split, even, odd, outcome) (pkv_xcd_split_from_stamps)."""
+    import numpy as np
+    w = np.ascontiguousarray(np.asarray(stamps, dtype=np.uint32))
+    e, o, k = ctypes.c_double(), ctypes.c_double(), _i32()
+    p = _lib().pkv_xcd_split_from_stamps(w.ctypes.data_as(ctypes.c_void_p), int(w.shape[0]),
+                                         ctypes.byref(e), ctypes.byref(o), ctypes.byref(k))
+    return int(p), e.value, o.value, k.value
 
 
 def decode_xcd_slot_unit(slot: int, units: int, split: int) -> int:

@@ -459,6 +459,17 @@ const void* pkv_stepper_last_index(const pkv_stepper_t* st) {
 
 int32_t pkv_stepper_xcd_split(const pkv_stepper_t* st) { return st ? st->xcd_split : -1; }
 
+int32_t pkv_xcd_split_from_stamps(const uint32_t* stamps, int64_t units, double* even,
+                                  double* odd, int32_t* outcome) {
+  if (!stamps || units <= 0 || !even || !odd || !outcome) return -2;
+  double rate[2] = {0.0, 0.0};
+  *outcome = PKV_XCD_NONE;
+  const int32_t p = split_from_stamps(stamps, units, rate, outcome);
+  *even = rate[0];
+  *odd = rate[1];
+  return p;
+}
+
 pkv_status_t pkv_stepper_xcd_rates(const pkv_stepper_t* st, double* even, double* odd,
                                    int32_t* outcome) {
   if (!st || !even || !odd || !outcome) return PKV_EINVAL;

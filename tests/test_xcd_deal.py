@@ -58,3 +58,78 @@ def test_bad_arguments():
     assert pkv.decode_xcd_slot_unit(-1, 10, 512) == -2
     assert pkv.decode_xcd_slot_unit(pkv.decode_xcd_grid(10, 600), 10, 600) == -2
     assert pkv.decode_xcd_slot_unit(0, 10, 1024) == -2
+
+
+# ---- the measurement the step driver makes from one stamped launch (host only)
+
+def _launch(units, speed_even, speed_odd, seed=0, slots_per_xcd=96, tail_boost=1.0):
+    """Stamps of a simulated launch dealing unit b to workgroup b (XCD b % 8): each XCD runs its
+    units in order on `slots_per_xcd` slots at its half's tokens per tick; once the first XCD
+    has no work left, the others run `tail_boost` times faster (they share its bandwidth)."""
+    g = np.random.default_rng(seed)
+    tokens = np.sort(g.integers(128, 2049, units))[::-1]
+    start = np.zeros(units)
+    end = np.zeros(units)
+    for x in range(8):
+        free = np.zeros(slots_per_xcd)
+        for b in range(x, units, 8):
+            i = int(np.argmin(free))
+            speed = speed_even if x % 2 == 0 else speed_odd
+            start[b] = free[i]
+            end[b] = free[i] + tokens[b] / speed
+            free[i] = end[b]
+    first_idle = min(end[x::8].max() for x in range(8))
+    late = end > first_idle          # the part past the first XCD's end runs faster
+    end[late] = first_idle + (end[late] - np.maximum(start[late], first_idle)) / tail_boost + \
+        np.maximum(0, first_idle - start[late])
+    st = np.zeros((units, 4), np.uint32)
+    base = 123456789                 # arbitrary start tick, 32-bit wrap-safe
+    st[:, 0] = np.maximum(1, np.round(end - start)).astype(np.uint32)
+    st[:, 1] = 0x100 | (np.arange(units) % 8)
+    st[:, 2] = tokens
+    st[:, 3] = (base + np.round(start).astype(np.int64)) % (1 << 32)
+    return st
+
+
+def test_measured_split_follows_the_halves_speeds():
+    for even, odd in [(1.0, 0.9), (1.0, 0.8), (0.9, 1.0)]:
+        p, re_, ro, outcome = pkv.xcd_split_from_stamps(_launch(2560, even, odd))
+        assert outcome == pkv.PKV_XCD_MEASURED
+        assert abs(re_ / ro - even / odd) < 0.02
+        assert abs(p - round(1024 * even / (even + odd))) <= 3
+
+
+def test_workgroups_after_the_first_xcd_ends_are_left_out():
+    # in the tail the remaining XCDs run faster; counting them would understate the gap
+    p_all_fast, _, _, _ = pkv.xcd_split_from_stamps(_launch(2560, 1.0, 0.9, tail_boost=3.0))
+    p_plain, _, _, _ = pkv.xcd_split_from_stamps(_launch(2560, 1.0, 0.9))
+    assert abs(p_all_fast - p_plain) <= 3
+    assert p_plain > 530
+
+
+def test_equal_halves_keep_the_even_deal():
+    p, re_, ro, outcome = pkv.xcd_split_from_stamps(_launch(2560, 1.0, 1.0))
+    assert (p, outcome) == (0, pkv.PKV_XCD_MEASURED) and abs(re_ / ro - 1) < 0.01
+
+
+def test_split_is_bounded():
+    # 2:1 would ask for 683 / 341 of 1024
+    p, _, _, outcome = pkv.xcd_split_from_stamps(_launch(2560, 1.0, 0.5))
+    assert outcome == pkv.PKV_XCD_MEASURED and p == 640
+    p, _, _, outcome = pkv.xcd_split_from_stamps(_launch(2560, 0.5, 1.0))
+    assert outcome == pkv.PKV_XCD_MEASURED and p == 384
+
+
+def test_unexpected_xcd_placement_turns_weighting_off():
+    st = _launch(2560, 1.0, 0.9)
+    st[17, 1] = 0x100 | 3                    # workgroup 17 reported on XCD 3, not 1
+    p, _, _, outcome = pkv.xcd_split_from_stamps(st)
+    assert (p, outcome) == (0, pkv.PKV_XCD_UNMAPPED)
+
+
+def test_too_few_workgroups_cannot_tell():
+    st = _launch(2560, 1.0, 0.9)
+    st[200:, 1] = 0                          # only 200 workgroups attended tokens
+    p, _, _, outcome = pkv.xcd_split_from_stamps(st)
+    assert (p, outcome) == (-1, pkv.PKV_XCD_TOO_FEW)
+    assert pkv.lib().pkv_xcd_split_from_stamps(None, 4, None, None, None) == -2

@@ -165,6 +165,13 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
  * outside the grid).  Outputs do not depend on the deal. */
 int64_t pkv_decode_xcd_grid(int64_t units, int32_t split);
 int64_t pkv_decode_xcd_slot_unit(int64_t slot, int64_t units, int32_t split);
+/* The split the stand-alone decode calls (pkv_paged_attention_decode, _scheduled, _noalloc) on
+ * the current device deal their units with: 0 (evenly) until a step driver on the device has
+ * measured one (see "XCD balance" below), which then applies to them too, or until
+ * pkv_decode_set_xcd_split sets it (0..1023; PKV_EINVAL otherwise).  pkv_decode_xcd_split
+ * returns it. */
+pkv_status_t pkv_decode_set_xcd_split(int32_t split);
+int32_t pkv_decode_xcd_split(void);
 
 /* The same attention as pkv_paged_attention_decode, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -54,6 +54,8 @@ _SIGNATURES = {
     "pkv_decode_single_pass_max": (_i32, []),
     "pkv_decode_xcd_grid": (_i64, [_i64, _i32]),
     "pkv_decode_xcd_slot_unit": (_i64, [_i64, _i64, _i32]),
+    "pkv_decode_set_xcd_split": (_i32, [_i32]),
+    "pkv_decode_xcd_split": (_i32, []),
     "pkv_decode_schedule": (_i32, [_pdesc, _p, _i32, _i32, _p, _i32]),
     "pkv_decode_schedule_grouped": (_i32, [_pdesc, _p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_decode_scheduled": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _i32,
@@ -190,6 +192,17 @@ def xcd_split_from_stamps(stamps):
     p = _lib().pkv_xcd_split_from_stamps(w.ctypes.data_as(ctypes.c_void_p), int(w.shape[0]),
                                          ctypes.byref(e), ctypes.byref(o), ctypes.byref(k))
     return int(p), e.value, o.value, k.value
+
+
+def decode_set_xcd_split(split: int) -> None:
+    """Split (of 1024; 0: even) the stand-alone decode calls on the current device deal their
+    units with (pkv_decode_set_xcd_split)."""
+    _check(_lib().pkv_decode_set_xcd_split(int(split)), "pkv_decode_set_xcd_split")
+
+
+def decode_xcd_split() -> int:
+    """The current device's split for the stand-alone decode calls (pkv_decode_xcd_split)."""
+    return int(_lib().pkv_decode_xcd_split())
 
 
 def decode_xcd_slot_unit(slot: int, units: int, split: int) -> int:

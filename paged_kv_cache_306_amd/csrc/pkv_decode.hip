@@ -35,6 +35,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -540,6 +541,28 @@ constexpr int kMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[kMaxDevices] = {};
 
+// The XCD split the stand-alone decode calls deal their units with, per device (0: evenly):
+// what a step driver on that device measured last, or what pkv_decode_set_xcd_split set.
+static std::atomic<int32_t> g_device_split[kMaxDevices];
+
+static int32_t current_device_split() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return dev >= 0 && dev < kMaxDevices ? g_device_split[dev].load(std::memory_order_relaxed) : 0;
+}
+
+void set_device_xcd_split(int32_t split) {
+  int dev = -1;
+  if (split < 0 || split >= kXcdSplitOne || hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  if (dev >= 0 && dev < kMaxDevices) g_device_split[dev].store(split, std::memory_order_relaxed);
+}
+
 static pkv_status_t scratch_for_current_device(void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) {
@@ -589,6 +612,20 @@ int32_t pkv_decode_partition_tokens(const pkv_cache_desc_t* desc, int32_t num_se
 }
 
 int32_t pkv_decode_single_pass_max(void) { return kSingleMax; }
+
+pkv_status_t pkv_decode_set_xcd_split(int32_t split) {
+  if (split < 0 || split >= kXcdSplitOne) return PKV_EINVAL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PKV_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PKV_EUNSUPPORTED;
+  g_device_split[dev].store(split, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int32_t pkv_decode_xcd_split(void) { return current_device_split(); }
 
 int64_t pkv_decode_xcd_grid(int64_t units, int32_t split) {
   if (units < 0 || split < 0 || split >= kXcdSplitOne) return -1;
@@ -689,7 +726,7 @@ pkv_status_t pkv_paged_attention_decode(const pkv_cache_desc_t* desc, void* out,
                                         size_t workspace_bytes, pkv_stream_t stream) {
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, nullptr, 0, 0u, workspace, workspace_bytes,
-                     stream);
+                     stream, nullptr, nullptr, current_device_split());
 }
 
 pkv_status_t pkv_paged_attention_decode_scheduled(
@@ -701,7 +738,7 @@ pkv_status_t pkv_paged_attention_decode_scheduled(
   if (!work_items) return PKV_EINVAL;
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, work_items, num_items, flags, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, nullptr, nullptr, current_device_split());
 }
 
 pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, void* out,
@@ -726,7 +763,8 @@ pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, vo
   }
   return decode_impl(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, max_context_len, scale, nullptr, 0, 0u, ws,
-                     ws ? static_cast<size_t>(PKV_DECODE_NOALLOC_SCRATCH_BYTES) : 0, stream);
+                     ws ? static_cast<size_t>(PKV_DECODE_NOALLOC_SCRATCH_BYTES) : 0, stream,
+                     nullptr, nullptr, current_device_split());
 }
 
 }  // extern "C"

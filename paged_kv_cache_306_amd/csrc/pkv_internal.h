@@ -50,6 +50,10 @@ pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, con
                                     void* ev_start, void* ev_stop, int32_t xcd_split = 0,
                                     uint32_t* stamps = nullptr);
 
+// The XCD split the stand-alone decode calls on the current device use from now on (a step
+// driver's measurement); out-of-range values are ignored.
+void set_device_xcd_split(int32_t split);
+
 // Host checks of a cache append's slots (distinct within [0, num_slots); others are skipped)
 // and of a block copy's pairs (among in-range pairs, destinations distinct and never a
 // source).  `scratch` is reused between calls to avoid allocating.

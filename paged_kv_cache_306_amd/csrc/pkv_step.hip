@@ -207,6 +207,8 @@ void poll_calibration(pkv_stepper* st) {
   if (p >= 0) {
     st->xcd_split = p;
     st->cal = pkv_stepper::kCalDone;
+    // the device's stand-alone decode calls deal their units the same way from now on
+    if (st->cal_outcome == PKV_XCD_MEASURED) pkv::set_device_xcd_split(p);
   } else {
     st->cal = ++st->cal_attempts < kCalMaxAttempts ? pkv_stepper::kCalPending
                                                     : pkv_stepper::kCalDone;

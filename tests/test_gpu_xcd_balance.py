@@ -147,3 +147,49 @@ def test_set_split_arguments():
     st.step(np.zeros(1, np.int64))
     torch.cuda.synchronize()
     assert st.xcd_split == 700
+
+
+def test_stand_alone_decode_takes_the_device_split():
+    """pkv_paged_attention_decode (and _noalloc) deal their units by the device's split, and
+    their outputs do not depend on it."""
+    import torch
+    dev = device()
+    g = W.rng(91)
+    H, S, MB = 40, 48, 128
+    lens = g.integers(1, 2049, S).astype(np.int32)
+    NB = int(sum(-(-int(L) // BS) for L in lens)) + 8
+    kp = to_dev(W.normal_values(g, (NB, H, BS, D), DT), DT, dev)
+    vp = to_dev(W.normal_values(g, (NB, H, BS, D), DT), DT, dev)
+    q = to_dev(W.normal_values(g, (S, H, D), DT), DT, dev)
+    tables = np.full((S, MB), 0, np.int32)
+    perm = g.permutation(NB)
+    used = 0
+    for s, L in enumerate(lens.tolist()):
+        nb = -(-L // BS)
+        tables[s, :nb] = perm[used:used + nb]
+        used += nb
+    bt = torch.from_numpy(tables).to(dev)
+    cl = torch.from_numpy(lens).to(dev)
+    before = pkv.decode_xcd_split()
+    assert 0 <= before < 1024
+    outs = {}
+    try:
+        for split in (0, 600, 400):
+            pkv.decode_set_xcd_split(split)
+            assert pkv.decode_xcd_split() == split
+            out = torch.empty_like(q)
+            pkv.paged_attention_decode(out, q, kp, vp, bt, cl, 1 / math.sqrt(D), 2048)
+            out2 = torch.empty_like(q)
+            pkv.paged_attention_decode_noalloc(out2, q, kp, vp, bt, cl, 1 / math.sqrt(D), 2048)
+            torch.cuda.synchronize()
+            outs[split] = (W.from_torch(out, DT).copy(), W.from_torch(out2, DT).copy())
+        with pytest.raises(pkv.PkvError):
+            pkv.decode_set_xcd_split(1024)
+    finally:
+        pkv.decode_set_xcd_split(before)
+    for split in (600, 400):
+        for a, b in zip(outs[split], outs[0]):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), split
+    ref = oracle.paged_attention_decode(W.from_torch(q, DT), W.from_torch(kp, DT),
+                                        W.from_torch(vp, DT), tables, lens, 1 / math.sqrt(D), DT)
+    check_close(oracle.decode(outs[600][0], DT), ref, DT, "stand-alone decode, split 600")

@@ -193,3 +193,60 @@ def test_stand_alone_decode_takes_the_device_split():
     ref = oracle.paged_attention_decode(W.from_torch(q, DT), W.from_torch(kp, DT),
                                         W.from_torch(vp, DT), tables, lens, 1 / math.sqrt(D), DT)
     check_close(oracle.decode(outs[600][0], DT), ref, DT, "stand-alone decode, split 600")
+
+
+def test_scheduled_shared_prefix_decode_takes_the_device_split():
+    """The scheduled entry point with cache-allocating loads (shared prefixes, grouped work list,
+    a few sequences split into partitions) deals its units by the device's split as well, with
+    outputs that do not depend on it."""
+    import torch
+    dev = device()
+    g = W.rng(93)
+    H, groups, per = 40, 12, 4
+    prefix = 32                                   # shared blocks of each group (512 tokens)
+    S = groups * per
+    tails = g.integers(0, 257, S)
+    tails[:3] = g.integers(4000, 5000, 3)         # long enough to be split into partitions
+    lens = (prefix * BS + tails).astype(np.int32)
+    MB = int(-(-int(lens.max()) // BS))
+    NB = groups * prefix + int(sum(-(-int(t) // BS) for t in tails)) + 8
+    perm = g.permutation(NB)
+    tables = np.zeros((S, MB), np.int32)
+    used = 0
+    for k in range(groups):
+        shared = perm[used:used + prefix]
+        used += prefix
+        for j in range(per):
+            s = k * per + j
+            nb = -(-int(tails[s]) // BS)
+            tables[s, :prefix] = shared
+            tables[s, prefix:prefix + nb] = perm[used:used + nb]
+            used += nb
+    kp = to_dev(W.normal_values(g, (NB, H, BS, D), DT), DT, dev)
+    vp = to_dev(W.normal_values(g, (NB, H, BS, D), DT), DT, dev)
+    q = to_dev(W.normal_values(g, (S, H, D), DT), DT, dev)
+    bt = torch.from_numpy(tables).to(dev)
+    cl = torch.from_numpy(lens).to(dev)
+    maxlen = int(lens.max())
+    desc = pkv.desc_for_pool(kp)
+    items = torch.from_numpy(pkv.decode_schedule(desc, lens, maxlen,
+                                                 group_keys=np.arange(S) // per)).to(dev)
+    scale = 1 / math.sqrt(D)
+    before = pkv.decode_xcd_split()
+    outs = {}
+    try:
+        for split in (0, 600, 400):
+            print(f"[xcd] scheduled shared-prefix decode, split {split}", flush=True)
+            pkv.decode_set_xcd_split(split)
+            out = torch.empty_like(q)
+            pkv.paged_attention_decode(out, q, kp, vp, bt, cl, scale, maxlen, work_items=items,
+                                       shared_kv=True)
+            torch.cuda.synchronize()
+            outs[split] = W.from_torch(out, DT).copy()
+    finally:
+        pkv.decode_set_xcd_split(before)
+    for split in (600, 400):
+        assert np.array_equal(outs[split].view(np.uint16), outs[0].view(np.uint16)), split
+    ref = oracle.paged_attention_decode(W.from_torch(q, DT), W.from_torch(kp, DT),
+                                        W.from_torch(vp, DT), tables, lens, scale, DT)
+    check_close(oracle.decode(outs[400], DT), ref, DT, "scheduled shared-prefix decode, split 400")

@@ -112,6 +112,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="block size x placement sweep of the llama13b_layer and long_context "
                          "workloads, 3 interleaved rounds: one JSON line per configuration")
+    ap.add_argument("--user-turns", default="16,512", metavar="LO,HI",
+                    help="prefix_hit: new tokens per request, uniform in [LO, HI]")
+    ap.add_argument("--mq-schedule", choices=("packed", "grouped"), default="packed",
+                    help="prefix_hit: full tiles packed across the requests that share a "
+                         "prompt's blocks, or one tile list per request grouped by prompt")
     ap.add_argument("--dtype", choices=("f16", "bf16"), default="f16",
                     help="storage type of the prefix_hit workload")
     ap.add_argument("--flush-mall", action="store_true",
@@ -902,7 +907,8 @@ def multi_query_bench(args):
     import paged_kv_cache_306_amd as pkv
     import workloads as W
     dev = torch.device("cuda:0")
-    w = W.prefix_hit(dtype=args.dtype)
+    lo, hi = (int(x) for x in args.user_turns.split(","))
+    w = W.prefix_hit(dtype=args.dtype, user_lo=lo, user_hi=hi)
     qs = w.extra["query_start"]
     T, H, D, BS, dt = int(qs[-1]), w.H, w.D, w.BS, w.dtype
     new = np.diff(qs).astype(np.int64)
@@ -920,10 +926,24 @@ def multi_query_bench(args):
     cl = torch.from_numpy(w.lens).to(dev)
     qsd = torch.from_numpy(qs).to(dev)
     sl = torch.from_numpy(slots).to(dev)
-    # requests that share a system prompt (the same first physical block) run side by side
-    items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len,
-                                                      group_keys=w.tables[:, 0])).to(dev)
+    packed = args.mq_schedule == "packed"
+    if packed:
+        # the new tokens of the requests that share a prompt's blocks fill whole tiles
+        items = torch.from_numpy(pkv.multi_query_schedule_packed(qs, w.lens, w.tables, BS,
+                                                                 w.max_len)).to(dev)
+    else:
+        # requests that share a system prompt (the same first physical block) side by side
+        items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len,
+                                                          group_keys=w.tables[:, 0])).to(dev)
     maxq = int(new.max())
+
+    def attend():
+        if packed:
+            pkv.paged_attention_multi_query_packed(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
+                                                   w.max_len, items)
+        else:
+            pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
+                                            w.max_len, work_items=items)
     # algorithmic work: token i of sequence s sees P + 1 = L_s - n_s + i + 1 keys; per key and
     # head 2 D flops for the score and 2 D for the output
     keys = int(sum(int(new[s]) * (int(w.lens[s]) - int(new[s])) + int(new[s]) * (int(new[s]) + 1) // 2
@@ -932,8 +952,7 @@ def multi_query_bench(args):
 
     def step():
         pkv.reshape_and_cache(kn, vn, kp, vp, sl)
-        pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len,
-                                        work_items=items)
+        attend()
 
     for _ in range(args.warmup):
         step()
@@ -945,8 +964,7 @@ def multi_query_bench(args):
         for a, z in evs:
             pkv.reshape_and_cache(kn, vn, kp, vp, sl)
             a.record()
-            pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
-                                            w.max_len, work_items=items)
+            attend()
             z.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -960,13 +978,15 @@ def multi_query_bench(args):
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
-        "config": {"workload": f"prefix_hit_{dt}",
+        "config": {"workload": f"prefix_hit_{dt}" + ("" if (lo, hi) == (16, 512)
+                                                     else f"_turns{lo}-{hi}"),
                    "description": f"{w.S} requests, {w.extra['prompts']} shared system prompts "
                                   f"of {w.extra['system_len']} cached tokens, user turns "
                                   f"U{list(w.extra['user_range'])} new tokens, 40 heads, "
                                   "head_dim 128, BS 16",
                    "requests": w.S, "new_tokens": T, "keys_seen": keys, "heads": H,
-                   "head_dim": D, "block_size": BS, "pool_blocks": w.num_blocks},
+                   "head_dim": D, "block_size": BS, "pool_blocks": w.num_blocks,
+                   "schedule": args.mq_schedule, "tiles_per_head": int(items.shape[0])},
         "new_tokens_per_s": round(T * args.steps / wall, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

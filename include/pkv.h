@@ -229,7 +229,7 @@ pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, vo
  * [0, num_blocks) among a tile's keys is never dereferenced: that tile's outputs are NaN; so
  * are the rows of a sequence with n_s > L_s.  Returns PKV_EINVAL (null or misaligned
  * pointers, negative sizes, a scale that is not finite and positive, bad num_items),
- * PKV_EUNSUPPORTED, PKV_EHIP or PKV_OK.
+ * PKV_EUNSUPPORTED (also for num_seqs * max_blocks_per_seq >= 2^32), PKV_EHIP or PKV_OK.
  *
  * pkv_multi_query_tile(): new tokens per workgroup tile (128: 8 waves of 16).
  * pkv_multi_query_schedule (host only): one item per (sequence s, tile of
@@ -245,6 +245,32 @@ pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, vo
  * prefix-cache hit ("Advanced Features" -> "Prefix Caching") -- are scheduled side by side,
  * so their shared K/V is read from L2 while they run; groups that read the most keys first,
  * inside a group the order above.  Same return values.
+ *
+ * pkv_multi_query_schedule_packed (host only): tiles that pack the new tokens of
+ * consecutive sequences sharing prefix blocks ("Advanced Features" -> "Prefix Caching", and
+ * "KV-Cache Sharing") into full tiles of pkv_multi_query_tile() rows, for
+ * pkv_paged_attention_multi_query_packed.  A run is a stretch of consecutive sequences with
+ * new tokens whose tables (host copy, int32 [num_seqs][max_blocks]) hold the same first
+ * `pre` keys in the same blocks, before every member's first new token; pre is a whole
+ * number of 64-key stages, at least one, fixed by the run's first two members (a sequence
+ * sharing fewer keys starts a new run).  Each tile is four int32: {sa, sb, first, pre}: rows
+ * query_start[sa] + first onward, at most pkv_multi_query_tile() of them, through sequence sb
+ * (pre = 0 and sa = sb outside runs).  Runs that read the most keys first, a run's tiles
+ * adjacent.  tiles: host, int32 [capacity][4]; a capacity of num_seqs *
+ * ceil(max new tokens / pkv_multi_query_tile()) always suffices.  Returns the number of
+ * tiles, or -1 for bad arguments (null pointers, max_blocks or block_size <= 0, a
+ * decreasing query_start) or too small a capacity.
+ * pkv_paged_attention_multi_query_packed: pkv_paged_attention_multi_query over such tiles
+ * (tiles: device, int32 [num_tiles][4], 16-byte aligned).  Per tile and head, a workgroup
+ * stages the shared keys once for all its rows and then each member's own keys for that
+ * member's rows, so tiles are full where sequences share a prompt.  The kernel re-checks on
+ * the device that every member's table holds the tile's first pre keys in the same blocks
+ * and that they precede every member's new tokens, and otherwise reads each member's keys on
+ * its own: outputs are those of pkv_paged_attention_multi_query for any tiles, bit for bit
+ * (the same 64-key stages in the same order for every row).  A tile naming sequences outside
+ * the call, a negative first or a pre that is not a whole number of stages is ignored.  Same
+ * other arguments and returns; PKV_EINVAL also for num_tiles < 0 or null or misaligned tiles
+ * with num_tiles > 0.
  */
 int32_t pkv_multi_query_tile(void);
 int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* context_lens,
@@ -260,6 +286,18 @@ pkv_status_t pkv_paged_attention_multi_query(
     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
     int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
     const int32_t* work_items, int32_t num_items, pkv_stream_t stream);
+int32_t pkv_multi_query_schedule_packed(const int32_t* query_start,
+                                        const int32_t* context_lens,
+                                        const int32_t* block_tables, int32_t max_blocks,
+                                        int32_t block_size, int32_t num_seqs,
+                                        int32_t max_context_len, int32_t* tiles,
+                                        int32_t capacity);
+pkv_status_t pkv_paged_attention_multi_query_packed(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* tiles, int32_t num_tiles, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Append new tokens' keys and values to the cache.

@@ -70,6 +70,10 @@ _SIGNATURES = {
     "pkv_multi_query_schedule_grouped": (_i32, [_p, _p, _p, _i32, _i32, _p, _i32]),
     "pkv_paged_attention_multi_query": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p, _i32,
                                                _i32, _i32, _i32, _f32, _p, _i32, _p]),
+    "pkv_multi_query_schedule_packed": (_i32, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32]),
+    "pkv_paged_attention_multi_query_packed": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p, _p,
+                                                      _i32, _i32, _i32, _i32, _f32, _p, _i32,
+                                                      _p]),
     "pkv_reshape_and_cache": (_i32, [_pdesc, _p, _p, _p, _p, _p, _i32, _p]),
     "pkv_check_slot_mapping": (_i32, [_pdesc, _p, _i32]),
     "pkv_copy_blocks": (_i32, [_pdesc, _p, _p, _i32, _p, _i32, _p]),
@@ -370,6 +374,63 @@ def paged_attention_multi_query(out, q, k_pool, v_pool, block_tables, context_le
         int(max_context_len), float(scale), work,
         int(work_items.numel()) if work_items is not None else 0, _stream_ptr(stream))
     _check(st, "pkv_paged_attention_multi_query")
+    return out
+
+
+def multi_query_schedule_packed(query_start, context_lens, block_tables, block_size: int,
+                                max_context_len: int):
+    """Tiles (int32 numpy [n][4]: first sequence, last sequence, first row of the first one,
+    shared keys) that pack the new tokens of consecutive sequences sharing prefix blocks into
+    full tiles, from host copies of query_start [S+1], context_lens [S] and block_tables
+    [S][max_blocks] (include/pkv.h)."""
+    import numpy as np
+    qs = np.ascontiguousarray(np.asarray(query_start, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    S = int(cl.shape[0])
+    if qs.shape != (S + 1,):
+        raise ValueError("query_start needs num_seqs + 1 entries")
+    if bt.ndim != 2 or bt.shape[0] != S or bt.shape[1] < 1:
+        raise ValueError("block_tables needs num_seqs rows")
+    tile = multi_query_tile()
+    n = np.diff(qs.astype(np.int64))
+    cap = max(1, int(np.sum(np.maximum(-(-n // tile), 0))))
+    tiles = np.empty((cap, 4), np.int32)
+    k = _lib().pkv_multi_query_schedule_packed(
+        qs.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p),
+        bt.ctypes.data_as(ctypes.c_void_p), int(bt.shape[1]), int(block_size), S,
+        int(max_context_len), tiles.ctypes.data_as(ctypes.c_void_p), cap)
+    if k < 0:
+        raise PkvError(PKV_EINVAL, "pkv_multi_query_schedule_packed")
+    return tiles[:k].copy()
+
+
+def paged_attention_multi_query_packed(out, q, k_pool, v_pool, block_tables, context_lens,
+                                       query_start, scale: float, max_query_len: int,
+                                       max_context_len: int, tiles, stream=None):
+    """paged_attention_multi_query over packed tiles (int32 device tensor [n][4] from
+    multi_query_schedule_packed): the same outputs, full tiles where sequences share a
+    prompt's blocks."""
+    import torch
+    desc = desc_for_pool(k_pool)
+    S = context_lens.shape[0]
+    if q.shape != out.shape or q.dim() != 3 or q.shape[1:] != (desc.num_heads, desc.head_dim):
+        raise ValueError("q/out shape mismatch")
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool/v_pool mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("block_tables/query_start shape mismatch")
+    if tiles.dim() != 2 or tiles.shape[1] != 4:
+        raise ValueError("tiles must be [n][4]")
+    st = _lib().pkv_paged_attention_multi_query_packed(
+        ctypes.byref(desc), _dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool", k_pool.dtype),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, int(q.shape[0]), int(max_query_len),
+        int(max_context_len), float(scale), _dev(tiles, "tiles", torch.int32),
+        int(tiles.shape[0]), _stream_ptr(stream))
+    _check(st, "pkv_paged_attention_multi_query_packed")
     return out
 
 

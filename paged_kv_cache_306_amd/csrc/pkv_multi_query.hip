@@ -9,7 +9,11 @@
 // With many queries per sequence this is a dense contraction, so both products run on the
 // matrix cores (v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate):
 //   * one workgroup = 128 consecutive new tokens of one (sequence, head), 16 per wave (one
-//     MFMA query tile; the shape is a compile-time choice, see below);
+//     MFMA query tile; the shape is a compile-time choice, see below); or, in packed mode,
+//     128 consecutive rows of q spanning several sequences that hold the same first blocks
+//     (requests sharing a cached prompt, "Prefix Caching" and "KV-Cache Sharing" on the same
+//     page): their shared keys are staged once for all the rows, then each sequence's own
+//     keys for its rows, so the tiles of short new-token runs are full;
 //   * keys go 64 at a time through a double-buffered LDS stage, K and V rows loaded straight
 //     from HBM into LDS (global_load_lds_dwordx4), stage c + 1 landing while stage c is
 //     computed as two 32-key steps, one barrier per stage; the stage rows are XOR-swizzled
@@ -150,13 +154,20 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <class Ty, int D, int BS>
-__global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
+// Four waves per SIMD (two workgroups per CU) is what the kernel's latency hiding rests on:
+// the register budget is held to that (128 VGPRs); the segment bookkeeping of packed tiles
+// would otherwise take it to 136-138.  PACKED: the work list holds packed tiles (several
+// sequences per tile); otherwise every tile is one sequence's, and the segment bookkeeping
+// folds away at compile time.
+template <class Ty, int D, int BS, bool PACKED>
+__global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+multi_query_kernel(
     typename Ty::store_t* __restrict__ out, const typename Ty::store_t* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start,
-    const int32_t* __restrict__ work, int num_seqs, int num_tokens, int tiles_per_seq,
+    const int32_t* __restrict__ work, const int32_t* __restrict__ packed, int num_seqs,
+    int num_tokens, int tiles_per_seq,
     int num_heads, int num_blocks, int max_len, float scale_log2) {
   using T = typename Ty::store_t;
   constexpr int KSTEPS = D / 32;    // k-steps of the score product
@@ -200,60 +211,155 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     h = static_cast<int>(blockIdx.x % num_heads);
     j = static_cast<int>(blockIdx.x / num_heads);
   }
-  int s, tile;
-  if (work) {
-    const int item = work[j];
-    s = item & kMqItemSeqMask;
-    tile = item >> kMqItemSeqBits;
-    if (s >= num_seqs || tile >= tiles_per_seq) return;  // not an item of this call
+  // The tile: up to kMqTileQueries consecutive rows of q, from row `first` of sequence sa's
+  // new tokens through sequence sb (the rows of consecutive sequences are consecutive in q).
+  // Its keys come in segments: the first `pre` keys, which every sequence of the tile holds
+  // in the same blocks and every row of it sees, with no mask; then each sequence's keys from
+  // `pre` on, seen by that sequence's rows only (pre = 0: one segment per sequence).
+  int sa, sb, first, pre;
+  if constexpr (PACKED) {
+    const int32_t* it = packed + 4 * static_cast<size_t>(j);
+    sa = it[0];
+    sb = it[1];
+    first = it[2];
+    pre = it[3];
+    if (sa < 0 || sb < sa || sb >= num_seqs || first < 0 || pre < 0 || pre % kMqStage != 0)
+      return;  // not a tile of this call
   } else {
-    s = j / tiles_per_seq;
-    tile = j % tiles_per_seq;
+    int s, tile;
+    if (work) {
+      const int item = work[j];
+      s = item & kMqItemSeqMask;
+      tile = item >> kMqItemSeqBits;
+      if (s >= num_seqs || tile >= tiles_per_seq) return;  // not an item of this call
+    } else {
+      s = j / tiles_per_seq;
+      tile = j % tiles_per_seq;
+    }
+    sa = sb = s;
+    first = tile * kMqTileQueries;
+    pre = 0;
   }
-  const int q0 = query_start[s];
-  const int n = query_start[s + 1] - q0;
-  const int first = tile * kMqTileQueries;
-  if (first >= n) return;  // tile past this sequence's new tokens (uniform)
-  if (q0 < 0 || q0 > num_tokens - n) return;  // rows outside q / out: touch nothing
-  const int nq = min(kMqTileQueries, n - first);
-  const int L = min(context_lens[s], max_len);
+  // One round of loads serves the common tile of one sequence.
+  const int qa = query_start[sa], qa1 = query_start[sa + 1];
+  const int La = min(context_lens[sa], max_len);
+  if (first >= qa1 - qa) return;  // tile past sa's new tokens (uniform)
+  if (qa < 0 || qa1 < qa || qa1 > num_tokens) return;  // rows outside q / out: touch nothing
+  for (int m = sa + 1; m <= sb; ++m) {
+    const int a = query_start[m], b = query_start[m + 1];
+    if (a < 0 || b < a || b > num_tokens) return;
+  }
+  const int R0 = qa + first;                                     // the tile's first row of q
+  const int nq = min(kMqTileQueries, (sb == sa ? qa1 : query_start[sb + 1]) - R0);  // its rows
   const size_t row_stride = static_cast<size_t>(num_heads) * D;
   const int tid = threadIdx.x;
-
-  if (n > L) {  // the new tokens must be the last tokens of the context: NaN rows
-    for (int e = tid; e < nq * D; e += kMqThreads)
-      out[static_cast<size_t>(q0 + first + e / D) * row_stride + static_cast<size_t>(h) * D +
-          e % D] = Ty::store(NAN);
-    return;
-  }
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int wave_first = first + wave * kMqWaveQueries;
-  const bool wave_on = wave_first < n;
-  const int tile_keys = L - n + first + nq;                       // keys the workgroup sees
-  const int wave_keys = L - n + min(wave_first + kMqWaveQueries, n);  // ... the wave sees
-  const int wave_unmasked = L - n + wave_first + 1;  // keys every query of the wave sees
-  const int nstages = (tile_keys + kMqStage - 1) / kMqStage;   // stages
-  // Per 16-query MFMA tile: whether it holds a new token, this lane's query and the last
-  // key that query sees (rows past n compute a copy of the last one).
+
+  // Sequence m's rows of the tile are [lo, hi) (tile-relative), and tile row i sits at
+  // position base + i of it; ok: its new tokens are the last tokens of its context (its rows
+  // are NaN otherwise).
+  struct Member {
+    int lo, hi, base;
+    bool ok;
+  };
+  auto member = [&](int m) {
+    const int a = m == sa ? qa : query_start[m], b = m == sa ? qa1 : query_start[m + 1];
+    const int L = m == sa ? La : min(context_lens[m], max_len);
+    Member x;
+    x.lo = max(a, R0) - R0;
+    x.hi = min(b, R0 + nq) - R0;
+    x.base = L - (b - a) - a + R0;
+    x.ok = b - a <= L;
+    return x;
+  };
+  // The shared keys: at most what every sequence's first row sees, a whole number of stages,
+  // and only if the tables agree on their blocks (otherwise every sequence reads its own).  A
+  // tile of one sequence reads its keys in one segment: the same stages.
+  if (sb == sa) pre = 0;
+  for (int m = sa; m <= sb && pre > 0; ++m) {
+    const Member x = member(m);
+    if (x.hi > x.lo) pre = x.ok ? min(pre, x.base + x.lo) : 0;
+  }
+  pre = max(pre, 0) / kMqStage * kMqStage;
+  if (pre > 0) {
+    const int32_t* ta = block_tables + static_cast<size_t>(sa) * max_blocks;
+    bool differ = false;
+    for (int m = sa + 1; m <= sb; ++m) {
+      const int32_t* tm = block_tables + static_cast<size_t>(m) * max_blocks;
+      for (int e = lane; e < pre / BS; e += 64) differ |= tm[e] != ta[e];
+    }
+    if (__builtin_amdgcn_ballot_w64(differ)) pre = 0;
+  }
+
+  // A cursor over the stages: segment m (sa - 1: the shared keys, read through sa's table),
+  // its keys from kb (a stage), its end and the offset of its table row.  The table is
+  // indexed from the kernel argument at each read: a pointer carried through the loop would
+  // hide that it is read-only, and the block ids would then come through vector loads whose
+  // wait also waits for the stage loads.
+  struct Cur {
+    int m, kb, end;
+    uint32_t row;
+  };
+  auto seg_begin = [&](Cur& cu, int m) {
+    for (; m <= sb; ++m) {
+      if (m < sa) {
+        if (pre == 0) continue;
+        cu.kb = 0;
+        cu.end = pre;
+        cu.row = static_cast<uint32_t>(sa) * max_blocks;
+      } else {
+        const Member x = member(m);
+        if (x.hi <= x.lo || !x.ok) continue;
+        cu.kb = pre;
+        cu.end = x.base + x.hi;
+        cu.row = static_cast<uint32_t>(m) * max_blocks;
+      }
+      break;
+    }
+    cu.m = m;
+  };
+  auto advance = [&](Cur& cu) {
+    cu.kb += kMqStage;
+    if (PACKED && cu.kb >= cu.end) seg_begin(cu, cu.m + 1);  // one segment otherwise
+  };
+  Cur c0;
+  int nstages = 0;
+  if (sb == sa) {  // one segment, from key 0
+    const Member x = member(sa);
+    c0 = {x.ok ? sa : sa + 1, 0, x.base + x.hi, static_cast<uint32_t>(sa) * max_blocks};
+    nstages = x.ok ? (c0.end + kMqStage - 1) / kMqStage : 0;
+  } else {
+    seg_begin(c0, sa - 1);
+    for (Cur cu = c0; cu.m <= sb; seg_begin(cu, cu.m + 1))
+      nstages += (cu.end - cu.kb + kMqStage - 1) / kMqStage;
+  }
+  if (nstages == 0) {  // no sequence of the tile has a valid context: NaN rows
+    for (int e = tid; e < nq * D; e += kMqThreads)
+      out[static_cast<size_t>(R0 + e / D) * row_stride + static_cast<size_t>(h) * D + e % D] =
+          Ty::store(NAN);
+    return;
+  }
+
+  // This wave's rows are [w0, w1) of the tile; a lane's row i past the tile's end computes a
+  // copy of its last row.
+  const int w0 = wave * kMqWaveQueries;
+  const int w1 = min(w0 + kMqWaveQueries, nq);
+  const bool wave_on = w0 < nq;
   bool qt_on[kMqQt];
-  int qi[kMqQt], qpos[kMqQt];
+  int qi[kMqQt];
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
-    const int f = wave_first + 16 * qt;
-    qt_on[qt] = f < n;
-    qi[qt] = f + r;
-    qpos[qt] = L - n + min(qi[qt], n - 1);
+    qt_on[qt] = w0 + 16 * qt < nq;
+    qi[qt] = min(w0 + 16 * qt + r, nq - 1);
   }
 
   // q rows as B fragments: lane (r, g) holds q[r][32k + 8g .. 32k + 8g + 7] of each tile.
   u32x4 qf[kMqQt][KSTEPS];
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
-    const T* qrow = q + static_cast<size_t>(q0 + min(qi[qt], n - 1)) * row_stride +
-                    static_cast<size_t>(h) * D;
+    const T* qrow = q + static_cast<size_t>(R0 + qi[qt]) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) qf[qt][k] = load16(qrow + 32 * k + 8 * g);
   }
@@ -265,9 +371,9 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   // id is a scalar and a lane's byte offset inside the group never changes.  In the last
   // chunk, rows the workgroup does not see read zeros; a block id outside the pool is
   // clamped into it for the read and turns the outputs into NaN.
-  const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks;
-  // Loop-invariant parts of a group's address: chunks are whole multiples of the block size
-  // or of a block, so the group's row inside its block never changes.
+  // Loop-invariant parts of a group's address: stages start at whole multiples of the stage
+  // (segments too), which is a whole number of blocks, so the group's row inside its block
+  // never changes.
   static_assert(kMqStage % BS == 0 || BS % kMqStage == 0, "stages align with blocks");
   const uint64_t block_stride = static_cast<uint64_t>(num_heads) * BS * ROW_BYTES;
   const gptr_t zeros = uniform_ptr(reinterpret_cast<const char*>(kMqZeros)) + 16 * lane;
@@ -286,20 +392,22 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   }
   uint32_t bid[GROUPS] = {};  // block ids of the groups of the next chunk to fetch, loaded early
   // Largest block id fetched.  An id outside the pool is clamped into it (the read stays in
-  // bounds) and turns the outputs into NaN at the end.  Groups of the last chunk that reach
-  // past the keys the workgroup sees read the block of its last key (clamped table index).
+  // bounds) and turns the outputs into NaN at the end.  Groups of a segment's last stage that
+  // reach past its keys read the block of its last key (clamped table index).
   uint32_t max_bid = 0;
   const uint32_t last_block = static_cast<uint32_t>(num_blocks - 1);
-  auto load_ids = [&](int c) {
-    const uint32_t last = static_cast<uint32_t>(tile_keys - 1);
+  auto load_ids = [&](const Cur& cu) {
+    const uint32_t last = static_cast<uint32_t>(cu.end - 1);
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i)
       if (ALL_GROUPS || grp_row[i] < kMqStage)
-        bid[i] = table[min(static_cast<uint32_t>(c * kMqStage) + grp_row[i], last) / BS];
+        bid[i] = block_tables[static_cast<size_t>(cu.row) +
+                              min(static_cast<uint32_t>(cu.kb) + grp_row[i], last) / BS];
   };
-  // stage c -> stage buffers (kst, vst), asynchronously (complete after wait_loads)
-  auto fetch = [&](int c, uint16_t* kst, uint16_t* vst) {
-    const bool tail = (c + 1) * kMqStage > tile_keys;  // uniform
+  // the stage at cursor cu -> stage buffers (kst, vst), asynchronously (complete after
+  // wait_loads)
+  auto fetch = [&](const Cur& cu, uint16_t* kst, uint16_t* vst) {
+    const bool tail = cu.kb + kMqStage > cu.end;  // uniform
 #pragma unroll
     for (int i = 0; i < GROUPS; ++i) {
       if (!ALL_GROUPS && grp_row[i] >= kMqStage) continue;  // more waves than groups
@@ -307,7 +415,7 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       const uint64_t off = static_cast<uint64_t>(min(bid[i], last_block)) * block_stride;
       gptr_t kp = kgrp[i] + off + koff[i];
       gptr_t vp = vgrp[i] + off + voff[i];
-      if (tail && c * kMqStage + static_cast<int>(grp_row[i] + lane / COLS) >= tile_keys) {
+      if (tail && cu.kb + static_cast<int>(grp_row[i] + lane / COLS) >= cu.end) {
         kp = zeros;
         vp = zeros;
       }
@@ -330,21 +438,47 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
   using den_t = std::conditional_t<Mma<Ty>::kSplit, f32x4, float>;
   // The move test runs on raw scores against mraw = (m + kMqSlack) / scale, so a lane need
   // not scale its largest score first; rounding here only shifts the point at which the exact
-  // test below is made.
+  // test below is made.  m starts finite: a step in which a query sees no key (in a packed
+  // tile, another sequence's keys) then adds exp2(-inf) = 0 for it, not NaN; its first key
+  // seen moves m (mraw starts at -inf) and scales the empty accumulators by exp2(-1e30 - m).
   const float inv_scale = 1.0f / scale_log2;
   float m[kMqQt], mraw[kMqQt];
   den_t den[kMqQt];
 #pragma unroll
   for (int qt = 0; qt < kMqQt; ++qt) {
-    m[qt] = -INFINITY;
+    m[qt] = -1e30f;
     mraw[qt] = -INFINITY;
     den[qt] = den_t{};
   }
+  // The last key each lane's query sees in the current segment (-1: the segment belongs to
+  // another sequence), and the wave's bounds there: keys past wave_keys are seen by none of
+  // its queries, keys below wave_unmasked by all of them.
+  int qpos[kMqQt];
+  int seg_m = sa - 2, wave_keys = 0, wave_unmasked = 0;
+  bool seg_on = false;
+  auto enter_segment = [&](int mm) {
+    seg_m = mm;
+    if (mm < sa) {  // the shared keys: every query sees all of them
+      seg_on = wave_on;
+      wave_keys = wave_unmasked = pre;
+#pragma unroll
+      for (int qt = 0; qt < kMqQt; ++qt) qpos[qt] = pre;
+      return;
+    }
+    const Member x = member(mm);
+    const int a = max(w0, x.lo), b = min(w1, x.hi);
+    seg_on = a < b;
+    wave_keys = x.base + b;
+    wave_unmasked = (a == w0 && b == w1) ? x.base + a + 1 : 0;
+#pragma unroll
+    for (int qt = 0; qt < kMqQt; ++qt)
+      qpos[qt] = (qi[qt] >= x.lo && qi[qt] < x.hi) ? x.base + qi[qt] : -1;
+  };
 
-  // One chunk of keys for the query tiles of the wave.  mask: the chunk holds keys that some
-  // query of the wave does not see (its own later positions, or keys past the workgroup's);
-  // wave-uniform.
-  auto chunk_step = [&](const uint16_t* kst, const uint16_t* vst, int c, bool mask) {
+  // One chunk of keys, from position kpos on, for the query tiles of the wave.  mask: the
+  // chunk holds keys that some query of the wave does not see (its own later positions, keys
+  // past the segment's, another sequence's); wave-uniform.
+  auto chunk_step = [&](const uint16_t* kst, const uint16_t* vst, int kpos, bool mask) {
     // all K fragments of the chunk first, then the products k-step by k-step over the
     // independent accumulators (query tiles x two 16-key halves)
     u32x4 kf[2][KSTEPS];
@@ -371,11 +505,15 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[qt][4 * hh + i] = sc[qt][hh][i];
     if (mask) {
+      // score e of lane (r, g) is key kpos + 4g + 16 (e / 4) + e % 4: compared against the
+      // query's last key taken relative to kpos + 4g, each test is against a constant
 #pragma unroll
-      for (int qt = 0; qt < kMqQt; ++qt)
+      for (int qt = 0; qt < kMqQt; ++qt) {
+        const int rel = qpos[qt] - kpos - 4 * g;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (c * kMqChunk + 16 * (e >> 2) + 4 * g + (e & 3) > qpos[qt]) z[qt][e] = -INFINITY;
+          if (16 * (e >> 2) + (e & 3) > rel) z[qt][e] = -INFINITY;
+      }
     }
     // Online softmax with a lazily moved reference: m moves only when a scaled score exceeds
     // it by more than kMqSlack, so probabilities stay below 2^kMqSlack and the accumulators
@@ -406,7 +544,6 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
         const float lmax = rmax[qt] * scale_log2;
         float cm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        // m is -inf until the query's first chunk (which holds key 0, seen by every query)
         if (cm > m[qt] + kMqSlack) {
           alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - cm);
           m[qt] = cm;
@@ -464,29 +601,39 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
     }
   };
 
-  load_ids(0);
-  fetch(0, ks0, vs0);
-  if (nstages > 1) load_ids(1);
+  if (!PACKED) enter_segment(sa);
+  // cursors at stage c (computed), c + 1 (being fetched) and c + 2 (its block ids read)
+  Cur cc = c0, cf = c0;
+  load_ids(c0);
+  fetch(c0, ks0, vs0);
+  advance(cf);
+  if (nstages > 1) load_ids(cf);
+  Cur ci = cf;
+  advance(ci);
   wait_loads();
   __syncthreads();
   // One stage: load stage c + 1 into (knext, vnext) while stage c is read from (kcur, vcur).
   auto step = [&](int c, const uint16_t* kcur, const uint16_t* vcur, uint16_t* knext,
                   uint16_t* vnext) {
     if (c + 1 < nstages) {
-      fetch(c + 1, knext, vnext);  // the other buffer was last read during stage c - 1
-      if (c + 2 < nstages) load_ids(c + 2);
+      fetch(cf, knext, vnext);  // the other buffer was last read during stage c - 1
+      if (c + 2 < nstages) load_ids(ci);
     }
+    if (PACKED && cc.m != seg_m) enter_segment(cc.m);
     // a tile past the wave's queries, or one whose queries all come before this step, gets
     // only masked scores and adds nothing
 #pragma unroll
     for (int u = 0; u < kMqSub; ++u) {
-      const int cc = c * kMqSub + u;   // 32-key compute step
-      if (wave_on && cc * kMqChunk < wave_keys)
-        chunk_step(kcur + u * kMqChunk * D, vcur + u * kMqChunk * D, cc,
-                   (cc + 1) * kMqChunk > wave_unmasked);
+      const int kpos = cc.kb + u * kMqChunk;  // 32-key compute step
+      if (seg_on && kpos < wave_keys)
+        chunk_step(kcur + u * kMqChunk * D, vcur + u * kMqChunk * D, kpos,
+                   kpos + kMqChunk > wave_unmasked);
     }
     wait_loads();  // stage c + 1 has landed in this wave's part of the other buffer
     __syncthreads();
+    cc = cf;
+    cf = ci;
+    advance(ci);
   };
   for (int c = 0; c < nstages; c += 2) {
     step(c, ks0, vs0, ks1, vs1);
@@ -509,9 +656,15 @@ __global__ __launch_bounds__(kMqThreads) void multi_query_kernel(
       l = den[qt] + __shfl_xor(den[qt], 16, 64);  // the query's four lanes
       l += __shfl_xor(l, 32, 64);
     }
-    if (!qt_on[qt] || qi[qt] >= n) continue;
-    const float inv = any_bad ? NAN : 1.0f / l;
-    T* orow = out + static_cast<size_t>(q0 + qi[qt]) * row_stride + static_cast<size_t>(h) * D;
+    const int i = w0 + 16 * qt + r;  // the lane's row of the tile
+    if (!qt_on[qt] || i >= nq) continue;
+    bool row_ok = !any_bad;           // and the rows of a sequence with n_s > L_s are NaN
+    for (int mm = sa; mm <= sb; ++mm) {
+      const Member x = member(mm);
+      if (!x.ok && i >= x.lo && i < x.hi) row_ok = false;
+    }
+    const float inv = row_ok ? 1.0f / l : NAN;
+    T* orow = out + static_cast<size_t>(R0 + i) * row_stride + static_cast<size_t>(h) * D;
 #pragma unroll
     for (int t = 0; t < DTILES; ++t) {
       T o[4];
@@ -535,6 +688,7 @@ struct MqArgs {
   const int32_t* context_lens;
   const int32_t* query_start;
   const int32_t* work;
+  const int32_t* packed;
   int64_t wgs;
   int num_seqs;
   int num_tokens;
@@ -550,11 +704,13 @@ template <class Ty, int D, int BS>
 static void launch_mq(const MqArgs& a) {
   using T = typename Ty::store_t;
   if (a.wgs <= 0) return;
-  hipLaunchKernelGGL((multi_query_kernel<Ty, D, BS>), dim3(static_cast<unsigned>(a.wgs)),
+  hipLaunchKernelGGL((a.packed ? multi_query_kernel<Ty, D, BS, true>
+                               : multi_query_kernel<Ty, D, BS, false>),
+                     dim3(static_cast<unsigned>(a.wgs)),
                      dim3(kMqThreads), 0, a.stream, static_cast<T*>(a.out),
                      static_cast<const T*>(a.q), static_cast<const char*>(a.k_pool),
                      static_cast<const char*>(a.v_pool), a.block_tables, a.max_blocks,
-                     a.context_lens, a.query_start, a.work, a.num_seqs, a.num_tokens,
+                     a.context_lens, a.query_start, a.work, a.packed, a.num_seqs, a.num_tokens,
                      a.tiles_per_seq, a.num_heads, a.num_blocks, a.max_len, a.scale_log2);
 }
 
@@ -656,30 +812,133 @@ int32_t pkv_multi_query_schedule(const int32_t* query_start, const int32_t* cont
                                           max_context_len, items, capacity);
 }
 
-pkv_status_t pkv_paged_attention_multi_query(
-    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
-    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
-    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
-    const int32_t* work_items, int32_t num_items, pkv_stream_t stream) {
+int32_t pkv_multi_query_schedule_packed(const int32_t* query_start,
+                                        const int32_t* context_lens,
+                                        const int32_t* block_tables, int32_t max_blocks,
+                                        int32_t block_size, int32_t num_seqs,
+                                        int32_t max_context_len, int32_t* tiles,
+                                        int32_t capacity) {
+  if (num_seqs < 0 || max_context_len < 0 || capacity < 0 || max_blocks <= 0 ||
+      block_size <= 0 ||
+      (num_seqs > 0 && (!query_start || !context_lens || !block_tables || !tiles)))
+    return -1;
+  if (num_seqs == 0) return 0;
+  for (int32_t s = 0; s < num_seqs; ++s)
+    if (query_start[s + 1] < query_start[s]) return -1;
+  const int64_t width = std::min<int64_t>(max_context_len,
+                                          static_cast<int64_t>(max_blocks) * block_size);
+  auto cached = [&](int32_t s) {  // tokens before the first new one, at most the table's
+    const int64_t n = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
+    return std::min<int64_t>(context_lens[s], width) - n;
+  };
+  // keys that sequences s and t hold in the same blocks, in whole stages
+  auto shared = [&](int32_t s, int32_t t, int64_t cap) -> int64_t {
+    if (kMqStage % block_size != 0) return 0;
+    const int32_t* ts = block_tables + static_cast<size_t>(s) * max_blocks;
+    const int32_t* tt = block_tables + static_cast<size_t>(t) * max_blocks;
+    int64_t keys = std::max<int64_t>(std::min({cap, cached(s), cached(t)}), 0);
+    keys = keys / kMqStage * kMqStage;
+    for (int64_t e = 0; e < keys / block_size; ++e)
+      if (ts[e] != tt[e]) return e * block_size / kMqStage * kMqStage;
+    return keys;
+  };
+  struct Tile {
+    int64_t run_keys;  // keys read by the run's largest tile
+    int32_t run;       // first sequence of the run
+    int64_t keys;      // keys read by this tile
+    int32_t sa, sb, first, pre;
+  };
+  std::vector<Tile> list;
+  int32_t s = 0;
+  while (s < num_seqs) {
+    if (query_start[s + 1] == query_start[s]) {
+      ++s;
+      continue;
+    }
+    // A run: consecutive sequences with new tokens that all hold the same first `pre` keys
+    // (at least one stage) in the same blocks; the second member fixes pre, and a sequence
+    // that shares fewer of them starts a run of its own.
+    int32_t t = s + 1;
+    int64_t pre = 0;
+    for (; t < num_seqs && query_start[t + 1] > query_start[t]; ++t) {
+      const int64_t p = shared(s, t, t == s + 1 ? INT64_MAX : pre);
+      if (t == s + 1 ? p < kMqStage : p != pre) break;
+      pre = p;
+    }
+    if (t == s + 1) pre = 0;
+    const int64_t rows = static_cast<int64_t>(query_start[t]) - query_start[s];
+    const size_t begin = list.size();
+    int32_t m = s;
+    for (int64_t r0 = 0; r0 < rows; r0 += kMqTileQueries) {
+      const int64_t R0 = query_start[s] + r0;
+      const int64_t R1 = std::min<int64_t>(R0 + kMqTileQueries, query_start[t]);
+      while (query_start[m + 1] <= R0) ++m;
+      Tile tl{0, s, 0, m, m, static_cast<int32_t>(R0 - query_start[m]),
+              static_cast<int32_t>(pre)};
+      int64_t keys = pre;
+      for (int32_t mm = m; mm < t && query_start[mm] < R1; ++mm) {
+        tl.sb = mm;
+        // keys of mm's last row in the tile, past the shared ones
+        const int64_t last = std::min<int64_t>(R1, query_start[mm + 1]) - 1;
+        keys += std::max<int64_t>(cached(mm) + (last - query_start[mm]) + 1 - pre, 0);
+      }
+      tl.keys = keys;
+      list.push_back(tl);
+    }
+    int64_t most = 0;
+    for (size_t i = begin; i < list.size(); ++i) most = std::max(most, list[i].keys);
+    for (size_t i = begin; i < list.size(); ++i) list[i].run_keys = most;
+    s = t;
+  }
+  if (static_cast<int64_t>(list.size()) > capacity) return -1;
+  // Runs that read the most keys first, a run's tiles adjacent (so the blocks they share stay
+  // in L2 while they run), inside a run the tiles reading the most keys first.
+  std::stable_sort(list.begin(), list.end(), [](const Tile& x, const Tile& y) {
+    if (x.run_keys != y.run_keys) return x.run_keys > y.run_keys;
+    if (x.run != y.run) return x.run < y.run;
+    return x.keys > y.keys;
+  });
+  for (size_t i = 0; i < list.size(); ++i) {
+    tiles[4 * i + 0] = list[i].sa;
+    tiles[4 * i + 1] = list[i].sb;
+    tiles[4 * i + 2] = list[i].first;
+    tiles[4 * i + 3] = list[i].pre;
+  }
+  return static_cast<int32_t>(list.size());
+}
+
+// What both launch entry points check, and the launch.
+static pkv_status_t mq_launch(const pkv_cache_desc_t* desc, void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, const int32_t* query_start,
+                              int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                              int32_t max_context_len, float scale, const int32_t* work_items,
+                              const int32_t* packed, bool use_packed, int32_t num_items,
+                              pkv_stream_t stream) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0 ||
-      max_blocks_per_seq <= 0 || !std::isfinite(scale) || !(scale > 0.0f))
+      max_blocks_per_seq <= 0 || !std::isfinite(scale) || !(scale > 0.0f) || num_items < 0)
     return PKV_EINVAL;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (use_packed && num_items == 0) return PKV_OK;
+  if (use_packed && (!packed || reinterpret_cast<uintptr_t>(packed) % 16 != 0))
+    return PKV_EINVAL;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return PKV_EINVAL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_EINVAL;
   if (num_seqs > kMqItemSeqMask + 1) return PKV_EUNSUPPORTED;
+  // table rows are addressed with 32-bit offsets
+  if (static_cast<int64_t>(num_seqs) * max_blocks_per_seq > UINT32_MAX) return PKV_EUNSUPPORTED;
   const int64_t tiles = (static_cast<int64_t>(max_query_len) + kMqTileQueries - 1) / kMqTileQueries;
   if (tiles > kMqMaxTiles) return PKV_EUNSUPPORTED;
 
   MqArgs a{};
-  if (work_items) {
-    if (num_items < 0 || num_items > static_cast<int64_t>(num_seqs) * tiles) return PKV_EINVAL;
+  if (use_packed || work_items) {
+    if (num_items > static_cast<int64_t>(num_seqs) * tiles) return PKV_EINVAL;
     a.wgs = static_cast<int64_t>(num_items) * desc->num_heads;
   } else {
     a.wgs = static_cast<int64_t>(num_seqs) * tiles * desc->num_heads;
@@ -693,7 +952,8 @@ pkv_status_t pkv_paged_attention_multi_query(
   a.max_blocks = max_blocks_per_seq;
   a.context_lens = context_lens;
   a.query_start = query_start;
-  a.work = work_items;
+  a.work = use_packed ? nullptr : work_items;
+  a.packed = use_packed ? packed : nullptr;
   a.num_seqs = num_seqs;
   a.num_tokens = num_tokens;
   a.tiles_per_seq = static_cast<int>(tiles);
@@ -709,6 +969,29 @@ pkv_status_t pkv_paged_attention_multi_query(
                               : mq_dispatch_d<BF16>(desc->head_dim, desc->block_size, a);
   if (st != PKV_OK) return st;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+pkv_status_t pkv_paged_attention_multi_query(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* work_items, int32_t num_items, pkv_stream_t stream) {
+  return mq_launch(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                   context_lens, query_start, num_seqs, num_tokens, max_query_len,
+                   max_context_len, scale, work_items, nullptr, false,
+                   work_items ? num_items : 0, stream);
+}
+
+pkv_status_t pkv_paged_attention_multi_query_packed(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* tiles, int32_t num_tiles, pkv_stream_t stream) {
+  return mq_launch(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                   context_lens, query_start, num_seqs, num_tokens, max_query_len,
+                   max_context_len, scale, nullptr, tiles, true, num_tiles, stream);
 }
 
 }  // extern "C"

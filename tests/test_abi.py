@@ -152,8 +152,34 @@ def test_multi_query_argument_errors():
     assert _mq(_desc(), T=-1) == pkv.PKV_EINVAL
     assert _mq(_desc(), S=0) == pkv.PKV_OK                               # nothing to do
     assert _mq(_desc(), S=(1 << 20) + 1) == pkv.PKV_EUNSUPPORTED          # > 2^20 sequences
+    assert _mq(_desc(), S=1 << 20, mb=1 << 12) == pkv.PKV_EUNSUPPORTED     # table offsets >= 2^32
     assert _mq(_desc(), T=0) == pkv.PKV_OK
     assert _mq(_desc(), maxq=0) == pkv.PKV_OK
+
+
+def _mqp(desc, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=4, cl=FAKE, qs=FAKE, S=2, T=100,
+             maxq=64, maxlen=64, scale=0.1, tiles=FAKE, ntiles=1)
+    a.update(kw)
+    return pkv.lib().pkv_paged_attention_multi_query_packed(
+        ctypes.byref(desc) if desc is not None else None, a["out"], a["q"], a["k"], a["v"],
+        a["bt"], a["mb"], a["cl"], a["qs"], a["S"], a["T"], a["maxq"], a["maxlen"], a["scale"],
+        a["tiles"], a["ntiles"], None)
+
+
+def test_multi_query_packed_argument_errors():
+    # every call here fails validation (or has nothing to do) before a launch
+    assert _mqp(None) == pkv.PKV_EINVAL
+    assert _mqp(_desc(dt=0)) == pkv.PKV_EUNSUPPORTED
+    assert _mqp(_desc(), tiles=None) == pkv.PKV_EINVAL
+    assert _mqp(_desc(), tiles=ctypes.c_void_p(0x1004)) == pkv.PKV_EINVAL  # not 16-byte aligned
+    assert _mqp(_desc(), ntiles=-1) == pkv.PKV_EINVAL
+    assert _mqp(_desc(), ntiles=2 * 1 + 1) == pkv.PKV_EINVAL    # more than 2 seqs x 1 tile
+    assert _mqp(_desc(), q=None) == pkv.PKV_EINVAL
+    assert _mqp(_desc(), scale=0.0) == pkv.PKV_EINVAL
+    assert _mqp(_desc(), ntiles=0, tiles=None) == pkv.PKV_OK        # nothing to do
+    assert _mqp(_desc(), S=0) == pkv.PKV_OK
+    assert _mqp(_desc(), maxq=0) == pkv.PKV_OK
 
 
 def test_multi_query_schedule_covers_every_tile_by_sequence():

@@ -45,21 +45,29 @@ def make_mq_case(seed, H, D, BS, pairs, dtype, pool_factor=1.3):
 
 
 def run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, items=None, max_len=None,
-           dev_ctx=None):
-    """Run the HIP kernel; rows it does not write stay NaN."""
+           dev_ctx=None, packed=None, dev_tables=None):
+    """Run the HIP kernel (over packed tiles when ``packed`` is given); rows it does not write
+    stay NaN."""
     import torch
     qd = to_dev(q, dtype, dev)
     kd = to_dev(kp, dtype, dev)
     vd = to_dev(vp, dtype, dev)
-    bt = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+    bt = torch.from_numpy(np.ascontiguousarray(tables if dev_tables is None else dev_tables,
+                                               np.int32)).to(dev)
     cl = torch.from_numpy(np.ascontiguousarray(ctx if dev_ctx is None else dev_ctx,
                                                np.int32)).to(dev)
     qsd = torch.from_numpy(np.ascontiguousarray(qs, np.int32)).to(dev)
     out = torch.full_like(qd, float("nan"))
     maxq = int(np.diff(qs).max()) if len(ctx) else 0
     ml = int(np.max(ctx)) if max_len is None else max_len
-    wi = None if items is None else torch.from_numpy(np.ascontiguousarray(items, np.int32)).to(dev)
-    pkv.paged_attention_multi_query(out, qd, kd, vd, bt, cl, qsd, scale, maxq, ml, work_items=wi)
+    if packed is not None:
+        tl = torch.from_numpy(np.ascontiguousarray(packed, np.int32).reshape(-1, 4)).to(dev)
+        pkv.paged_attention_multi_query_packed(out, qd, kd, vd, bt, cl, qsd, scale, maxq, ml, tl)
+    else:
+        wi = (None if items is None
+              else torch.from_numpy(np.ascontiguousarray(items, np.int32)).to(dev))
+        pkv.paged_attention_multi_query(out, qd, kd, vd, bt, cl, qsd, scale, maxq, ml,
+                                        work_items=wi)
     torch.cuda.synchronize()
     return W.from_torch(out, dtype)
 
@@ -172,9 +180,9 @@ def test_multi_query_clamps_context_to_max_len():
 def test_multi_query_prefix_hit_full_size_sampled(dtype):
     """64 chat requests after a prefix-cache hit (LLaMA-13B shapes), scheduled launch: every
     row of 8 requests (two per shared prompt, the shortest and the longest user turn) in every
-    head vs the oracle on the blocks read back from the device; a second launch, and the
-    plain grid, give the same bits (a race between the waves that share the LDS stage would
-    show up as a difference)."""
+    head vs the oracle on the blocks read back from the device; a second launch, the plain
+    grid and the packed tiles give the same bits (a race between the waves that share the
+    LDS stage would show up as a difference)."""
     import torch
     from concurrent.futures import ThreadPoolExecutor
     dev = device()
@@ -190,12 +198,19 @@ def test_multi_query_prefix_hit_full_size_sampled(dtype):
     cl = torch.from_numpy(w.lens).to(dev)
     qsd = torch.from_numpy(qs).to(dev)
     items = torch.from_numpy(pkv.multi_query_schedule(qs, w.lens, w.max_len)).to(dev)
+    tiles = pkv.multi_query_schedule_packed(qs, w.lens, w.tables, w.BS, w.max_len)
+    assert len(tiles) < len(items)            # the prompts' requests share full tiles
+    tiles = torch.from_numpy(tiles).to(dev)
     maxq = int(np.diff(qs).max())
     outs = []
-    for wi in (items, items, None):
+    for wi in (items, items, None, "packed"):
         out = torch.full_like(q, float("nan"))
-        pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq, w.max_len,
-                                        work_items=wi)
+        if isinstance(wi, str):
+            pkv.paged_attention_multi_query_packed(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
+                                                   w.max_len, tiles)
+        else:
+            pkv.paged_attention_multi_query(out, q, kp, vp, bt, cl, qsd, w.scale, maxq,
+                                            w.max_len, work_items=wi)
         torch.cuda.synchronize()
         outs.append(out)
     for o in outs[1:]:
@@ -332,3 +347,101 @@ def test_multi_query_ignores_rows_and_items_outside_the_call():
         done = int(qs[2]) if name == "grid" else int(qs[1])   # the list holds only sequence 0
         check_close(g_[:done], ref[:done], "f16", f"unaffected sequences ({name})")
         assert np.isnan(g_[done:int(qs[2])]).all()
+
+
+# ---- packed tiles: the new tokens of consecutive sequences that share a prompt's blocks
+
+PACKED_GROUPS = [(6, 300, (1, 200)), (3, 40, (5, 90)), (4, 200, (50, 300)), (2, 130, (100, 140))]
+
+
+def make_packed_case(seed, H, D, BS, dtype):
+    """Prompts shared by consecutive sequences (whole blocks), a prompt shorter than one
+    64-key stage (not packed), sequences sharing nothing; block ids permuted over a pool 1.2x
+    the need, slots no sequence uses NaN."""
+    qs, ctx, tables = W.shared_prompt_runs(seed, PACKED_GROUPS, BS, solo=[64, 700])
+    g = W.rng(seed + 1)
+    nb = int(tables.max()) + 1
+    perm = g.permutation(int(nb * 1.2) + 4).astype(np.int32)
+    tables = np.where(tables >= 0, perm[np.maximum(tables, 0)], -1).astype(np.int32)
+    NB = len(perm)
+    q = W.normal_values(g, (int(qs[-1]), H, D), dtype)
+    kp = W.normal_values(g, (NB, H, BS, D), dtype)
+    vp = W.normal_values(g, (NB, H, BS, D), dtype)
+    W.poison_unused(kp, tables, ctx, BS, dtype)
+    W.poison_unused(vp, tables, ctx, BS, dtype)
+    return q, kp, vp, tables, ctx, qs
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("BS", [8, 16, 32])
+def test_packed_tiles_match_the_oracle_and_the_grid_bit_for_bit(dtype, D, BS):
+    """Every row against the oracle; the packed launch (in schedule order and shuffled) gives
+    the plain grid's bits: each row sees the same keys in the same 64-key stages."""
+    dev = device()
+    H = 4
+    q, kp, vp, tables, ctx, qs = make_packed_case(4100 + BS + D + (dtype == "bf16"), H, D, BS,
+                                                  dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, BS, int(ctx.max()))
+    assert (tiles[:, 0] != tiles[:, 1]).any() and (tiles[:, 3] > 0).any()
+    print(f"packed {dtype} D{D} BS{BS}: {len(tiles)} tiles for {int(qs[-1])} rows", flush=True)
+    plain = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev)
+    packed = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, packed=tiles)
+    shuffled = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev,
+                      packed=tiles[W.rng(5).permutation(len(tiles))])
+    ref = oracle.paged_attention_multi_query(q, kp, vp, tables, ctx, qs, scale, dtype)
+    check_close(oracle.decode(packed, dtype), ref, dtype, f"packed {dtype} D{D} BS{BS}")
+    assert np.array_equal(plain.view(np.uint16), packed.view(np.uint16))
+    assert np.array_equal(plain.view(np.uint16), shuffled.view(np.uint16))
+
+
+def test_packed_tiles_recheck_what_they_share():
+    """Tiles made for other tables or lengths stay exact: (a) one sequence's shared block
+    moved to a copy with other values after scheduling -- the kernel's own check of the tables
+    finds it and reads every sequence's keys on its own; (b) shared-key counts larger than the
+    sequences' cached tokens are cut to them; (c) a sequence whose device length drops below
+    its new-token count gets NaN rows and the others are unaffected; (d) tiles naming no
+    sequence of the call, or with a shared-key count that is not whole stages, are ignored."""
+    dev = device()
+    dtype, H, D, BS = "f16", 4, 128, 16
+    q, kp, vp, tables, ctx, qs = make_packed_case(4200, H, D, BS, dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, BS, int(ctx.max()))
+    span = next(t for t in tiles.tolist() if t[1] > t[0] and t[3] > 0)
+    victim = span[1]
+    # (a): the victim's first block now lives in a new block holding other values
+    g = W.rng(4201)
+    NB = kp.shape[0]
+    kp2 = np.concatenate([kp, W.normal_values(g, (1, H, BS, D), dtype)])
+    vp2 = np.concatenate([vp, W.normal_values(g, (1, H, BS, D), dtype)])
+    t2 = tables.copy()
+    t2[victim, 0] = NB
+    got = run_mq(q, kp2, vp2, t2, ctx, qs, scale, dtype, dev, packed=tiles)
+    ref = oracle.paged_attention_multi_query(q, kp2, vp2, t2, ctx, qs, scale, dtype)
+    check_close(oracle.decode(got, dtype), ref, dtype, "packed tiles, moved shared block")
+    plain2 = run_mq(q, kp2, vp2, t2, ctx, qs, scale, dtype, dev)
+    assert np.array_equal(plain2.view(np.uint16), got.view(np.uint16))
+    # (b): every shared-key count inflated
+    big = tiles.copy()
+    big[:, 3] = np.where(big[:, 3] > 0, 64 * 64, 0)
+    plain = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev)
+    got = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, packed=big)
+    assert np.array_equal(plain.view(np.uint16), got.view(np.uint16))
+    # (c): the victim's device length below its new tokens
+    short = ctx.copy()
+    short[victim] = int(qs[victim + 1] - qs[victim]) - 1
+    got = oracle.decode(run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, dev_ctx=short,
+                               packed=tiles), dtype)
+    base = oracle.decode(plain, dtype)
+    rows = slice(int(qs[victim]), int(qs[victim + 1]))
+    assert np.isnan(got[rows]).all()
+    keep = np.ones(len(got), bool)
+    keep[rows] = False
+    assert np.array_equal(got[keep].view(np.uint16), base[keep].view(np.uint16))
+    # (d): nothing is written
+    S = len(ctx)
+    bad = np.array([[S, S, 0, 0], [S - 1, S, 0, 0], [-1, 0, 0, 0], [0, 0, 1 << 20, 0],
+                    [span[0], span[1], span[2], 32], [1, 0, 0, 0], [0, 0, -1, 0]], np.int32)
+    got = run_mq(q, kp, vp, tables, ctx, qs, scale, dtype, dev, packed=bad)
+    assert np.isnan(oracle.decode(got, dtype)).all()

@@ -1,0 +1,120 @@
+"""The packed multi-query tiles (pkv_multi_query_schedule_packed, host only): every new token in
+exactly one tile, a tile's sequences sharing its first keys in the same blocks before their
+first new token, runs of sharing sequences packed into full tiles, and bad arguments refused.
+The device side of the same tiles is checked against the oracle in test_gpu_multi_query.py."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_306_amd as pkv
+import workloads as W
+
+TILE = 128
+STAGE = 64
+
+
+def _batch(groups, seed=0, bs=16, solo=()):
+    qs, ctx, tables = W.shared_prompt_runs(seed, groups, bs, solo)
+    return qs, ctx, tables, bs
+
+
+def _check_tiles(tiles, qs, ctx, tables, bs, maxlen=1 << 30):
+    S = len(ctx)
+    covered = np.zeros(int(qs[-1]), np.int32)
+    for sa, sb, first, pre in tiles.tolist():
+        assert 0 <= sa <= sb < S and first >= 0 and pre >= 0 and pre % STAGE == 0
+        R0 = qs[sa] + first
+        assert first < qs[sa + 1] - qs[sa]
+        R1 = min(R0 + TILE, qs[sb + 1])
+        assert qs[sb] < R1                       # the tile reaches its last sequence
+        covered[R0:R1] += 1
+        if sa == sb:
+            continue
+        assert pre >= STAGE                      # only sharing sequences are packed
+        for m in range(sa, sb + 1):
+            L = min(int(ctx[m]), maxlen)
+            assert pre <= L - (qs[m + 1] - qs[m])           # before every new token
+            assert np.array_equal(tables[m, :pre // bs], tables[sa, :pre // bs])
+    assert np.all(covered == 1)
+
+
+def test_prefix_groups_pack_into_full_tiles():
+    # the prefix-hit shape: 4 prompts of 1024 tokens, 16 requests each, 16-512 new tokens
+    qs, ctx, tables, bs = _batch([(16, 1024, (16, 512))] * 4, seed=1)
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 1 << 20)
+    _check_tiles(tiles, qs, ctx, tables, bs)
+    per_group = [int(qs[16 * (k + 1)] - qs[16 * k]) for k in range(4)]
+    assert len(tiles) == sum(-(-r // TILE) for r in per_group)
+    assert set(tiles[:, 3].tolist()) == {1024}
+    n = np.diff(qs)
+    assert len(tiles) < sum(-(-int(x) // TILE) for x in n)   # fewer than one per sequence tile
+    # runs that read the most keys first, a run's tiles adjacent
+    runs = [int(t[0]) // 16 for t in tiles]
+    assert runs == sorted(runs, key=runs.index) and len(set(runs)) == 4
+    assert all(runs[i] == runs[i + 1] or runs[i + 1] not in runs[:i + 1]
+               for i in range(len(runs) - 1))
+
+
+def test_without_sharing_the_tiles_are_per_sequence():
+    qs, ctx, tables, bs = _batch([], seed=2, solo=[100, 5000, 300, 129, 1, 4000])
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 1 << 20)
+    _check_tiles(tiles, qs, ctx, tables, bs)
+    assert np.all(tiles[:, 0] == tiles[:, 1]) and np.all(tiles[:, 3] == 0)
+    n = np.diff(qs)
+    want = sorted((s, TILE * t) for s in range(len(n)) for t in range(-(-int(n[s]) // TILE)))
+    assert sorted(zip(tiles[:, 0].tolist(), tiles[:, 2].tolist())) == want
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_mixed_runs(bs):
+    # a prompt shared by 5, one of 40 tokens (less than a stage: not packed), one of 200
+    # tokens (three stages), solo sequences between them
+    qs, ctx, tables, _ = _batch([(5, 700, (1, 300)), (3, 40, (5, 90)), (4, 200, (50, 400))],
+                                seed=3, bs=bs, solo=[64, 3000])
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 1 << 20)
+    _check_tiles(tiles, qs, ctx, tables, bs)
+    pre = {int(t[0]): int(t[3]) for t in tiles}
+    assert all(pre[s] == 640 for s in pre if s < 5)
+    assert all(pre[s] == 0 for s in pre if 5 <= s < 8)
+    assert all(pre[s] == 192 for s in pre if 8 <= s < 12)
+    # max_context_len below the prompt's length caps what is shared
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 300)
+    _check_tiles(tiles, qs, ctx, tables, bs, maxlen=300)
+
+
+def test_a_sequence_sharing_fewer_keys_starts_a_new_run():
+    qs, ctx, tables, bs = _batch([(3, 512, (10, 20))], seed=4)
+    tables = np.concatenate([tables, tables[2:3]], 0)
+    tables[3, 8:] += 1000                     # shares only the first 128 tokens
+    ctx = np.concatenate([ctx, ctx[2:3]])
+    qs = np.concatenate([qs, [qs[-1] + 15]]).astype(np.int32)
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 1 << 20)
+    _check_tiles(tiles, qs, ctx, tables, bs)
+    assert sorted(tiles.tolist()) == [[0, 2, 0, 512], [3, 3, 0, 0]]
+
+
+def test_bad_arguments():
+    qs, ctx, tables, bs = _batch([(3, 256, (10, 20))], seed=5)
+    lib = pkv.lib()
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    buf = np.zeros((8, 4), np.int32)
+    S, mb = len(ctx), tables.shape[1]
+    args = lambda **k: [k.get("qs", ptr(qs)), k.get("cl", ptr(ctx)), k.get("bt", ptr(tables)),
+                        k.get("mb", mb), k.get("bs", bs), k.get("S", S), k.get("ml", 1 << 20),
+                        k.get("out", ptr(buf)), k.get("cap", 8)]
+    assert lib.pkv_multi_query_schedule_packed(*args()) == 1
+    assert lib.pkv_multi_query_schedule_packed(*args(cap=0)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(qs=None)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(bt=None)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(mb=0)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(bs=0)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(S=-1)) == -1
+    assert lib.pkv_multi_query_schedule_packed(*args(S=0, qs=None)) == 0
+    bad = qs.copy()
+    bad[2] = bad[1] - 1                       # decreasing
+    assert lib.pkv_multi_query_schedule_packed(*args(qs=ptr(bad))) == -1
+    with pytest.raises(ValueError):
+        pkv.multi_query_schedule_packed(qs[:-1], ctx, tables, bs, 1 << 20)
+    with pytest.raises(ValueError):
+        pkv.multi_query_schedule_packed(qs, ctx, tables[:-1], bs, 1 << 20)

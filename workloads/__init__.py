@@ -252,6 +252,43 @@ def long_context(seed: int = 4, block_size: int = 16) -> DecodeShape:
                        lens, tables, nb, float(np.float32(1.0 / math.sqrt(128))), seed)
 
 
+def shared_prompt_runs(seed: int, groups, block_size: int, solo=()):
+    """Consecutive sequences in groups, each group sharing the whole blocks of a prompt (a
+    partly filled last block is each member's own, as a prefix cache keeps it), then a few
+    cached tokens of each member's own and its new tokens; ``groups``: list of (members,
+    prompt tokens, (lo, hi) new tokens per member); ``solo``: context lengths of sequences that
+    share nothing, appended, each with U[1, L] new tokens.  Block ids are consecutive (callers
+    permute them).  Returns ``(query_start, context_lens, tables)``; tables are padded with
+    -1."""
+    g = rng(seed)
+    rows, lens, nxt = [], [], 0
+    for members, prompt, (lo, hi) in groups:
+        shared = list(range(nxt, nxt + prompt // block_size))
+        nxt += len(shared)
+        for _ in range(members):
+            own = int(g.integers(0, 40))
+            n = int(g.integers(lo, hi + 1))
+            L = prompt + own + n
+            k = nblocks_for(L, block_size) - len(shared)
+            rows.append(shared + list(range(nxt, nxt + k)))
+            nxt += k
+            lens.append((L, n))
+    for L in solo:
+        n = int(g.integers(1, L + 1))
+        k = nblocks_for(L, block_size)
+        rows.append(list(range(nxt, nxt + k)))
+        nxt += k
+        lens.append((L, n))
+    mb = max(len(r) for r in rows)
+    tables = np.full((len(rows), mb), -1, np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
+    ctx = np.array([L for L, _ in lens], np.int32)
+    n = np.array([n for _, n in lens], np.int64)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    return qs, ctx, tables
+
+
 def prefix_hit(seed: int = 6, requests: int = 64, prompts: int = 4, system_len: int = 1024,
                user_lo: int = 16, user_hi: int = 512, block_size: int = 16,
                dtype: str = "f16") -> DecodeShape:

@@ -484,7 +484,7 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * pkv_stepper_step(seqs[0..n-1]) does, in order:
  *   1. pkv_alloc_append_slots on the stepper's block manager (one new slot per sequence),
  *      then exports the dense block tables and lengths, into a pinned host staging area
- *      (two areas used alternately, so the host can prepare step i+1 while step i runs);
+ *      (eight areas used in turn, so the host can prepare later steps while step i runs);
  *   2. one prologue kernel on `stream` pulls the packed index data from the pinned area (over
  *      PCIe) into an area of d_index and, when there are no copy-on-write pairs, also
  *      appends the first layer's new K/V:
@@ -527,10 +527,13 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *
  * The stepper allocates only pinned host memory (staging areas, calibration stamps) and HIP
  * events of its own; the caller owns the device buffer d_index (pkv_stepper_index_bytes
- * bytes, 16-byte aligned: two areas used by alternate steps) and the workspace.  The host refills a staging area only after the
- * prologue that read it (two steps earlier) has finished; that launch records its own
- * completion marker, so no event packet sits between kernels.  pkv_stepper_last_index returns the
- * device address of the packed index data of the last step.
+ * bytes, 16-byte aligned: eight areas used by the steps in turn) and the workspace.  The
+ * host refills a staging area only after the prologue that read it (eight launches earlier)
+ * is known to have finished: every seventh prologue launch records its own completion marker
+ * (no event packet sits between kernels, and the few microseconds of idle GPU a marked
+ * launch leaves behind it come once every seven steps), and the host waits for the oldest
+ * marker at or after that prologue.  pkv_stepper_last_index returns the device address of
+ * the packed index data of the last step.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t (created with timing): event
  * 2l takes the start and event 2l+1 the end of layer l's attention launch, recorded by the
  * launch itself (hipExtLaunchKernel) so that no event packet sits between kernels; a step with

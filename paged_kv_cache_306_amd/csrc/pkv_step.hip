@@ -86,11 +86,18 @@ size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_ite
 
 }  // namespace
 
-// Two stages are used alternately.  Stage k owns a pinned host area and a device area of
-// d_index.  The prologue of step i reads the host area of its stage; the host refills that
-// area at step i+2 only after the completion event of step i's prologue launch has fired.  The
-// device area is rewritten at step i+2 by a kernel on the same stream, so step i's readers are
-// done.
+// kStages stages are used in turn.  Stage k owns a pinned host area and a device area of
+// d_index.  The prologue of launch i reads the host area of its stage; the host refills that
+// area at launch i + kStages only after a completion marker at or after launch i has fired.
+// Every kMarkEvery-th prologue launch carries such a marker (its own completion event): a
+// launch that carries one leaves the GPU idle for a few microseconds before the next kernel,
+// so markers are spread over several steps, and with kMarkEvery < kStages the kStages
+// launches before any launch always include a marked one.  The device area is rewritten at
+// launch i + kStages by a kernel on the same stream, so launch i's readers are done.
+constexpr int kStages = 8;
+constexpr int kMarkEvery = 7;
+static_assert(kMarkEvery < kStages, "a marked launch among any kStages consecutive ones");
+
 struct pkv_stepper {
   pkv_alloc_t* alloc = nullptr;
   pkv_cache_desc_t desc{};
@@ -109,10 +116,15 @@ struct pkv_stepper {
     int32_t* host = nullptr;        // pinned: tables | lens | slots | pairs | items
     const char* host_dev = nullptr; // the same memory as the device sees it
     char* dev = nullptr;            // device area of the same size inside d_index
-    hipEvent_t read = nullptr;      // completion of the prologue launch that read `host`
-    bool pending = false;
-  } stage[2];
-  int cur = 0;
+  } stage[kStages];
+  // Completion markers of marked prologue launches (launch -1: free), the number of prologue
+  // launches so far, and the last launch known on the host to have finished.
+  struct Mark {
+    hipEvent_t ev = nullptr;
+    int64_t launch = -1;
+  } mark[kStages];
+  int64_t launches = 0;
+  int64_t done_upto = -1;
   // XCD balance: the split the attention launches deal their units with (0: none), and its
   // measurement from the stamps one attention launch leaves in pinned host memory.
   enum Cal { kCalPending, kCalInFlight, kCalDone };
@@ -222,8 +234,8 @@ extern "C" {
 size_t pkv_stepper_index_bytes(const pkv_cache_desc_t* desc, int32_t max_seqs,
                                int32_t max_blocks_per_seq) {
   if (pkv::check_desc(desc) != PKV_OK || max_seqs <= 0 || max_blocks_per_seq <= 0) return 0;
-  return 2 * stage_bytes(max_seqs, max_blocks_per_seq,
-                         max_work_items(desc, max_seqs, max_blocks_per_seq));
+  return kStages * stage_bytes(max_seqs, max_blocks_per_seq,
+                               max_work_items(desc, max_seqs, max_blocks_per_seq));
 }
 
 pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* desc,
@@ -239,7 +251,7 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   st->max_blocks = max_blocks_per_seq;
   st->max_items = max_work_items(desc, max_seqs, max_blocks_per_seq);
   const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq, st->max_items);
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kStages; ++k) {
     auto& sg = st->stage[k];
     sg.dev = static_cast<char*>(d_index) + k * bytes;
     // The staging area is fine-grained (coherent) host memory, so the prologue's reads of it
@@ -251,7 +263,8 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
     if (hipHostMalloc(reinterpret_cast<void**>(&sg.host), bytes,
                       hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
         hipHostGetDevicePointer(&dptr, sg.host, 0) != hipSuccess ||
-        hipEventCreateWithFlags(&sg.read, hipEventDisableTiming | hipEventDisableSystemFence) !=
+        hipEventCreateWithFlags(&st->mark[k].ev,
+                                hipEventDisableTiming | hipEventDisableSystemFence) !=
             hipSuccess) {
       (void)hipGetLastError();
       pkv_stepper_destroy(st);
@@ -283,13 +296,17 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
 
 void pkv_stepper_destroy(pkv_stepper_t* st) {
   if (!st) return;
-  for (auto& sg : st->stage) {
-    if (sg.read) {
-      if (sg.pending) (void)hipEventSynchronize(sg.read);
-      (void)hipEventDestroy(sg.read);
-    }
+  // prologues still reading the staging areas (the last ones carry no marker)
+  for (auto& mk : st->mark)
+    if (mk.ev && mk.launch >= 0) (void)hipEventSynchronize(mk.ev);
+  if (st->launched && st->handoff &&
+      hipEventRecord(st->handoff, st->last_stream) == hipSuccess)
+    (void)hipEventSynchronize(st->handoff);
+  (void)hipGetLastError();
+  for (auto& mk : st->mark)
+    if (mk.ev) (void)hipEventDestroy(mk.ev);
+  for (auto& sg : st->stage)
     if (sg.host) (void)hipHostFree(sg.host);
-  }
   if (st->handoff) (void)hipEventDestroy(st->handoff);
   if (st->cal_done) {
     // a stamped launch still running writes into cal_host
@@ -329,11 +346,28 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int32_t L = io->num_layers;
 
   if (st->cal == pkv_stepper::kCalInFlight) poll_calibration(st);
-  auto& sg = st->stage[st->cur ^ 1];
-  if (sg.pending) {
-    // the prologue that read this host area two steps ago must be done with it
-    if (hipEventSynchronize(sg.read) != hipSuccess) return PKV_EHIP;
-    sg.pending = false;
+  const int64_t launch = st->launches;  // this step's prologue launch
+  auto& sg = st->stage[launch % kStages];
+  const int64_t prev = launch - kStages;  // the launch that last read this host area
+  if (prev > st->done_upto) {
+    // wait for the oldest marker at or after it (one of the kStages launches before this one
+    // carries a marker), which frees every area read up to that launch
+    int pick = -1;
+    for (int k = 0; k < kStages; ++k)
+      if (st->mark[k].launch >= prev &&
+          (pick < 0 || st->mark[k].launch < st->mark[pick].launch))
+        pick = k;
+    if (pick < 0 || hipEventSynchronize(st->mark[pick].ev) != hipSuccess) return PKV_EHIP;
+    st->done_upto = st->mark[pick].launch;
+    for (auto& mk : st->mark)
+      if (mk.launch <= st->done_upto) mk.launch = -1;
+  }
+  // this launch's marker, if it carries one: a free marker (at most two are outstanding)
+  int mark_slot = -1;
+  if (launch % kMarkEvery == 0) {
+    for (int k = 0; k < kStages && mark_slot < 0; ++k)
+      if (st->mark[k].launch < 0) mark_slot = k;
+    if (mark_slot < 0) return PKV_EHIP;
   }
   // A step on another stream than the last one first waits for all the last stream queued:
   // the two share the staging areas, the device index area and the workspace.
@@ -342,7 +376,6 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       (hipEventRecord(st->handoff, st->last_stream) != hipSuccess ||
        hipStreamWaitEvent(hs, st->handoff, 0) != hipSuccess))
     return PKV_EHIP;
-  st->cur ^= 1;
 
   const int32_t MB = st->max_blocks;
   int32_t* tables = sg.host;
@@ -395,13 +428,14 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
 
   const int32_t* slots_host_dev =
       reinterpret_cast<const int32_t*>(sg.host_dev) + static_cast<size_t>(n) * MB + n;
-  // The marker that frees this staging area is the prologue launch's own completion (the
-  // launch records sg.read when the kernel ends): the prologue is the only reader of the
-  // area, and an event recorded on the stream between two kernels would leave the GPU idle
-  // for a few microseconds.  The host waits on it only two steps later.
+  // A marker that frees this staging area is a prologue launch's own completion (the launch
+  // records it when the kernel ends): the prologue is the only reader of the area, and an
+  // event recorded on the stream between two kernels would leave the GPU idle for a few
+  // microseconds.  The host waits on one only kStages - kMarkEvery launches later, at least.
   hipExtLaunchKernelGGL(
       step_prologue_kernel, dim3(static_cast<unsigned>(copy_wgs + append_wgs)),
-      dim3(kPrologueThreads), 0, hs, nullptr, sg.read, 0u,
+      dim3(kPrologueThreads), 0, hs, nullptr,
+      mark_slot >= 0 ? st->mark[mark_slot].ev : nullptr, 0u,
       reinterpret_cast<const pkv::u32x4*>(sg.host_dev),
       reinterpret_cast<pkv::u32x4*>(sg.dev), idx_vecs, copy_wgs, slots_host_dev,
       fuse_append ? static_cast<const pkv::u32x4*>(io->k_new[0]) : nullptr,
@@ -411,7 +445,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       st->desc.num_heads, st->desc.block_size,
       static_cast<int64_t>(st->desc.num_blocks) * st->desc.block_size);
   if (hipGetLastError() != hipSuccess) return PKV_EHIP;
-  sg.pending = true;
+  if (mark_slot >= 0) st->mark[mark_slot].launch = launch;
+  st->launches = launch + 1;
   st->launched = true;
   st->last_stream = hs;
 
@@ -456,7 +491,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
 }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {
-  return st ? st->stage[st->cur].dev : nullptr;
+  return st ? st->stage[st->launches > 0 ? (st->launches - 1) % kStages : 0].dev : nullptr;
 }
 
 int32_t pkv_stepper_xcd_split(const pkv_stepper_t* st) { return st ? st->xcd_split : -1; }

@@ -87,13 +87,14 @@ def test_small_two_layer_step_with_copy_on_write():
 
 
 def test_consecutive_steps_without_host_sync():
-    """Eight steps issued back to back behind a long GPU job, with new q / K / V every step and
+    """Twenty steps issued back to back behind a long GPU job, with new q / K / V every step and
     sequences that cross into fresh blocks.  The host runs ahead of the GPU, so it refills each
-    of the two staging areas only on the completion of the prologue that read it; every step's
-    output and the final pools match the oracle replaying the same block-manager decisions."""
+    of the eight staging areas only once a completion marker (every seventh prologue carries
+    one) at or after the prologue that read it has fired; every step's output and the final
+    pools match the oracle replaying the same block-manager decisions."""
     import torch
     dev = device()
-    H, D, BS, dt, steps, scale = 4, 128, 16, "f16", 8, 0.1
+    H, D, BS, dt, steps, scale = 4, 128, 16, "f16", 20, 0.1
     NB, MB = 200, 16
     g = W.rng(321)
     order = g.permutation(NB)

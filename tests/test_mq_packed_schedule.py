@@ -118,3 +118,23 @@ def test_bad_arguments():
         pkv.multi_query_schedule_packed(qs[:-1], ctx, tables, bs, 1 << 20)
     with pytest.raises(ValueError):
         pkv.multi_query_schedule_packed(qs, ctx, tables[:-1], bs, 1 << 20)
+
+
+def test_a_sequence_with_more_new_tokens_than_context_is_not_packed():
+    # its rows come out NaN on the device; the schedule keeps it out of the run around it
+    qs, ctx, tables, bs = _batch([(5, 512, (10, 60))], seed=6)
+    bad = 2
+    n_bad = int(qs[bad + 1] - qs[bad])
+    ctx = ctx.copy()
+    ctx[bad] = n_bad - 1
+    tiles = pkv.multi_query_schedule_packed(qs, ctx, tables, bs, 1 << 20)
+    covered = np.zeros(int(qs[-1]), np.int32)
+    for sa, sb, first, pre in tiles.tolist():
+        R0 = qs[sa] + first
+        covered[R0:min(R0 + TILE, qs[sb + 1])] += 1
+        if sa <= bad <= sb:
+            assert sa == sb == bad and pre == 0
+        if sb > sa:
+            assert pre == 512
+    assert np.all(covered == 1)
+    assert sorted(t[:2] for t in tiles.tolist()) == [[0, 1], [2, 2], [3, 4]]

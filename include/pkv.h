@@ -533,7 +533,9 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  * (no event packet sits between kernels, and the few microseconds of idle GPU a marked
  * launch leaves behind it come once every seven steps), and the host waits for the oldest
  * marker at or after that prologue.  pkv_stepper_last_index returns the device address of
- * the packed index data of the last step.
+ * the packed index data of the last step.  pkv_stepper_destroy waits until the stepper's
+ * prologues are done with the staging areas before freeing them (it records an event on the
+ * stream of the last step), so destroy the stepper before that stream.
  * attn_events: NULL, or a host array of 2 * num_layers hipEvent_t (created with timing): event
  * 2l takes the start and event 2l+1 the end of layer l's attention launch, recorded by the
  * launch itself (hipExtLaunchKernel) so that no event packet sits between kernels; a step with

@@ -1120,6 +1120,10 @@ def main():
     dt_name = {"f16": "F16", "bf16": "BF16", "f32": "F32"}[b.dtype]
     kname = f"decode_partition_kernel<{dt_name},{b.D},{b.BS}>"
     kname += " + decode_reduce_kernel (split context)" if split else " (single pass: one launch)"
+    if b.stepper.last_attention == pkv.PKV_STEP_ATTN_MULTI_QUERY:
+        # groups sharing their first blocks: the step driver attends through packed tiles
+        kname = (f"multi_query_kernel<{dt_name},{b.D},{b.BS}> over packed tiles (sequences "
+                 "sharing their first blocks, one new token each)")
     default = args.workload == "llama13b_layer" and args.placement == "permuted"
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -496,7 +496,15 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *   4. for each layer l: pkv_reshape_and_cache(k_new[l], v_new[l] -> pools[l]) (done by the
  *      prologue for layer 0 when there was no copy), then
  *      pkv_paged_attention_decode_scheduled(q[l] -> out[l]) with the lengths including the
- *      new token.
+ *      new token -- or, when sequences share their first blocks (parallel sampling, beam
+ *      search, a cached prompt: "Advanced Features" -> "KV-Cache Sharing"), the cache is f16
+ *      or bf16, q and out are 16-byte aligned, no context exceeds 4096 tokens, the packed
+ *      tiles (pkv_multi_query_schedule_packed, one new token per sequence) hold two sequences
+ *      or more on average and number at least 512 / num_heads, the same attention through
+ *      pkv_paged_attention_multi_query_packed, which stages each group's shared blocks once
+ *      for all its members (the index area then holds query_start [n + 1] and the tiles
+ *      after the pairs).  pkv_stepper_last_attention tells which ran (PKV_STEP_ATTN_*; -1
+ *      before any step and after a step with n = 0).
  * Everything after step 1 is asynchronous on `stream`.
  *
  * Errors.  Before step 1 the call makes every check pkv_stepper_check makes (below) and
@@ -585,6 +593,9 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
                               void* const* attn_events, int32_t* max_len, int32_t* num_cow,
                               int32_t* num_done, pkv_stream_t stream);
 const void* pkv_stepper_last_index(const pkv_stepper_t* st);
+int32_t pkv_stepper_last_attention(const pkv_stepper_t* st);
+#define PKV_STEP_ATTN_DECODE 0       /* pkv_paged_attention_decode_scheduled */
+#define PKV_STEP_ATTN_MULTI_QUERY 1  /* pkv_paged_attention_multi_query_packed */
 int32_t pkv_stepper_xcd_split(const pkv_stepper_t* st);
 pkv_status_t pkv_stepper_set_xcd_split(pkv_stepper_t* st, int32_t split);
 #define PKV_XCD_NONE 0       /* nothing measured (yet) */

@@ -100,6 +100,7 @@ _SIGNATURES = {
     "pkv_alloc_move_seqs": (_i32, [_p, _p, _p, _i32, _p, _i32, _pi32]),
     "pkv_swap_blocks": (_i32, [_pdesc, _pdesc, _p, _p, _p, _p, _i32, _p, _i32, _p]),
     "pkv_stepper_index_bytes": (_sz, [_pdesc, _i32, _i32]),
+    "pkv_stepper_last_attention": (_i32, [_p]),
     "pkv_stepper_create": (_p, [_p, _pdesc, _i32, _i32, _p]),
     "pkv_stepper_destroy": (None, [_p]),
     "pkv_stepper_step": (_i32, [_p, _p, _i32, _p, _p, _sz, _p, _pi32, _pi32, _pi32, _p]),
@@ -216,6 +217,7 @@ def decode_xcd_slot_unit(slot: int, units: int, split: int) -> int:
 
 
 PKV_DECODE_SHARED_KV = 1
+PKV_STEP_ATTN_DECODE, PKV_STEP_ATTN_MULTI_QUERY = 0, 1   # pkv_stepper_last_attention
 # outcome of a stepper's XCD measurement (pkv_stepper_xcd_rates)
 PKV_XCD_NONE, PKV_XCD_IN_FLIGHT, PKV_XCD_MEASURED, PKV_XCD_TOO_FEW, PKV_XCD_UNMAPPED, \
     PKV_XCD_FAILED = range(6)
@@ -793,6 +795,12 @@ class DecodeStepper:
             err.num_done = self._ndone.value
             raise err
         return self._max_len.value, self._ncow.value
+
+    @property
+    def last_attention(self) -> int:
+        """Which attention the last step ran: PKV_STEP_ATTN_DECODE, PKV_STEP_ATTN_MULTI_QUERY
+        (sequences sharing their first blocks, packed tiles), or -1 (no step with sequences)."""
+        return int(_lib().pkv_stepper_last_attention(self._h))
 
     @property
     def xcd_split(self) -> int:

@@ -50,6 +50,16 @@ pkv_status_t decode_scheduled_timed(const pkv_cache_desc_t* desc, void* out, con
                                     void* ev_start, void* ev_stop, int32_t xcd_split = 0,
                                     uint32_t* stamps = nullptr);
 
+// pkv_paged_attention_multi_query_packed with optional timing (ev_start / ev_stop as above).
+pkv_status_t multi_query_packed_timed(const pkv_cache_desc_t* desc, void* out, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, const int32_t* query_start,
+                                      int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                                      int32_t max_context_len, float scale, const int32_t* tiles,
+                                      int32_t num_tiles, pkv_stream_t stream, void* ev_start,
+                                      void* ev_stop);
+
 // The XCD split the stand-alone decode calls on the current device use from now on (a step
 // driver's measurement); out-of-range values are ignored.
 void set_device_xcd_split(int32_t split);

@@ -33,6 +33,7 @@
 //   * O^T accumulates in 16 x 16 tiles: lane (r, g) holds output elements d = 16 t + 4 g + i
 //     of query r.  The softmax denominator sums the same rounded probabilities: with v_dot2
 //     per lane at fp16, through one more tile whose V^T rows are all ones at bf16.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -698,16 +699,17 @@ struct MqArgs {
   int max_len;
   float scale_log2;
   hipStream_t stream;
+  hipEvent_t start, stop;  // taken by the launch itself, or null
 };
 
 template <class Ty, int D, int BS>
 static void launch_mq(const MqArgs& a) {
   using T = typename Ty::store_t;
   if (a.wgs <= 0) return;
-  hipLaunchKernelGGL((a.packed ? multi_query_kernel<Ty, D, BS, true>
-                               : multi_query_kernel<Ty, D, BS, false>),
+  hipExtLaunchKernelGGL((a.packed ? multi_query_kernel<Ty, D, BS, true>
+                                  : multi_query_kernel<Ty, D, BS, false>),
                      dim3(static_cast<unsigned>(a.wgs)),
-                     dim3(kMqThreads), 0, a.stream, static_cast<T*>(a.out),
+                     dim3(kMqThreads), 0, a.stream, a.start, a.stop, 0u, static_cast<T*>(a.out),
                      static_cast<const T*>(a.q), static_cast<const char*>(a.k_pool),
                      static_cast<const char*>(a.v_pool), a.block_tables, a.max_blocks,
                      a.context_lens, a.query_start, a.work, a.packed, a.num_seqs, a.num_tokens,
@@ -915,7 +917,8 @@ static pkv_status_t mq_launch(const pkv_cache_desc_t* desc, void* out, const voi
                               int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
                               int32_t max_context_len, float scale, const int32_t* work_items,
                               const int32_t* packed, bool use_packed, int32_t num_items,
-                              pkv_stream_t stream) {
+                              pkv_stream_t stream, void* ev_start = nullptr,
+                              void* ev_stop = nullptr) {
   pkv_status_t st = check_desc(desc);
   if (st != PKV_OK) return st;
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
@@ -963,6 +966,8 @@ static pkv_status_t mq_launch(const pkv_cache_desc_t* desc, void* out, const voi
       max_context_len, static_cast<int64_t>(max_blocks_per_seq) * desc->block_size));
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.stream = static_cast<hipStream_t>(stream);
+  a.start = static_cast<hipEvent_t>(ev_start);
+  a.stop = static_cast<hipEvent_t>(ev_stop);
 
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this launch
   st = desc->dtype == PKV_F16 ? mq_dispatch_d<F16>(desc->head_dim, desc->block_size, a)
@@ -970,6 +975,23 @@ static pkv_status_t mq_launch(const pkv_cache_desc_t* desc, void* out, const voi
   if (st != PKV_OK) return st;
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
+
+}  // extern "C"
+
+pkv_status_t pkv::multi_query_packed_timed(
+    const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,
+    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+    int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale,
+    const int32_t* tiles, int32_t num_tiles, pkv_stream_t stream, void* ev_start,
+    void* ev_stop) {
+  return mq_launch(desc, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                   context_lens, query_start, num_seqs, num_tokens, max_query_len,
+                   max_context_len, scale, nullptr, tiles, true, num_tiles, stream, ev_start,
+                   ev_stop);
+}
+
+extern "C" {
 
 pkv_status_t pkv_paged_attention_multi_query(
     const pkv_cache_desc_t* desc, void* out, const void* q, const void* k_pool,

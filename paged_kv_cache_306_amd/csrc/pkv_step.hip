@@ -75,9 +75,19 @@ int32_t max_work_items(const pkv_cache_desc_t* d, int32_t n, int32_t max_blocks)
 }
 
 size_t index_ints(int32_t n, int32_t max_blocks, int32_t max_items) {
-  // tables [n][max_blocks], lens [n], slots [n], pairs [n][2], work items [max_items]
-  return static_cast<size_t>(n) * max_blocks + 4 * static_cast<size_t>(n) + max_items;
+  // tables [n][max_blocks], lens [n], slots [n], pairs [n][2], then either the decode work
+  // items [max_items] or, for the multi-query path, query_start [n + 1], padding to 16 bytes
+  // and packed tiles [n][4]
+  return static_cast<size_t>(n) * max_blocks + 4 * static_cast<size_t>(n) +
+         std::max<size_t>(max_items, 5 * static_cast<size_t>(n) + 4);
 }
+
+// Decode of sequences that share their first blocks goes through the multi-query kernel over
+// packed tiles when its launch has at least this many workgroups, when at least two
+// sequences share each tile on average, and when no context is longer than this (longer ones
+// need the decode's split into partitions to spread over the chip).
+constexpr int64_t kMqMinWorkgroups = 512;
+constexpr int32_t kMqMaxContext = 4096;
 
 size_t stage_bytes(int32_t max_seqs, int32_t max_blocks_per_seq, int32_t max_items) {
   return static_cast<size_t>(pkv::align_up(
@@ -125,6 +135,8 @@ struct pkv_stepper {
   } mark[kStages];
   int64_t launches = 0;
   int64_t done_upto = -1;
+  bool mq_ok = false;       // the multi-query kernel supports this cache's shape and type
+  int32_t last_kernel = -1; // PKV_STEP_ATTN_* of the last step's attention launches
   // XCD balance: the split the attention launches deal their units with (0: none), and its
   // measurement from the stamps one attention launch leaves in pinned host memory.
   enum Cal { kCalPending, kCalInFlight, kCalDone };
@@ -250,6 +262,8 @@ pkv_stepper_t* pkv_stepper_create(pkv_alloc_t* alloc, const pkv_cache_desc_t* de
   st->max_seqs = max_seqs;
   st->max_blocks = max_blocks_per_seq;
   st->max_items = max_work_items(desc, max_seqs, max_blocks_per_seq);
+  st->mq_ok = (desc->dtype == PKV_F16 || desc->dtype == PKV_BF16) && max_seqs <= (1 << 20) &&
+              static_cast<int64_t>(max_seqs) * max_blocks_per_seq <= UINT32_MAX;
   const size_t bytes = stage_bytes(max_seqs, max_blocks_per_seq, st->max_items);
   for (int k = 0; k < kStages; ++k) {
     auto& sg = st->stage[k];
@@ -327,6 +341,7 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   *max_len = 0;
   *num_cow = 0;
   *num_done = 0;
+  st->last_kernel = -1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (n == 0) {
     // nothing to attend: timing events, if any, are recorded back to back (zero duration)
@@ -405,15 +420,38 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const bool shared =
       std::adjacent_find(st->sorted_keys.begin(), st->sorted_keys.end()) != st->sorted_keys.end();
   int32_t* items = pairs + 2 * static_cast<size_t>(*num_cow);
-  const int32_t num_items =
-      shared ? pkv_decode_schedule_grouped(&st->desc, lens, st->keys.data(), n, *max_len, items,
-                                           st->max_items)
-             : pkv_decode_schedule(&st->desc, lens, n, *max_len, items, st->max_items);
-  if (num_items < 0) return PKV_EINVAL;
+  // Groups that share their first blocks (parallel sampling, beam search, a cached prompt):
+  // the multi-query kernel over packed tiles, one new token per sequence, stages each group's
+  // shared blocks once for all its members, where the decode reads them once per member
+  // (from L2).  It needs enough tiles to fill the chip and contexts short enough to need no
+  // split.  The staging area then holds query_start (0 .. n) and the tiles after the pairs.
+  const size_t qs_off = static_cast<size_t>(items - tables);
+  const size_t tiles_off = (qs_off + n + 1 + 3) / 4 * 4;  // 16-byte aligned on the device
+  int32_t num_tiles = 0;
+  bool mq = false;
+  bool mq_aligned = true;  // the multi-query kernel reads q and writes out 16 bytes at a time
+  for (int32_t l = 0; l < L; ++l)
+    mq_aligned = mq_aligned && reinterpret_cast<uintptr_t>(io->q[l]) % 16 == 0 &&
+                 reinterpret_cast<uintptr_t>(io->out[l]) % 16 == 0;
+  if (shared && st->mq_ok && mq_aligned && *max_len <= kMqMaxContext) {
+    for (int32_t i = 0; i <= n; ++i) tables[qs_off + i] = i;
+    num_tiles = pkv_multi_query_schedule_packed(tables + qs_off, lens, tables, MB,
+                                                st->desc.block_size, n, *max_len,
+                                                tables + tiles_off, n);
+    mq = num_tiles > 0 && 2 * static_cast<int64_t>(num_tiles) <= n &&
+         static_cast<int64_t>(num_tiles) * st->desc.num_heads >= kMqMinWorkgroups;
+  }
+  int32_t num_items = 0;
+  if (!mq) {
+    num_items = shared ? pkv_decode_schedule_grouped(&st->desc, lens, st->keys.data(), n,
+                                                     *max_len, items, st->max_items)
+                       : pkv_decode_schedule(&st->desc, lens, n, *max_len, items, st->max_items);
+    if (num_items < 0) return PKV_EINVAL;
+  }
   const uint32_t decode_flags = shared ? PKV_DECODE_SHARED_KV : 0u;
 
-  const size_t used_ints = static_cast<size_t>(n) * MB + 2 * static_cast<size_t>(n) +
-                           2 * static_cast<size_t>(*num_cow) + num_items;
+  const size_t used_ints = mq ? tiles_off + 4 * static_cast<size_t>(num_tiles)
+                              : qs_off + static_cast<size_t>(num_items);
   const int idx_vecs = static_cast<int>((used_ints * 4 + 15) / 16);
   const int copy_wgs = (idx_vecs + kPrologueThreads * kCopyVecsPerThread - 1) /
                        (kPrologueThreads * kCopyVecsPerThread);
@@ -455,6 +493,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   const int32_t* d_slots = d_lens + n;
   const int32_t* d_pairs = d_slots + n;
   const int32_t* d_items = d_pairs + 2 * static_cast<size_t>(*num_cow);
+  const int32_t* d_qs = d_tables + qs_off;
+  const int32_t* d_tiles = d_tables + tiles_off;
 
   if (*num_cow > 0 && L > 0) {
     s = pkv_copy_blocks(&st->desc, io->k_pools, io->v_pools, L, d_pairs, *num_cow, stream);
@@ -462,8 +502,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   }
   // The first step with enough units measures the XCD halves on its layer-0 attention.
   const int64_t units = static_cast<int64_t>(num_items) * st->desc.num_heads;
-  const bool stamp = st->cal == pkv_stepper::kCalPending && L > 0 && units >= kCalMinUnits &&
-                     units <= st->cal_capacity;
+  const bool stamp = !mq && st->cal == pkv_stepper::kCalPending && L > 0 &&
+                     units >= kCalMinUnits && units <= st->cal_capacity;
   if (stamp) std::memset(st->cal_host, 0, static_cast<size_t>(units) * 16);
   for (int32_t l = 0; l < L; ++l) {
     if (!(l == 0 && fuse_append)) {
@@ -473,6 +513,15 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
     }
     // timing, when asked for, comes from the attention launch itself
     const bool stamp_here = stamp && l == 0;
+    if (mq) {
+      s = pkv::multi_query_packed_timed(&st->desc, io->out[l], io->q[l], io->k_pools[l],
+                                        io->v_pools[l], d_tables, MB, d_lens, d_qs, n, n, 1,
+                                        *max_len, io->scale, d_tiles, num_tiles, stream,
+                                        attn_events ? attn_events[2 * l] : nullptr,
+                                        attn_events ? attn_events[2 * l + 1] : nullptr);
+      if (s != PKV_OK) return s;
+      continue;
+    }
     s = pkv::decode_scheduled_timed(&st->desc, io->out[l], io->q[l], io->k_pools[l],
                                     io->v_pools[l], d_tables, MB, d_lens, n, *max_len, io->scale,
                                     d_items, num_items, decode_flags, workspace, workspace_bytes,
@@ -487,8 +536,11 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
       st->cal_units = units;
     }
   }
+  st->last_kernel = mq ? PKV_STEP_ATTN_MULTI_QUERY : PKV_STEP_ATTN_DECODE;
   return PKV_OK;
 }
+
+int32_t pkv_stepper_last_attention(const pkv_stepper_t* st) { return st ? st->last_kernel : -1; }
 
 const void* pkv_stepper_last_index(const pkv_stepper_t* st) {
   return st ? st->stage[st->launches > 0 ? (st->launches - 1) % kStages : 0].dev : nullptr;

@@ -155,7 +155,8 @@ def test_consecutive_steps_without_host_sync():
 def test_fork_step_shared_prefix_copy_on_write():
     """32 groups x 8 sequences forked from a 512 + r (r in [1, 15]) token prompt: one decode
     step copies each group's shared partial block 7 times (the 8th writer owns it) -- 224
-    pairs -- then appends and attends.  Whole pools are compared bit for bit."""
+    pairs -- then appends and attends (through packed multi-query tiles: the groups share
+    their first 32 blocks).  Whole pools are compared bit for bit."""
     import torch
     dev = device()
     H, D, BS, dt = 40, 128, 16, "f16"
@@ -184,6 +185,8 @@ def test_fork_step_shared_prefix_copy_on_write():
                            MB * BS)
     max_len, ncow = st.step(seqs)
     torch.cuda.synchronize()
+    # 32 groups sharing 512 tokens each: packed multi-query tiles, one per group and head
+    assert st.last_attention == pkv.PKV_STEP_ATTN_MULTI_QUERY
     mslots, mpairs, _ = m.append_slots(seqs.tolist())
     assert ncow == len(mpairs) == 7 * G == 224
     ck, cv = oracle.copy_blocks([kp, vp], mpairs)
@@ -459,3 +462,73 @@ def test_steps_alternating_between_streams():
         ref = oracle.paged_attention_decode(q, ek, ev, tables, lens, scale, dt)
         check_close(oracle.decode(W.from_torch(outs[i], dt), dt), ref, dt, f"step {i}")
     assert np.array_equal(W.from_torch(kpt, dt).view(np.uint16), ek.view(np.uint16))
+
+
+@pytest.mark.parametrize("dt,D,BS", [("f16", 128, 16), ("bf16", 128, 32), ("f16", 64, 8)])
+def test_shared_groups_attend_through_packed_tiles(dt, D, BS):
+    """Sequences in groups that share a prompt's blocks: the step driver attends through the
+    multi-query kernel over packed tiles (one new token per sequence) when the tiles fill the
+    chip, and through the decode kernel otherwise; two steps each, every unit against the
+    oracle replaying the same block-manager decisions."""
+    import torch
+    dev = device()
+    H, steps = 40, 2
+    for groups, expect in ((16, pkv.PKV_STEP_ATTN_MULTI_QUERY), (4, pkv.PKV_STEP_ATTN_DECODE)):
+        print(f"[packed step] {dt} D{D} BS{BS}: {groups} groups of 8", flush=True)
+        qs_, ctx, tables0 = W.shared_prompt_runs(900 + groups, [(8, 320, (1, 100))] * groups, BS)
+        S = len(ctx)
+        MB = int(tables0.shape[1]) + 2
+        NB = int(tables0.max()) + 1 + S * 2 + 8
+        order = W.rng(901).permutation(NB)
+        a = pkv.BlockAllocator(NB, BS, free_order=order)
+        m = oracle.BlockManager(NB, BS, free_order=order)
+        # each group: the first member takes the prompt, the others fork it, then every member
+        # grows its own cached tokens
+        base = 0
+        for grp in range(groups):
+            lead = grp * 8
+            for sid in (lead,):
+                a.add_seq(sid, 320)
+                m.add_seq(sid, 320)
+            for j in range(1, 8):
+                a.fork(lead, lead + j)
+                m.fork(lead, lead + j)
+        seqs = np.arange(S, dtype=np.int64)
+        grow = (ctx - 320).astype(np.int64)
+        for _ in range(int(grow.max())):
+            sel = seqs[grow > 0]
+            a.append_slots(sel)
+            m.append_slots(sel.tolist())
+            grow[grow > 0] -= 1
+        g = W.rng(902)
+        kp = W.normal_values(g, (NB, H, BS, D), dt)
+        vp = W.normal_values(g, (NB, H, BS, D), dt)
+        qs = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+        kn = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+        vn = [W.normal_values(g, (S, H, D), dt) for _ in range(steps)]
+        kpt, vpt = to_dev(kp, dt, dev), to_dev(vp, dt, dev)
+        q_t, kn_t, vn_t = (to_dev(x[0], dt, dev) for x in (qs, kn, vn))
+        out_t = torch.empty_like(q_t)
+        scale = 1 / math.sqrt(D)
+        st = pkv.DecodeStepper(a, [kpt], [vpt], [q_t], [kn_t], [vn_t], [out_t], scale, S, MB,
+                               MB * BS)
+        ek, ev = kp, vp
+        for i in range(steps):
+            q_t.copy_(to_dev(qs[i], dt, dev))
+            kn_t.copy_(to_dev(kn[i], dt, dev))
+            vn_t.copy_(to_dev(vn[i], dt, dev))
+            st.step(seqs)
+            torch.cuda.synchronize()
+            assert st.last_attention == expect, (groups, st.last_attention)
+            mslots, mpairs, _ = m.append_slots(seqs.tolist())
+            ek, ev = oracle.copy_blocks([ek, ev], mpairs)
+            ek, ev = oracle.reshape_and_cache(kn[i], vn[i], ek, ev, np.array(mslots))
+            lens = np.array([m.seq_len(int(s)) for s in seqs], np.int32)
+            tab = np.full((S, MB), -1, np.int32)
+            for j, s_ in enumerate(seqs):
+                row = m.block_table(int(s_))
+                tab[j, :len(row)] = row
+            ref = oracle.paged_attention_decode(qs[i], ek, ev, tab, lens, scale, dt)
+            check_close(oracle.decode(W.from_torch(out_t, dt), dt), ref, dt,
+                        f"{groups} groups, step {i}")
+        del st

@@ -433,7 +433,8 @@ pkv_status_t pkv_stepper_step(pkv_stepper_t* st, const int64_t* seqs, int32_t n,
   for (int32_t l = 0; l < L; ++l)
     mq_aligned = mq_aligned && reinterpret_cast<uintptr_t>(io->q[l]) % 16 == 0 &&
                  reinterpret_cast<uintptr_t>(io->out[l]) % 16 == 0;
-  if (shared && st->mq_ok && mq_aligned && *max_len <= kMqMaxContext) {
+  // (the multi-query kernel also takes only a positive scale; the decode takes any finite one)
+  if (shared && st->mq_ok && mq_aligned && io->scale > 0.0f && *max_len <= kMqMaxContext) {
     for (int32_t i = 0; i <= n; ++i) tables[qs_off + i] = i;
     num_tiles = pkv_multi_query_schedule_packed(tables + qs_off, lens, tables, MB,
                                                 st->desc.block_size, n, *max_len,

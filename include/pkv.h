@@ -500,7 +500,7 @@ int64_t pkv_alloc_wasted_slots(const pkv_alloc_t* a);
  *      search, a cached prompt: "Advanced Features" -> "KV-Cache Sharing"), the cache is f16
  *      or bf16, q and out are 16-byte aligned, no context exceeds 4096 tokens, the packed
  *      tiles (pkv_multi_query_schedule_packed, one new token per sequence) hold two sequences
- *      or more on average and number at least 512 / num_heads, the same attention through
+ *      or more on average and number at least 448 / num_heads, the same attention through
  *      pkv_paged_attention_multi_query_packed, which stages each group's shared blocks once
  *      for all its members (the index area then holds query_start [n + 1] and the tiles
  *      after the pairs).  pkv_stepper_last_attention tells which ran (PKV_STEP_ATTN_*; -1

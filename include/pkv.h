@@ -266,8 +266,9 @@ pkv_status_t pkv_paged_attention_decode_noalloc(const pkv_cache_desc_t* desc, vo
  * member's rows, so tiles are full where sequences share a prompt.  The kernel re-checks on
  * the device that every member's table holds the tile's first pre keys in the same blocks
  * and that they precede every member's new tokens, and otherwise reads each member's keys on
- * its own: outputs are those of pkv_paged_attention_multi_query for any tiles, bit for bit
- * (the same 64-key stages in the same order for every row).  A tile naming sequences outside
+ * its own: for tiles that cover every new token once (the schedule's do), the outputs are
+ * those of pkv_paged_attention_multi_query bit for bit (every row sees the same keys in the
+ * same 64-key stages; a step a row does not see adds exact zeros).  A tile naming sequences outside
  * the call, a negative first or a pre that is not a whole number of stages is ignored.  Same
  * other arguments and returns; PKV_EINVAL also for num_tiles < 0 or null or misaligned tiles
  * with num_tiles > 0.
